@@ -1,0 +1,18 @@
+"""Float64 CPU oracle for the affine group-quantized matmul.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, the smoke check and the CPU-baseline
+leg of the bench may import it; the GPU library never does, and the oracle never
+imports the GPU package.
+"""
+from .oracle import (  # noqa: F401
+    decode_bf16,
+    decode_f32,
+    unpack,
+    matmul,
+    matmul_at,
+    bound_terms,
+    tolerance,
+    build,
+    load_library,
+    tolerance_coefficient,
+)

@@ -1,0 +1,163 @@
+"""ctypes front end of the float64 CPU oracle (``qmm_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.
+
+Decoding of the stored input dtypes to float64 lives here:
+  * f32 values widen exactly;
+  * a bf16 value is the upper half of an f32, so its bits shifted left by 16
+    and read as f32 give the exact value.
+Everything else (unpack, dequantize, dot product) is in the C file, which
+follows the plain definition from the pages one step at a time.
+
+Acceptance bound used by the parity tests (an element-wise bound, checked per
+output element):
+    |y(m,n) - y_ref(m,n)| <= c * sum_k |x(m,k)| * max_k |W(n,k)| + 1e-6
+with c = 1e-3 for f32 activations and c = 8e-3 for bf16 activations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qmm_oracle.c")
+_LIB = os.path.join(_HERE, "libqmm_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+             "-std=c11", "-Wall", "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """Open an oracle shared object and declare its entry points."""
+    lib = ctypes.CDLL(path)
+    i64, i32 = ctypes.c_int64, ctypes.c_int
+    p = ctypes.c_void_p
+    lib.qmm_oracle_unpack.argtypes = [i32, i64, i64, p, p]
+    lib.qmm_oracle_matmul.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, p, i32]
+    lib.qmm_oracle_matmul_at.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, i64, p, p, p]
+    lib.qmm_oracle_bound_terms.argtypes = [i32, i64, i64, i64, i64, p, p, p, p, p, p]
+    for f in (lib.qmm_oracle_unpack, lib.qmm_oracle_matmul,
+              lib.qmm_oracle_matmul_at, lib.qmm_oracle_bound_terms):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def _load(lib=None):
+    global _lib
+    if lib is not None:
+        return lib
+    with _lock:
+        if _lib is None:
+            _lib = load_library(build())
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def decode_bf16(raw: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact float64 values."""
+    raw = np.ascontiguousarray(raw, dtype=np.uint16)
+    return (raw.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def decode_f32(raw: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(raw, dtype=np.float32).astype(np.float64)
+
+
+def _as_f64(a: np.ndarray) -> np.ndarray:
+    """Accepts float64 values, f32 values, or bf16 bit patterns (uint16)."""
+    if a.dtype == np.uint16:
+        return decode_bf16(a)
+    if a.dtype == np.float32:
+        return decode_f32(a)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments" % what)
+
+
+def unpack(bits: int, K: int, N: int, w: np.ndarray, lib=None) -> np.ndarray:
+    """Codes q(n,k) as uint8 [N, K] from MLX-layout words [N, K*bits/32]."""
+    w = np.ascontiguousarray(w, dtype=np.uint32)
+    if (K * bits) % 32 != 0 or w.size != N * K * bits // 32:
+        raise ValueError("packed words do not match K=%d, N=%d, bits=%d" % (K, N, bits))
+    codes = np.empty((N, K), dtype=np.uint8)
+    _check(_load(lib).qmm_oracle_unpack(bits, K, N, _ptr(w), _ptr(codes)), "unpack")
+    return codes
+
+
+def _prep(bits, K, x, w, scales, biases, group_size):
+    x = _as_f64(x)
+    M = x.size // K
+    x = x.reshape(M, K)
+    w = np.ascontiguousarray(w, dtype=np.uint32)
+    N = w.size * 32 // (K * bits)
+    s = _as_f64(scales).reshape(N, K // group_size)
+    b = _as_f64(biases).reshape(N, K // group_size)
+    return x, w, s, b, M, N
+
+
+def matmul(bits: int, K: int, x, w, scales, biases, group_size: int = 64,
+           threads: int = 1, lib=None) -> np.ndarray:
+    """y = x . W^T in float64 for all rows; returns [M, N]."""
+    x, w, s, b, M, N = _prep(bits, K, x, w, scales, biases, group_size)
+    y = np.empty((M, N), dtype=np.float64)
+    _check(_load(lib).qmm_oracle_matmul(bits, group_size, K, N, M, _ptr(x), _ptr(w),
+                                     _ptr(s), _ptr(b), _ptr(y), threads), "matmul")
+    return y
+
+
+def matmul_at(bits: int, K: int, x, w, scales, biases, ms, ns,
+              group_size: int = 64) -> np.ndarray:
+    """y(ms[i], ns[i]) for sampled output coordinates."""
+    x, w, s, b, M, N = _prep(bits, K, x, w, scales, biases, group_size)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    out = np.empty(ms.size, dtype=np.float64)
+    _check(_load().qmm_oracle_matmul_at(bits, group_size, K, N, M, _ptr(x), _ptr(w),
+                                        _ptr(s), _ptr(b), ms.size, _ptr(ms), _ptr(ns),
+                                        _ptr(out)), "matmul_at")
+    return out
+
+
+def bound_terms(bits: int, K: int, x, w, scales, biases, group_size: int = 64):
+    """(sum_k |x(m,k)| [M], max_k |W(n,k)| [N])."""
+    x, w, s, b, M, N = _prep(bits, K, x, w, scales, biases, group_size)
+    sx = np.empty(M, dtype=np.float64)
+    mw = np.empty(N, dtype=np.float64)
+    _check(_load().qmm_oracle_bound_terms(bits, group_size, K, N, M, _ptr(x), _ptr(w),
+                                          _ptr(s), _ptr(b), _ptr(sx), _ptr(mw)),
+           "bound_terms")
+    return sx, mw
+
+
+def tolerance_coefficient(x_dtype: str) -> float:
+    """c of the acceptance bound: 1e-3 for f32 activations, 8e-3 for bf16."""
+    return {"f32": 1e-3, "bf16": 8e-3}[x_dtype]
+
+
+def tolerance(bits: int, K: int, x, w, scales, biases, x_dtype: str,
+              group_size: int = 64) -> np.ndarray:
+    """Element-wise acceptance bound [M, N]."""
+    sx, mw = bound_terms(bits, K, x, w, scales, biases, group_size)
+    return tolerance_coefficient(x_dtype) * np.outer(sx, mw) + 1e-6
