@@ -1,0 +1,235 @@
+"""Thin ctypes binding of libqmm (include/qmm.h).
+
+Argument marshalling only: every step of the matmul runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  If the
+library has not been built this module raises on first use -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqmm.so")
+
+QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED = 0, -1, -2
+QMM_ERR_HIP, QMM_ERR_WORKSPACE, QMM_ERR_NO_DEVICE = -3, -4, -5
+QMM_F32, QMM_BF16 = 0, 1
+VARIANT_AUTO, VARIANT_GEMV, VARIANT_MFMA = 0, 1, 2
+VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "mfma": VARIANT_MFMA}
+_DTYPES = {"f32": QMM_F32, "bf16": QMM_BF16}
+
+# Every entry point of include/qmm.h with its ctypes signature.
+_c = ctypes
+_P = _c.c_void_p
+SIGNATURES = {
+    "qmm_create": (_c.c_int, [_P, _P]),
+    "qmm_destroy": (None, [_P]),
+    "qmm_packed_bytes": (_c.c_int, [_P, _P, _P]),
+    "qmm_prepack": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P]),
+    "qmm_workspace_bytes": (_c.c_size_t, [_P, _c.c_int32]),
+    "qmm_workspace_bytes_ex": (_c.c_size_t, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32]),
+    "qmm_run": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _P, _c.c_size_t, _P]),
+    "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _P,
+                              _c.c_int32, _P, _c.c_size_t, _P]),
+    "qmm_debug_unpack": (_c.c_int, [_P, _P, _P, _P]),
+    "qmm_get_stats": (_c.c_int, [_P, _P]),
+    "qmm_last_error": (_c.c_char_p, []),
+    "qmm_hbm_probe": (_c.c_int, [_P, _c.c_size_t, _P, _c.c_int32, _P]),
+}
+
+
+class QmmDesc(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("max_rows", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+                ("sb_dtype", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class QmmStats(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_uint64 * 3), ("last_variant", ctypes.c_int32),
+                ("last_ntw", ctypes.c_int32), ("last_splitk", ctypes.c_int32),
+                ("last_grid", ctypes.c_int32)]
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("qmm status %d: %s" % (status, msg))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """Load libqmm.so (raises if it was not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libqmm.so is not built (run __graft_entry__.build()): " + LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != QMM_OK:
+        raise QmmError(status, lib().qmm_last_error().decode())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    """numpy array -> torch tensor on `device`; uint16 arrays are taken as bf16
+    bit patterns and come back as torch.bfloat16."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.uint32:
+        return torch.from_numpy(a.view(np.int32)).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def to_numpy_bits(t) -> np.ndarray:
+    """torch tensor -> numpy; bf16 comes back as uint16 bit patterns."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.int32:
+        return t.numpy().view(np.uint32)
+    return t.numpy()
+
+
+class Plan:
+    """One projection shape: qmm_create / qmm_destroy plus the calls on it."""
+
+    def __init__(self, bits: int, K: int, N: int, max_rows: int, x_dtype: str = "bf16",
+                 sb_dtype: str | None = None, group_size: int = 64):
+        self.bits, self.K, self.N, self.max_rows = bits, K, N, max_rows
+        self.x_dtype = x_dtype
+        self.sb_dtype = sb_dtype or x_dtype
+        d = QmmDesc(bits, group_size, K, N, max_rows, _DTYPES[x_dtype],
+                    _DTYPES[self.sb_dtype], 0)
+        h = ctypes.c_void_p()
+        _check(lib().qmm_create(ctypes.byref(d), ctypes.byref(h)))
+        self._h = h
+        self._ws = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.qmm_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def packed_bytes(self):
+        cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(lib().qmm_packed_bytes(self._h, ctypes.byref(cb), ctypes.byref(sb)))
+        return cb.value, sb.value
+
+    def prepack(self, w, scales, biases, stream=None):
+        """MLX-layout device tensors -> (codes, sb) native-layout tensors."""
+        import torch
+        cb, sbb = self.packed_bytes()
+        codes = torch.empty(cb // 4, dtype=torch.int32, device=w.device)
+        sb = torch.empty(sbb // (4 if self.sb_dtype == "f32" else 2),
+                         dtype=torch.float32 if self.sb_dtype == "f32" else torch.bfloat16,
+                         device=w.device)
+        _check(lib().qmm_prepack(self._h, _ptr(w), _ptr(scales), _ptr(biases), _ptr(codes),
+                                 _ptr(sb), _stream(stream)))
+        return codes, sb
+
+    def workspace_bytes(self, rows: int, variant: int = 0, ntw: int = 0, splitk: int = 0) -> int:
+        if variant or ntw or splitk:
+            return lib().qmm_workspace_bytes_ex(self._h, variant, ntw, splitk, rows)
+        return lib().qmm_workspace_bytes(self._h, rows)
+
+    def workspace(self, nbytes: int, device):
+        """A zero-filled workspace of at least nbytes, cached per device."""
+        import torch
+        if nbytes == 0:
+            return None
+        key = str(device)
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self._ws[key] = ws
+        return ws
+
+    def run(self, x, codes, sb, out=None, variant="auto", ntw: int = 0, splitk: int = 0,
+            stream=None, workspace=None):
+        """y = x . W^T; x is [..., K] on the device, y is [..., N] in x's dtype."""
+        import torch
+        rows = x.numel() // self.K
+        if out is None:
+            out = torch.empty(*x.shape[:-1], self.N, dtype=x.dtype, device=x.device)
+        v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
+        need = self.workspace_bytes(rows, v, ntw, splitk)
+        ws = workspace if workspace is not None else self.workspace(need, x.device)
+        wsb = ws.numel() if ws is not None else 0
+        _check(lib().qmm_run_ex(self._h, v, ntw, splitk, _ptr(x), _ptr(codes), _ptr(sb),
+                                _ptr(out), rows, _ptr(ws), wsb, _stream(stream)))
+        return out
+
+    def debug_unpack(self, codes, stream=None):
+        import torch
+        out = torch.empty(self.N, self.K, dtype=torch.uint8, device=codes.device)
+        _check(lib().qmm_debug_unpack(self._h, _ptr(codes), _ptr(out), _stream(stream)))
+        return out
+
+    def stats(self) -> dict:
+        s = QmmStats()
+        _check(lib().qmm_get_stats(self._h, ctypes.byref(s)))
+        return {"launches": {"gemv": s.launches[VARIANT_GEMV], "mfma": s.launches[VARIANT_MFMA]},
+                "last_variant": {1: "gemv", 2: "mfma"}.get(s.last_variant, "none"),
+                "last_ntw": s.last_ntw, "last_splitk": s.last_splitk, "last_grid": s.last_grid}
+
+
+def hbm_probe(buf, grid: int = 0, stream=None):
+    """Stream-read a device buffer (measurement hook)."""
+    import torch
+    g = grid or 4096
+    sink = torch.empty(g, dtype=torch.int32, device=buf.device)
+    _check(lib().qmm_hbm_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), g,
+                               _stream(stream)))
+    return sink
+
+
+class QuantizedLinear:
+    """A projection ready to run: plan + weights in the native layout."""
+
+    def __init__(self, problem_or_shape, w=None, scales=None, biases=None, max_rows=None,
+                 device="cuda"):
+        p = problem_or_shape
+        self.plan = Plan(p.bits, p.K, p.N, max_rows or max(p.M, 1), p.x_dtype, p.sb_dtype)
+        wd = to_device(p.w if w is None else w, device)
+        sd = to_device(p.scales if scales is None else scales, device)
+        bd = to_device(p.biases if biases is None else biases, device)
+        self.codes, self.sb = self.plan.prepack(wd, sd, bd)
+
+    def __call__(self, x, **kw):
+        return self.plan.run(x, self.codes, self.sb, **kw)

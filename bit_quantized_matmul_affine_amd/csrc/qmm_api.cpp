@@ -1,0 +1,364 @@
+// qmm_api.cpp -- the C ABI of include/qmm.h: argument validation, launch
+// planning and dispatch.  All validation happens on the host before any HIP
+// call.
+//
+// [P1] = page "@mlx-bun/inference 0.0.0-stage -> 1.0.0" (diffend npm page 53).
+//   * affineSplitMmaEligible(): eligibility is a separate predicate (affine,
+//     group 64, bits 3 or 4, shape multiples, at least one row) -> here the
+//     QMM_ERR_UNSUPPORTED status, raised in qmm_create.
+//   * affineSplitMma(): throws when there are no rows -> QMM_ERR_INVALID_ARG
+//     from qmm_run for rows < 1.
+//   * affineSplitMmaPlan(): the launch shape is a small value chosen from the
+//     output width N -> here plan_config(), which also looks at the row count
+//     and the chip's 256 compute units.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+qmm_status fail(qmm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+struct Cfg {
+  int variant;  // QMM_VARIANT_GEMV or QMM_VARIANT_MFMA
+  int rows_per_launch;
+  int tile_rows;  // mt (MFMA, 16-row tiles of x) or mr (GEMV rows)
+  int ntw;        // W tiles per wavefront
+  int S;          // K splits
+  int nTB;        // tile blocks
+  size_t lds;     // dynamic LDS bytes (GEMV)
+};
+
+}  // namespace
+
+struct qmm_plan {
+  qmm_desc d;
+  int nT, nC;
+  int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
+  int env_ntw, env_splitk;
+  mutable std::atomic<uint64_t> launches[3];
+  mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
+};
+
+namespace {
+
+constexpr int kTargetBlocks = 1024;   // about four workgroups per compute unit
+constexpr size_t kMaxGemvLds = 64 * 1024;
+
+int env_int(const char* name) {
+  const char* v = getenv(name);
+  return v ? atoi(v) : 0;
+}
+
+int round_up_pow2(int v, int cap) {
+  int p = 1;
+  while (p < v && p < cap) p <<= 1;
+  return p;
+}
+
+size_t ticket_bytes(const qmm_plan* p) {
+  return ((size_t)p->nT * 4 + 255) / 256 * 256;
+}
+
+// Pick the kernel family.  Vector-ALU for f32 activations (the MFMA path takes
+// bf16 operands) and, for bf16, wherever it is measured faster.
+int pick_variant(const qmm_plan* p, int rows, int forced) {
+  if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
+  if (forced) return forced;
+  if (p->force_variant) return p->force_variant;
+  (void)rows;
+  return QMM_VARIANT_MFMA;
+}
+
+// Launch shape for one launch of `rows` rows (rows <= rows_per_launch).
+Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int s_req) {
+  Cfg c{};
+  c.variant = variant;
+  const int nT = p->nT, nC = p->nC;
+  if (variant == QMM_VARIANT_MFMA) {
+    c.rows_per_launch = qmm::kMaxMfmaRows;
+    const int r = std::min(rows, qmm::kMaxMfmaRows);
+    c.tile_rows = round_up_pow2((r + 15) / 16, 8);
+    int ntw = c.tile_rows <= 2 ? 2 : 1;
+    if (ntw_req) ntw = ntw_req;
+    const int cap = c.tile_rows <= 2 ? 4 : (c.tile_rows == 4 ? 2 : 1);
+    c.ntw = std::min(ntw >= 4 ? 4 : (ntw >= 2 ? 2 : 1), cap);
+  } else {
+    c.rows_per_launch = qmm::kMaxGemvRows;
+    const int r = std::min(rows, qmm::kMaxGemvRows);
+    c.tile_rows = round_up_pow2(r, 8);
+    int ntw = c.tile_rows == 1 ? 2 : 1;
+    if (ntw_req) ntw = ntw_req;
+    const int cap = c.tile_rows == 1 ? 4 : (c.tile_rows <= 4 ? 2 : 1);
+    c.ntw = std::min(ntw >= 4 ? 4 : (ntw >= 2 ? 2 : 1), cap);
+  }
+  c.nTB = (nT + qmm::kWaves * c.ntw - 1) / (qmm::kWaves * c.ntw);
+  int S;
+  if (s_req) {
+    S = s_req;
+  } else {
+    S = (kTargetBlocks + c.nTB - 1) / c.nTB;
+    // partial sums cost S*rows*N*8 bytes of traffic: keep S*rows bounded
+    const int r = std::min(rows, c.rows_per_launch);
+    S = std::min(S, std::max(1, 64 / std::max(1, r)));
+    S = std::min(S, std::max(1, nC / 2));
+  }
+  S = std::max(1, std::min(S, nC));
+  if (variant == QMM_VARIANT_GEMV) {
+    const bool xf = p->d.x_dtype == QMM_F32;
+    // the activation slice of one split must fit the LDS budget
+    while (S < nC && qmm::gemv_lds_bytes(xf, c.tile_rows, ((nC + S - 1) / S) * qmm::kChunkK) > kMaxGemvLds) ++S;
+    c.lds = qmm::gemv_lds_bytes(xf, c.tile_rows, ((nC + S - 1) / S) * qmm::kChunkK);
+  }
+  c.S = S;
+  return c;
+}
+
+size_t cfg_workspace(const qmm_plan* p, const Cfg& c, int rows) {
+  if (c.S <= 1) return 0;
+  const int r = std::min(rows, c.rows_per_launch);
+  return ticket_bytes(p) + (size_t)c.S * r * p->d.N * sizeof(float);
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+qmm_status check_plan(const qmm_plan* p) {
+  if (!p) return fail(QMM_ERR_INVALID_ARG, "plan is NULL");
+  return QMM_OK;
+}
+
+qmm_status hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorNoDevice ? QMM_ERR_NO_DEVICE : QMM_ERR_HIP, "%s: %s", what,
+              hipGetErrorString(e));
+}
+
+qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int s_req, const void* x,
+                    const void* codes, const void* sb, void* y, int32_t rows, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (qmm_status st = check_plan(p)) return st;
+  if (rows < 1 || rows > p->d.max_rows)
+    return fail(QMM_ERR_INVALID_ARG, "rows=%d outside 1..max_rows=%d", rows, p->d.max_rows);
+  if (!x || !codes || !sb || !y) return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(sb, 16) || !aligned(y, 4))
+    return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
+  if (variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GEMV &&
+      variant_req != QMM_VARIANT_MFMA)
+    return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
+  if (variant_req == QMM_VARIANT_MFMA && p->d.x_dtype != QMM_BF16)
+    return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
+  if (ntw_req < 0 || ntw_req > 8 || s_req < 0)
+    return fail(QMM_ERR_INVALID_ARG, "ntw must be 0..8 and splitk >= 0");
+  const int ntw_eff = ntw_req ? ntw_req : p->env_ntw;
+  const int s_eff = s_req ? s_req : p->env_splitk;
+  const int variant = pick_variant(p, rows, variant_req);
+  const Cfg c = plan_config(p, rows, variant, ntw_eff, s_eff);
+  const size_t need = cfg_workspace(p, c, rows);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  ws ? ws_bytes : (size_t)0);
+    if (!aligned(ws, 256)) return fail(QMM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  const bool xf = p->d.x_dtype == QMM_F32, sf = p->d.sb_dtype == QMM_F32;
+  const size_t xe = xf ? 4 : 2;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  for (int r0 = 0; r0 < rows; r0 += c.rows_per_launch) {
+    const int rb = std::min(c.rows_per_launch, rows - r0);
+    const Cfg cb = plan_config(p, rb, variant, ntw_eff, s_eff);
+    qmm::LaunchArgs a{};
+    a.x = static_cast<const char*>(x) + (size_t)r0 * p->d.K * xe;
+    a.codes = static_cast<const uint32_t*>(codes);
+    a.sb = sb;
+    a.y = static_cast<char*>(y) + (size_t)r0 * p->d.N * xe;
+    a.tickets = static_cast<uint32_t*>(ws);
+    a.part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + ticket_bytes(p)) : nullptr;
+    a.M = rb;
+    a.N = (int)p->d.N;
+    a.K = (int)p->d.K;
+    a.S = cb.S;
+    a.nTB = cb.nTB;
+    a.ldx = (int)p->d.K;
+    a.ldy = (int)p->d.N;
+    if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
+      return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
+    hipError_t e;
+    if (variant == QMM_VARIANT_MFMA)
+      e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, a, st);
+    else
+      e = qmm::launch_gemv(p->d.bits, xf, sf, cb.tile_rows, cb.ntw, a, cb.lds, st);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    p->launches[variant].fetch_add(1);
+    p->last_variant = variant;
+    p->last_ntw = cb.ntw;
+    p->last_splitk = cb.S;
+    p->last_grid = cb.nTB * cb.S;
+  }
+  if (getenv("QMM_LOG"))
+    fprintf(stderr, "qmm: rows=%d variant=%d ntw=%d splitk=%d grid=%d\n", rows, variant, c.ntw,
+            c.S, c.nTB * c.S);
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
+  if (!out) return fail(QMM_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!d) return fail(QMM_ERR_INVALID_ARG, "desc is NULL");
+  const int b = d->bits;
+  if (b != 2 && b != 3 && b != 4 && b != 5 && b != 6 && b != 8)
+    return fail(QMM_ERR_INVALID_ARG, "bits=%d is not an MLX affine width", b);
+  if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128)
+    return fail(QMM_ERR_INVALID_ARG, "group_size=%d is not an MLX affine group size", d->group_size);
+  if (d->K <= 0 || d->N <= 0) return fail(QMM_ERR_INVALID_ARG, "K and N must be positive");
+  if (d->K % d->group_size != 0)
+    return fail(QMM_ERR_INVALID_ARG, "K=%lld is not a multiple of the group size", (long long)d->K);
+  if (d->max_rows < 1) return fail(QMM_ERR_INVALID_ARG, "max_rows must be >= 1");
+  if ((d->x_dtype != QMM_F32 && d->x_dtype != QMM_BF16) ||
+      (d->sb_dtype != QMM_F32 && d->sb_dtype != QMM_BF16))
+    return fail(QMM_ERR_INVALID_ARG, "unknown dtype");
+  if (d->flags != 0) return fail(QMM_ERR_INVALID_ARG, "flags must be 0");
+  if (b != 3 && b != 4) return fail(QMM_ERR_UNSUPPORTED, "bits=%d: only 3 and 4 are implemented", b);
+  if (d->group_size != 64)
+    return fail(QMM_ERR_UNSUPPORTED, "group_size=%d: only 64 is implemented", d->group_size);
+  if (d->K % qmm::kChunkK != 0)
+    return fail(QMM_ERR_UNSUPPORTED, "K=%lld: must be a multiple of %d", (long long)d->K, qmm::kChunkK);
+  if (d->N % qmm::kTileN != 0)
+    return fail(QMM_ERR_UNSUPPORTED, "N=%lld: must be a multiple of %d", (long long)d->N, qmm::kTileN);
+  if (d->K > (1LL << 24) || d->N > (1LL << 24) || (int64_t)d->max_rows * d->K > (1LL << 31) ||
+      (int64_t)d->max_rows * d->N > (1LL << 31))
+    return fail(QMM_ERR_UNSUPPORTED, "shape exceeds 32-bit indexing");
+  qmm_plan* p = new (std::nothrow) qmm_plan();
+  if (!p) return fail(QMM_ERR_INVALID_ARG, "out of host memory");
+  p->d = *d;
+  p->nT = (int)(d->N / qmm::kTileN);
+  p->nC = (int)(d->K / qmm::kChunkK);
+  p->force_variant = 0;
+  if (const char* v = getenv("QMM_FORCE_VARIANT")) {
+    if (!strcmp(v, "gemv")) p->force_variant = QMM_VARIANT_GEMV;
+    if (!strcmp(v, "mfma")) p->force_variant = QMM_VARIANT_MFMA;
+  }
+  p->env_ntw = env_int("QMM_NTW");
+  p->env_splitk = env_int("QMM_SPLITK");
+  for (auto& l : p->launches) l = 0;
+  p->last_variant = 0;
+  p->last_ntw = 0;
+  p->last_splitk = 0;
+  p->last_grid = 0;
+  *out = p;
+  return QMM_OK;
+}
+
+void qmm_destroy(qmm_plan* p) { delete p; }
+
+qmm_status qmm_packed_bytes(const qmm_plan* p, size_t* codes_bytes, size_t* sb_bytes) {
+  if (qmm_status st = check_plan(p)) return st;
+  if (!codes_bytes || !sb_bytes) return fail(QMM_ERR_INVALID_ARG, "NULL output pointer");
+  *codes_bytes = (size_t)p->d.N * p->d.K * p->d.bits / 8;
+  *sb_bytes = (size_t)2 * p->d.N * (p->d.K / 64) * (p->d.sb_dtype == QMM_F32 ? 4 : 2);
+  return QMM_OK;
+}
+
+qmm_status qmm_prepack(const qmm_plan* p, const uint32_t* w, const void* scales,
+                       const void* biases, void* codes_out, void* sb_out, void* stream) {
+  if (qmm_status st = check_plan(p)) return st;
+  if (!w || !scales || !biases || !codes_out || !sb_out)
+    return fail(QMM_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(w, 4) || !aligned(codes_out, 16) || !aligned(sb_out, 16) ||
+      !aligned(scales, p->d.sb_dtype == QMM_F32 ? 4 : 2) ||
+      !aligned(biases, p->d.sb_dtype == QMM_F32 ? 4 : 2))
+    return fail(QMM_ERR_INVALID_ARG, "misaligned pointer");
+  hipError_t e = qmm::launch_repack(p->d.bits, p->d.sb_dtype == QMM_F32, w, scales, biases,
+                                    static_cast<uint32_t*>(codes_out), sb_out, (int)p->d.N,
+                                    (int)p->d.K, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "repack launch");
+  return QMM_OK;
+}
+
+size_t qmm_workspace_bytes_ex(const qmm_plan* p, int32_t variant, int32_t ntw, int32_t splitk,
+                              int32_t rows) {
+  if (!p || rows < 1) return 0;
+  const int v = pick_variant(p, rows, variant);
+  const Cfg c = plan_config(p, rows, v, ntw ? ntw : p->env_ntw, splitk ? splitk : p->env_splitk);
+  return cfg_workspace(p, c, rows);
+}
+
+size_t qmm_workspace_bytes(const qmm_plan* p, int32_t rows) {
+  if (!p || rows < 1) return 0;
+  size_t need = qmm_workspace_bytes_ex(p, QMM_VARIANT_AUTO, 0, 0, rows);
+  if (p->d.x_dtype == QMM_BF16) {
+    need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_GEMV, 0, 0, rows));
+    need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_MFMA, 0, 0, rows));
+  }
+  return need;
+}
+
+qmm_status qmm_run(const qmm_plan* p, const void* x, const void* codes, const void* sb, void* y,
+                   int32_t rows, void* ws, size_t ws_bytes, void* stream) {
+  return run_impl(p, QMM_VARIANT_AUTO, 0, 0, x, codes, sb, y, rows, ws, ws_bytes, stream);
+}
+
+qmm_status qmm_run_ex(const qmm_plan* p, int32_t variant, int32_t ntw, int32_t splitk,
+                      const void* x, const void* codes, const void* sb, void* y, int32_t rows,
+                      void* ws, size_t ws_bytes, void* stream) {
+  return run_impl(p, variant, ntw, splitk, x, codes, sb, y, rows, ws, ws_bytes, stream);
+}
+
+qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, void* stream) {
+  if (qmm_status st = check_plan(p)) return st;
+  if (!codes || !out) return fail(QMM_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(codes, 4)) return fail(QMM_ERR_INVALID_ARG, "misaligned codes");
+  hipError_t e = qmm::launch_debug_unpack(p->d.bits, static_cast<const uint32_t*>(codes), out,
+                                          (int)p->d.N, (int)p->d.K,
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "debug unpack launch");
+  return QMM_OK;
+}
+
+qmm_status qmm_get_stats(const qmm_plan* p, qmm_stats* out) {
+  if (qmm_status st = check_plan(p)) return st;
+  if (!out) return fail(QMM_ERR_INVALID_ARG, "out is NULL");
+  for (int i = 0; i < 3; ++i) out->launches[i] = p->launches[i].load();
+  out->last_variant = p->last_variant;
+  out->last_ntw = p->last_ntw;
+  out->last_splitk = p->last_splitk;
+  out->last_grid = p->last_grid;
+  return QMM_OK;
+}
+
+const char* qmm_last_error(void) { return g_err.c_str(); }
+
+qmm_status qmm_hbm_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
+                         void* stream) {
+  if (!buf || !sink) return fail(QMM_ERR_INVALID_ARG, "NULL pointer");
+  if (bytes == 0 || bytes % 16 != 0 || !aligned(buf, 16))
+    return fail(QMM_ERR_INVALID_ARG, "bytes must be a positive multiple of 16, buf 16-byte aligned");
+  if (grid < 0) return fail(QMM_ERR_INVALID_ARG, "grid must be >= 0");
+  hipError_t e = qmm::launch_probe(buf, bytes, sink, grid ? grid : 4096,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return QMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// qmm_internal.h -- declarations shared by the C-ABI front end (qmm_api.cpp)
+// and the HIP kernels (qmm_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+// Kernel-native tiling.  One wavefront multiplies a block of 16 rows of W by
+// 128 columns (two quantization groups) per step.
+constexpr int kTileN = 16;
+constexpr int kChunkK = 128;
+constexpr int kWaves = 4;            // wavefronts per workgroup
+constexpr int kBlockThreads = 64 * kWaves;
+constexpr int kMaxMfmaRows = 128;    // rows per MFMA launch (8 tiles of 16)
+constexpr int kMaxGemvRows = 8;      // rows per vector-ALU launch
+
+struct LaunchArgs {
+  const void* x;          // [M, K] activations (x_dtype)
+  const uint32_t* codes;  // native packed codes
+  const void* sb;         // native packed scales/biases (sb_dtype)
+  void* y;                // [M, N] output (x_dtype)
+  float* part;            // [S, M, N] split-K partials (S > 1)
+  uint32_t* tickets;      // one counter per tile block (S > 1)
+  int M, N, K;
+  int S;                  // K splits
+  int nTB;                // tile blocks (kWaves * ntw tiles each)
+  int ldx, ldy;           // row strides of x and y in elements
+};
+
+// All launchers return hipSuccess or the launch error.
+hipError_t launch_repack(int bits, bool sb_f32, const uint32_t* w, const void* scales,
+                         const void* biases, uint32_t* codes, void* sb, int N, int K,
+                         hipStream_t st);
+hipError_t launch_debug_unpack(int bits, const uint32_t* codes, uint8_t* out, int N, int K,
+                               hipStream_t st);
+hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, const LaunchArgs& a,
+                       hipStream_t st);
+hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const LaunchArgs& a,
+                       size_t lds_bytes, hipStream_t st);
+hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
+
+// Bytes of LDS the vector-ALU kernel needs for `mr` rows over `kslice` columns.
+size_t gemv_lds_bytes(bool x_f32, int mr, int kslice);
+
+}  // namespace qmm

@@ -1,0 +1,710 @@
+// qmm_kernels.hip -- gfx950 kernels for y = x . W^T over affine 3/4-bit,
+// group-64 quantized weights.
+//
+// Sources.  [P1] = page "@mlx-bun/inference 0.0.0-stage -> 1.0.0" (diffend npm
+// page 53).  [P3] = page "mlx-bun 0.0.4" (diffend npm page 56).
+//   * The operation and the MLX packing: [P1] affine-split-mma.ts header
+//     comment and helper affine_unit; affine3-mma.ts helper affine_q3;
+//     affine4-mma.ts helper affine_q4; weight = scale*q + bias per group of 64.
+//   * Decode each weight once and reuse it for every activation row:
+//     [P1] affine3-rows.ts / affine4-rows.ts header comments.
+//   * Factored per-group algebra sum_g scale*sum(q*x) + bias*sum(x):
+//     [P1] affine3-rows.ts header comment; [P3] fused-decode-kernel.ts
+//     SCORE_PREAMBLE comment (dequant factored out of the inner loop).
+//   * K split across workers, partials added in a fixed order with no
+//     atomics on the data: [P1] affine-split-mma.ts (threadgroup fold over
+//     SPLITS, summed in split order); [P3] fused-decode-kernel.ts header
+//     (deterministic merge, no atomic adds).
+//   * Rows past the last activation row are never written: [P1]
+//     affine-split-mma.ts fold ("columns below M only").
+//
+// What is ours (gfx950, not the pages' Metal design):
+//   * Codes become bf16 values 128+q with one and-or per PAIR of codes:
+//     (w >> shift) & mask | 0x43004300 (bf16 0x4300 is 128.0 and q < 128 fits
+//     in the 7 mantissa bits exactly).  The 128 offset is removed per group
+//     through the factored form: for one group,
+//         sum_k (s*q_k + b) x_k = s * sum_k (128+q_k) x_k + (b - 128 s) * sum_k x_k.
+//   * A one-time repack ("native layout") makes every wavefront load 768 or
+//     1024 contiguous bytes per instruction and hands each lane exactly the
+//     codes its MFMA operand needs.  Byte count is unchanged.
+//   * MFMA path: v_mfma_f32_16x16x32_bf16 with A = 16 activation rows and
+//     B = 16 weight rows; per group the B operand is the 128+q pairs, a second
+//     product against all-ones gives sum_k x_k, and the accumulator is scaled
+//     in f32 before the next group.
+//   * Vector-ALU path: v_dot2_f32_bf16 on (128+q) pairs against activation
+//     pairs staged in LDS.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "qmm_internal.h"
+
+namespace qmm {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
+typedef float f32x4 __attribute__((__vector_size__(16)));
+typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
+
+// ---------------------------------------------------------------------------
+// Native layout.
+//
+// Tiles of 16 rows of W (nT = N/16) by chunks of 128 columns (nC = K/128, two
+// quantization groups).  Block (tile t, chunk c) has index t*nC + c.
+// Codes: block b occupies words [b*64*BITS, (b+1)*64*BITS); lane l of the
+// block owns words [l*BITS, (l+1)*BITS).  Lane l serves row r = l & 15 of the
+// tile and quarter kg = l >> 4 of each group: its 32 codes are
+//     (g', i) for g' in {0,1}, i in [0,16):  k = 128c + 64g' + 16kg + i.
+// The codes are grouped in 16 pairs p = 8g' + u holding (g', 2u) in the low
+// and (g', 2u+1) in the high 16 bits after the unpack:
+//   4-bit: pair p = 4j + t sits in word j, low code at bits [4t, 4t+4),
+//          high code at bits [16+4t, 16+4t+4).
+//   3-bit: pair p = 5j + t (p < 15) sits in word j, low code at bits
+//          [3t, 3t+3), high code at bits [16+3t, 16+3t+3); pair 15 keeps bit
+//          b of its low code in bit 15 of word b and bit b of its high code in
+//          bit 31 of word b (b = 0,1,2).
+// Scales/biases: block b holds 16 rows x {s_g0, s_g1, b_g0, b_g1}.
+// ---------------------------------------------------------------------------
+
+template <int BITS>
+__device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* P) {
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) P[4 * j + t] = ((w[j] >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int t = 0; t < 5; ++t) P[5 * j + t] = ((w[j] >> (3 * t)) & 0x00070007u) | 0x43004300u;
+    P[15] = ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
+            ((w[2] >> 13) & 0x00040004u) | 0x43004300u;
+  }
+}
+
+// Inverse of unpack_pairs for one code: OR code q of (g', i) into w.
+template <int BITS>
+__device__ __forceinline__ void place_code(uint32_t* w, int gp, int i, uint32_t q) {
+  const int p = 8 * gp + (i >> 1), half = i & 1;
+  if constexpr (BITS == 4) {
+    w[p >> 2] |= q << (16 * half + 4 * (p & 3));
+  } else {
+    if (p < 15) {
+      w[p / 5] |= q << (16 * half + 3 * (p % 5));
+    } else {
+#pragma unroll
+      for (int b = 0; b < 3; ++b) w[b] |= ((q >> b) & 1u) << (half ? 31 : 15);
+    }
+  }
+}
+
+// Code k of an MLX row: bits [k*BITS, (k+1)*BITS) of the row's LSB-first
+// stream; a field crossing a word boundary takes its high bits from the next
+// word ([P1] affine3-mma.ts, affine_q3).
+template <int BITS>
+__device__ __forceinline__ uint32_t mlx_code(const uint32_t* row, int k) {
+  const int p = k * BITS, wi = p >> 5, off = p & 31;
+  uint32_t v = row[wi] >> off;
+  if (off + BITS > 32) v |= row[wi + 1] << (32 - off);
+  return v & ((1u << BITS) - 1u);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);                                            // nearest even
+  return (uint16_t)(u >> 16);
+}
+
+// Workgroups go to the eight XCDs round-robin by id.  Renumber them so that
+// each XCD gets a contiguous range of work items: the K splits of one tile
+// block then share an L2.
+__device__ __forceinline__ int xcd_item(int bid, int total) {
+  const int xcd = bid & 7, j = bid >> 3, q = total >> 3, rem = total & 7;
+  return xcd * q + (xcd < rem ? xcd : rem) + j;
+}
+
+// ---------------------------------------------------------------------------
+// One-time loader and the test decoder.
+// ---------------------------------------------------------------------------
+
+template <int BITS, typename ST>
+__global__ void __launch_bounds__(256) repack_kernel(const uint32_t* __restrict__ w,
+                                                     const ST* __restrict__ scales,
+                                                     const ST* __restrict__ biases,
+                                                     uint32_t* __restrict__ codes,
+                                                     ST* __restrict__ sb, int N, int K) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nC = K / kChunkK, nT = N / kTileN;
+  if (gid >= (long)nT * nC * 64) return;
+  const int lane = (int)(gid & 63);
+  const long blk = gid >> 6;
+  const int c = (int)(blk % nC), tile = (int)(blk / nC);
+  const int r = lane & 15, kg = lane >> 4, n = tile * kTileN + r;
+  const uint32_t* row = w + (long)n * (K * BITS / 32);
+  uint32_t out[BITS];
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) out[j] = 0u;
+  for (int gp = 0; gp < 2; ++gp)
+    for (int i = 0; i < 16; ++i)
+      place_code<BITS>(out, gp, i, mlx_code<BITS>(row, kChunkK * c + 64 * gp + 16 * kg + i));
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) codes[blk * 64 * BITS + lane * BITS + j] = out[j];
+  if (kg == 0) {
+    const int G = K / 64;
+    ST* e = sb + (blk * kTileN + r) * 4;
+    e[0] = scales[(long)n * G + 2 * c];
+    e[1] = scales[(long)n * G + 2 * c + 1];
+    e[2] = biases[(long)n * G + 2 * c];
+    e[3] = biases[(long)n * G + 2 * c + 1];
+  }
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(256) debug_unpack_kernel(const uint32_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ out, int N,
+                                                           int K) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int nC = K / kChunkK, nT = N / kTileN;
+  if (gid >= (long)nT * nC * 64) return;
+  const int lane = (int)(gid & 63);
+  const long blk = gid >> 6;
+  const int c = (int)(blk % nC), tile = (int)(blk / nC);
+  const int r = lane & 15, kg = lane >> 4, n = tile * kTileN + r;
+  uint32_t w[BITS], P[16];
+#pragma unroll
+  for (int j = 0; j < BITS; ++j) w[j] = codes[blk * 64 * BITS + lane * BITS + j];
+  unpack_pairs<BITS>(w, P);
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int gp = p >> 3, u = p & 7;
+    const long k = (long)kChunkK * c + 64 * gp + 16 * kg + 2 * u;
+    out[(long)n * K + k] = (uint8_t)((P[p] & 0xFFFFu) - 0x4300u);
+    out[(long)n * K + k + 1] = (uint8_t)((P[p] >> 16) - 0x4300u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scales and biases of one (tile row, chunk): s_g0, s_g1, b_g0, b_g1.
+// ---------------------------------------------------------------------------
+template <typename ST> struct SBPair;
+template <> struct SBPair<uint16_t> {
+  uint32_t s2, b2;
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    s2 = v.x;
+    b2 = v.y;
+  }
+  __device__ __forceinline__ float s(int g) const {
+    return __uint_as_float(g ? (s2 & 0xFFFF0000u) : (s2 << 16));
+  }
+  __device__ __forceinline__ float b(int g) const {
+    return __uint_as_float(g ? (b2 & 0xFFFF0000u) : (b2 << 16));
+  }
+};
+template <> struct SBPair<float> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const float4*>(p); }
+  __device__ __forceinline__ float s(int g) const { return g ? v.y : v.x; }
+  __device__ __forceinline__ float b(int g) const { return g ? v.w : v.z; }
+};
+
+// ---------------------------------------------------------------------------
+// Split-K epilogue.  S > 1: every workgroup stores its partial tile to
+// part[s][m][n]; the last workgroup of a tile block to take a ticket adds the
+// S partials in split order 0..S-1 and writes y, then re-arms the ticket.
+// The sum order never depends on arrival order, so results are bitwise
+// reproducible.
+// ---------------------------------------------------------------------------
+template <bool Y_F32>
+__device__ __forceinline__ void store_y(void* y, long idx, float v) {
+  if constexpr (Y_F32)
+    reinterpret_cast<float*>(y)[idx] = v;
+  else
+    reinterpret_cast<uint16_t*>(y)[idx] = f32_to_bf16(v);
+}
+
+template <bool Y_F32>
+__device__ void fold_partials(const LaunchArgs& a, int tb, int n0, int n1) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = atomicAdd(&a.tickets[tb], 1u);
+    s_last = (old == (uint32_t)(a.S - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int width = n1 - n0;
+  const long plane = (long)a.M * a.N;
+  for (int idx = threadIdx.x; idx < a.M * width; idx += blockDim.x) {
+    const int m = idx / width, n = n0 + idx % width;
+    const float* p = a.part + (long)m * a.N + n;
+    float sum = 0.f;
+    for (int s = 0; s < a.S; ++s) sum += __builtin_nontemporal_load(p + s * plane);
+    store_y<Y_F32>(a.y, (long)m * a.ldy + n, sum);
+  }
+  if (threadIdx.x == 0) atomicExch(&a.tickets[tb], 0u);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel (bf16 activations).  Workgroup = 4 wavefronts; wavefront w owns
+// NTW consecutive tiles of W (16 rows each) and, for the workgroup's K split,
+// multiplies them by MT tiles of 16 activation rows.
+// ---------------------------------------------------------------------------
+template <int BITS, int MT, int NTW, typename ST>
+__global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kg = lane >> 4;
+  const int item = xcd_item(blockIdx.x, a.nTB * a.S);
+  const int tb = item / a.S, s = item - tb * a.S;
+  const int nT = a.N / kTileN, nC = a.K / kChunkK;
+  const int c0 = (int)((long)s * nC / a.S), c1 = (int)((long)(s + 1) * nC / a.S);
+  const int tile0 = (tb * kWaves + wave) * NTW;
+  const uint16_t* __restrict__ x = reinterpret_cast<const uint16_t*>(a.x);
+  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
+
+  f32x4 acc[NTW][MT];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (tile0 < nT && c0 < c1) {
+    bool tvalid[NTW];
+    const uint32_t* cptr[NTW];
+    const ST* sptr[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int t = tile0 + nt < nT ? tile0 + nt : nT - 1;
+      tvalid[nt] = tile0 + nt < nT;
+      cptr[nt] = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
+      sptr[nt] = sbp + ((long)t * nC * kTileN + r) * 4;
+    }
+    const uint16_t* xrow[MT];
+    bool xvalid[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + r;
+      xvalid[mt] = m < a.M;
+      xrow[mt] = x + (long)(xvalid[mt] ? m : 0) * a.ldx + 16 * kg;
+    }
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    uint32_t W[NTW][BITS];
+    SBPair<ST> SBv[NTW];
+    u32x4 A[MT][4];
+    auto load_chunk = [&](int c, uint32_t (&Wd)[NTW][BITS], SBPair<ST> (&Sd)[NTW],
+                          u32x4 (&Ad)[MT][4]) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const uint32_t* p = cptr[nt] + (long)c * 64 * BITS;
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) Wd[nt][j] = __builtin_nontemporal_load(p + j);
+        Sd[nt].load(sptr[nt] + (long)c * kTileN * 4);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          // step t: group g' = t>>1, half h = t&1 -> 8 values at 64g' + 16kg + 8h
+          const u32x4* p = reinterpret_cast<const u32x4*>(xrow[mt] + (long)kChunkK * c +
+                                                          64 * (t >> 1) + 8 * (t & 1));
+          Ad[mt][t] = xvalid[mt] ? *p : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    load_chunk(c0, W, SBv, A);
+    for (int c = c0; c < c1; ++c) {
+      uint32_t Wn[NTW][BITS];
+      SBPair<ST> Sn[NTW];
+      u32x4 An[MT][4];
+      if (c + 1 < c1) load_chunk(c + 1, Wn, Sn, An);
+
+      // sum_k x_k of each group, replicated in every column
+      f32x4 EX[MT][2];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, A[mt][2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0,
+              0, 0);
+          EX[mt][gp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, A[mt][2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e,
+              0, 0, 0);
+        }
+
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        if (!tvalid[nt]) continue;
+        uint32_t P[16];
+        unpack_pairs<BITS>(W[nt], P);
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const float sc = SBv[nt].s(gp);
+          const float bp = SBv[nt].b(gp) - 128.f * sc;
+          const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
+          const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, A[mt][2 * gp]), __builtin_bit_cast(bf16x8, B0), zero,
+                0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[mt][2 * gp + 1]),
+                                                        __builtin_bit_cast(bf16x8, B1), d, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (16 * mt + q < a.M)
+                acc[nt][mt][q] = fmaf(sc, d[q], fmaf(bp, EX[mt][gp][q], acc[nt][mt][q]));
+          }
+        }
+      }
+      if (c + 1 < c1) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+          for (int j = 0; j < BITS; ++j) W[nt][j] = Wn[nt][j];
+          SBv[nt] = Sn[nt];
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) A[mt][t] = An[mt][t];
+      }
+    }
+  }
+
+  // Output: lane holds column n = 16*tile + r, rows m = 16*mt + 4*kg + q.
+  if (a.S == 1) {
+    if (tile0 >= nT) return;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      if (tile0 + nt >= nT) continue;
+      const int n = (tile0 + nt) * kTileN + r;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = 16 * mt + 4 * kg + q;
+          if (m < a.M) store_y<false>(a.y, (long)m * a.ldy + n, acc[nt][mt][q]);
+        }
+    }
+    return;
+  }
+  if (tile0 < nT) {
+    float* part = a.part + (long)s * a.M * a.N;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      if (tile0 + nt >= nT) continue;
+      const int n = (tile0 + nt) * kTileN + r;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = 16 * mt + 4 * kg + q;
+          if (m < a.M) __builtin_nontemporal_store(acc[nt][mt][q], part + (long)m * a.N + n);
+        }
+    }
+  }
+  const int n0 = tb * kWaves * NTW * kTileN;
+  const int n1 = min(a.N, n0 + kWaves * NTW * kTileN);
+  fold_partials<false>(a, tb, n0, n1);
+}
+
+// ---------------------------------------------------------------------------
+// Vector-ALU kernel: up to MR activation rows per pass, activations of the
+// workgroup's K split staged in LDS together with per-(row, group, quarter)
+// sums.  Lane (r, kg) accumulates its quarter of each group; the four
+// quarters are added with cross-lane shuffles at the end.
+// ---------------------------------------------------------------------------
+template <bool X_F32>
+using XStore = typename std::conditional<X_F32, float, uint16_t>::type;
+
+size_t gemv_lds_bytes(bool x_f32, int mr, int kslice) {
+  return (size_t)mr * kslice * (x_f32 ? 4 : 2) + (size_t)mr * (kslice / 64) * 4 * sizeof(float);
+}
+
+template <int BITS, int MR, int NTW, bool X_F32, typename ST>
+__global__ void __launch_bounds__(kBlockThreads) gemv_kernel(LaunchArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  using XT = XStore<X_F32>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, kg = lane >> 4;
+  const int item = xcd_item(blockIdx.x, a.nTB * a.S);
+  const int tb = item / a.S, s = item - tb * a.S;
+  const int nT = a.N / kTileN, nC = a.K / kChunkK;
+  const int c0 = (int)((long)s * nC / a.S), c1 = (int)((long)(s + 1) * nC / a.S);
+  const int ks = (c1 - c0) * kChunkK, gs = ks / 64;
+  const int tile0 = (tb * kWaves + wave) * NTW;
+  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
+  XT* xs = reinterpret_cast<XT*>(lds);                                   // [MR][ks]
+  float* xq = reinterpret_cast<float*>(lds + (size_t)MR * ks * sizeof(XT));  // [MR][gs][4]
+
+  // Stage the activation slice, 16 bytes per thread per step.
+  {
+    constexpr int per16 = 16 / sizeof(XT);
+    const int vecs_per_row = ks / per16;
+    const XT* xg = reinterpret_cast<const XT*>(a.x);
+    for (int idx = threadIdx.x; idx < a.M * vecs_per_row; idx += kBlockThreads) {
+      const int m = idx / vecs_per_row, v = idx - m * vecs_per_row;
+      const uint4 val = *reinterpret_cast<const uint4*>(xg + (long)m * a.ldx +
+                                                        (long)kChunkK * c0 + v * per16);
+      *reinterpret_cast<uint4*>(xs + (long)m * ks + v * per16) = val;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.M * gs * 4; idx += kBlockThreads) {
+    const int m = idx / (gs * 4), rem = idx - m * gs * 4;
+    const XT* p = xs + (long)m * ks + 16 * rem;  // rem = g*4 + quarter
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (X_F32)
+        sum += p[i];
+      else
+        sum += bf16_to_f32(p[i]);
+    }
+    xq[idx] = sum;
+  }
+  __syncthreads();
+
+  float acc[NTW][MR];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) acc[nt][m] = 0.f;
+
+  if (tile0 < nT && c0 < c1) {
+    bool tvalid[NTW];
+    const uint32_t* cptr[NTW];
+    const ST* sptr[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int t = tile0 + nt < nT ? tile0 + nt : nT - 1;
+      tvalid[nt] = tile0 + nt < nT;
+      cptr[nt] = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
+      sptr[nt] = sbp + ((long)t * nC * kTileN + r) * 4;
+    }
+    uint32_t W[NTW][BITS];
+    SBPair<ST> SBv[NTW];
+    auto load_chunk = [&](int c, uint32_t (&Wd)[NTW][BITS], SBPair<ST> (&Sd)[NTW]) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const uint32_t* p = cptr[nt] + (long)c * 64 * BITS;
+#pragma unroll
+        for (int j = 0; j < BITS; ++j) Wd[nt][j] = __builtin_nontemporal_load(p + j);
+        Sd[nt].load(sptr[nt] + (long)c * kTileN * 4);
+      }
+    };
+    load_chunk(c0, W, SBv);
+    for (int c = c0; c < c1; ++c) {
+      uint32_t Wn[NTW][BITS];
+      SBPair<ST> Sn[NTW];
+      if (c + 1 < c1) load_chunk(c + 1, Wn, Sn);
+      const int cl = c - c0;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        if (!tvalid[nt]) continue;
+        uint32_t P[16];
+        unpack_pairs<BITS>(W[nt], P);
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const float sc = SBv[nt].s(gp);
+          const float bp = SBv[nt].b(gp) - 128.f * sc;
+          const int kl = kChunkK * cl + 64 * gp + 16 * kg;  // lane's 16 columns
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            if (m >= a.M) break;
+            float dot = 0.f;
+            if constexpr (X_F32) {
+              const float4* xp = reinterpret_cast<const float4*>(xs + (long)m * ks + kl);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float4 xv = xp[v];
+                const uint32_t p0 = P[8 * gp + 2 * v], p1 = P[8 * gp + 2 * v + 1];
+                dot = fmaf(__uint_as_float(p0 << 16), xv.x, dot);
+                dot = fmaf(__uint_as_float(p0 & 0xFFFF0000u), xv.y, dot);
+                dot = fmaf(__uint_as_float(p1 << 16), xv.z, dot);
+                dot = fmaf(__uint_as_float(p1 & 0xFFFF0000u), xv.w, dot);
+              }
+            } else {
+              const uint4* xp = reinterpret_cast<const uint4*>(xs + (long)m * ks + kl);
+#pragma unroll
+              for (int v = 0; v < 2; ++v) {
+                const uint4 xv = xp[v];
+                const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  dot = __builtin_amdgcn_fdot2_f32_bf16(
+                      __builtin_bit_cast(bf16x2, P[8 * gp + 4 * v + e]),
+                      __builtin_bit_cast(bf16x2, xw[e]), dot, false);
+              }
+            }
+            const float xsum = xq[((long)m * gs + 2 * cl + gp) * 4 + kg];
+            acc[nt][m] = fmaf(sc, dot, fmaf(bp, xsum, acc[nt][m]));
+          }
+        }
+      }
+      if (c + 1 < c1) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+          for (int j = 0; j < BITS; ++j) W[nt][j] = Wn[nt][j];
+          SBv[nt] = Sn[nt];
+        }
+      }
+    }
+  }
+  // Add the four quarters: (q0+q1) + (q2+q3) on every lane.
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      acc[nt][m] += __shfl_xor(acc[nt][m], 16);
+      acc[nt][m] += __shfl_xor(acc[nt][m], 32);
+    }
+
+  if (a.S == 1) {
+    if (tile0 >= nT || kg != 0) return;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      if (tile0 + nt >= nT) continue;
+      const int n = (tile0 + nt) * kTileN + r;
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        if (m < a.M) store_y<X_F32>(a.y, (long)m * a.ldy + n, acc[nt][m]);
+    }
+    return;
+  }
+  if (tile0 < nT && kg == 0) {
+    float* part = a.part + (long)s * a.M * a.N;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      if (tile0 + nt >= nT) continue;
+      const int n = (tile0 + nt) * kTileN + r;
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        if (m < a.M) __builtin_nontemporal_store(acc[nt][m], part + (long)m * a.N + n);
+    }
+  }
+  const int n0 = tb * kWaves * NTW * kTileN;
+  const int n1 = min(a.N, n0 + kWaves * NTW * kTileN);
+  fold_partials<X_F32>(a, tb, n0, n1);
+}
+
+// ---------------------------------------------------------------------------
+// HBM read probe: every thread streams 16-byte words with a grid stride.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) probe_kernel(const u32x4* __restrict__ buf, long n16,
+                                                    uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  const long stride = (long)gridDim.x * blockDim.x;
+  long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 v0 = __builtin_nontemporal_load(buf + i);
+    const u32x4 v1 = __builtin_nontemporal_load(buf + i + stride);
+    const u32x4 v2 = __builtin_nontemporal_load(buf + i + 2 * stride);
+    const u32x4 v3 = __builtin_nontemporal_load(buf + i + 3 * stride);
+    acc ^= v0[0] ^ v1[1] ^ v2[2] ^ v3[3] ^ v0[3] ^ v1[0] ^ v2[1] ^ v3[2];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(buf + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  acc ^= __shfl_xor(acc, 1);
+  if (threadIdx.x == 0) sink[blockIdx.x] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+static inline unsigned blocks_for(long threads, int per) { return (unsigned)((threads + per - 1) / per); }
+
+hipError_t launch_repack(int bits, bool sb_f32, const uint32_t* w, const void* scales,
+                         const void* biases, uint32_t* codes, void* sb, int N, int K,
+                         hipStream_t st) {
+  const long threads = (long)(N / kTileN) * (K / kChunkK) * 64;
+  const unsigned grid = blocks_for(threads, 256);
+  if (bits == 3 && !sb_f32)
+    repack_kernel<3, uint16_t><<<grid, 256, 0, st>>>(w, (const uint16_t*)scales, (const uint16_t*)biases, codes, (uint16_t*)sb, N, K);
+  else if (bits == 3)
+    repack_kernel<3, float><<<grid, 256, 0, st>>>(w, (const float*)scales, (const float*)biases, codes, (float*)sb, N, K);
+  else if (!sb_f32)
+    repack_kernel<4, uint16_t><<<grid, 256, 0, st>>>(w, (const uint16_t*)scales, (const uint16_t*)biases, codes, (uint16_t*)sb, N, K);
+  else
+    repack_kernel<4, float><<<grid, 256, 0, st>>>(w, (const float*)scales, (const float*)biases, codes, (float*)sb, N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_unpack(int bits, const uint32_t* codes, uint8_t* out, int N, int K,
+                               hipStream_t st) {
+  const long threads = (long)(N / kTileN) * (K / kChunkK) * 64;
+  const unsigned grid = blocks_for(threads, 256);
+  if (bits == 3)
+    debug_unpack_kernel<3><<<grid, 256, 0, st>>>(codes, out, N, K);
+  else
+    debug_unpack_kernel<4><<<grid, 256, 0, st>>>(codes, out, N, K);
+  return hipGetLastError();
+}
+
+template <int BITS, typename ST>
+static hipError_t mfma_dispatch(int mt, int ntw, const LaunchArgs& a, hipStream_t st) {
+  const unsigned grid = (unsigned)(a.nTB * a.S);
+#define QMM_MFMA(MTV, NTV)                                                    \
+  if (mt == MTV && ntw == NTV) {                                              \
+    mfma_kernel<BITS, MTV, NTV, ST><<<grid, kBlockThreads, 0, st>>>(a);      \
+    return hipGetLastError();                                                 \
+  }
+  QMM_MFMA(1, 1) QMM_MFMA(1, 2) QMM_MFMA(1, 4)
+  QMM_MFMA(2, 1) QMM_MFMA(2, 2) QMM_MFMA(2, 4)
+  QMM_MFMA(4, 1) QMM_MFMA(4, 2)
+  QMM_MFMA(8, 1)
+#undef QMM_MFMA
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, const LaunchArgs& a,
+                       hipStream_t st) {
+  if (bits == 3) return sb_f32 ? mfma_dispatch<3, float>(mt, ntw, a, st) : mfma_dispatch<3, uint16_t>(mt, ntw, a, st);
+  return sb_f32 ? mfma_dispatch<4, float>(mt, ntw, a, st) : mfma_dispatch<4, uint16_t>(mt, ntw, a, st);
+}
+
+template <int BITS, bool XF, typename ST>
+static hipError_t gemv_dispatch(int mr, int ntw, const LaunchArgs& a, size_t lds,
+                                hipStream_t st) {
+  const unsigned grid = (unsigned)(a.nTB * a.S);
+#define QMM_GEMV(MRV, NTV)                                                          \
+  if (mr == MRV && ntw == NTV) {                                                    \
+    gemv_kernel<BITS, MRV, NTV, XF, ST><<<grid, kBlockThreads, lds, st>>>(a);      \
+    return hipGetLastError();                                                       \
+  }
+  QMM_GEMV(1, 1) QMM_GEMV(1, 2) QMM_GEMV(1, 4)
+  QMM_GEMV(2, 1) QMM_GEMV(2, 2)
+  QMM_GEMV(4, 1) QMM_GEMV(4, 2)
+  QMM_GEMV(8, 1)
+#undef QMM_GEMV
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const LaunchArgs& a,
+                       size_t lds_bytes, hipStream_t st) {
+  if (bits == 3) {
+    if (x_f32) return sb_f32 ? gemv_dispatch<3, true, float>(mr, ntw, a, lds_bytes, st) : gemv_dispatch<3, true, uint16_t>(mr, ntw, a, lds_bytes, st);
+    return sb_f32 ? gemv_dispatch<3, false, float>(mr, ntw, a, lds_bytes, st) : gemv_dispatch<3, false, uint16_t>(mr, ntw, a, lds_bytes, st);
+  }
+  if (x_f32) return sb_f32 ? gemv_dispatch<4, true, float>(mr, ntw, a, lds_bytes, st) : gemv_dispatch<4, true, uint16_t>(mr, ntw, a, lds_bytes, st);
+  return sb_f32 ? gemv_dispatch<4, false, float>(mr, ntw, a, lds_bytes, st) : gemv_dispatch<4, false, uint16_t>(mr, ntw, a, lds_bytes, st);
+}
+
+hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {
+  probe_kernel<<<grid, 256, 0, st>>>(reinterpret_cast<const u32x4*>(buf), (long)(bytes / 16), sink);
+  return hipGetLastError();
+}
+
+}  // namespace qmm

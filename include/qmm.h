@@ -1,0 +1,166 @@
+/*
+ * qmm.h -- C ABI of libqmm: y = x . W^T over MLX-style affine group-quantized
+ * weights on AMD MI355X (gfx950).
+ *
+ * The operation.  [P1] = page "@mlx-bun/inference 0.0.0-stage -> 1.0.0"
+ * (diffend npm page 53).
+ *   - affine-split-mma.ts, header comment: matmul over MLX affine 3- or 4-bit,
+ *     group-64 weights, y = x . W^T, for any number of activation rows; the
+ *     row count is read at run time with one pipeline per projection shape.
+ *   - affine-split-mma.ts, HEADER comment and helper affine_unit; affine3-mma.ts
+ *     helper affine_q3; affine4-mma.ts helper affine_q4: codes are `bits`-bit
+ *     fields of MLX's LSB-first bit stream of uint32 words, a 3-bit field may
+ *     straddle two words, a 4-bit field never does.
+ *   - affine3-mma.ts / affine4-mma.ts kernel bodies: row n of w starts at byte
+ *     n*K*bits/8; scale and bias of (row n, group g) sit at n*(K/64)+g; the
+ *     weight is scale*q + bias.
+ *   - affine-split-mma.ts, affineSplitMma(): x [..., K] times W^T gives
+ *     [..., N] in x's dtype; it borrows its inputs and throws when there are
+ *     no rows.  affineSplitMmaEligible(): a separate yes/no predicate (affine,
+ *     group 64, bits 3 or 4, shape rules) under which the caller falls back.
+ * So for rows m < M and outputs n < N:
+ *     y[m][n] = sum_k x[m][k] * (scale[n][k/64] * q(n,k) + bias[n][k/64]).
+ * Summation order is the kernels' own (not bit-identical to any other
+ * implementation); each kernel is deterministic run to run.
+ *
+ * Memory.  Every pointer argument that names data is a DEVICE pointer
+ * (hipMalloc'd or a framework's device allocation) owned by the caller and
+ * only borrowed until the enqueued work completes.  `stream` is a
+ * hipStream_t (NULL = the default stream).  qmm_run and qmm_prepack only
+ * enqueue work: they never synchronize and never allocate device memory.
+ *
+ * Errors.  Every entry point validates its arguments on the host before any
+ * HIP call and returns a negative qmm_status on failure, with a message for
+ * qmm_last_error().  QMM_ERR_INVALID_ARG: the format or an argument is wrong
+ * (the page's "throw").  QMM_ERR_UNSUPPORTED: a valid format that no kernel
+ * here covers (the page's "not eligible": the caller should fall back).
+ */
+#ifndef QMM_H_
+#define QMM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMM_OK = 0,
+  QMM_ERR_INVALID_ARG = -1,
+  QMM_ERR_UNSUPPORTED = -2,
+  QMM_ERR_HIP = -3,
+  QMM_ERR_WORKSPACE = -4,
+  QMM_ERR_NO_DEVICE = -5
+} qmm_status;
+
+/* Element types of x/y and of scales/biases. */
+typedef enum { QMM_F32 = 0, QMM_BF16 = 1 } qmm_dtype;
+
+/* Kernel families (qmm_run picks one; qmm_run_ex can force one). */
+typedef enum {
+  QMM_VARIANT_AUTO = 0,
+  QMM_VARIANT_GEMV = 1,  /* vector-ALU kernel, activations staged in LDS; 1..8 rows per pass */
+  QMM_VARIANT_MFMA = 2   /* matrix-core kernel (bf16 in, f32 accumulate); bf16 activations only */
+} qmm_variant;
+
+/* Shape and format of one projection.  bits: 3 or 4 (other MLX widths are
+ * UNSUPPORTED).  group_size: 64.  K: multiple of 128.  N: multiple of 16.
+ * max_rows: the largest row count qmm_run will be given (>= 1).
+ * x_dtype: dtype of x and y.  sb_dtype: dtype of scales and biases.
+ * flags: must be 0. */
+typedef struct {
+  int32_t bits;
+  int32_t group_size;
+  int64_t K;
+  int64_t N;
+  int32_t max_rows;
+  int32_t x_dtype;
+  int32_t sb_dtype;
+  uint32_t flags;
+} qmm_desc;
+
+typedef struct qmm_plan qmm_plan;
+
+typedef struct {
+  uint64_t launches[3];   /* indexed by qmm_variant: kernels run per family */
+  int32_t last_variant;   /* family of the last qmm_run */
+  int32_t last_ntw;       /* output tiles (16 rows of W each) per wavefront */
+  int32_t last_splitk;    /* K splits folded through the workspace */
+  int32_t last_grid;      /* workgroups launched */
+} qmm_stats;
+
+/* Validate `desc` and build a plan (host state only; no device memory).
+ * Returns QMM_OK and *out, or an error and *out = NULL. */
+qmm_status qmm_create(const qmm_desc* desc, qmm_plan** out);
+
+/* Free a plan.  NULL is allowed. */
+void qmm_destroy(qmm_plan* plan);
+
+/* Bytes of the two buffers of the kernel-native weight layout written by
+ * qmm_prepack: packed codes (exactly N*K*bits/8, the MLX byte count) and
+ * packed scales+biases (exactly 2*N*(K/64) elements of sb_dtype). */
+qmm_status qmm_packed_bytes(const qmm_plan* plan, size_t* codes_bytes, size_t* sb_bytes);
+
+/* One-time weight loader: MLX layout -> kernel-native layout.
+ *   w       uint32 [N, K*bits/32]  (MLX packed words, row-major)
+ *   scales  sb_dtype [N, K/64]
+ *   biases  sb_dtype [N, K/64]
+ *   codes_out, sb_out: buffers of qmm_packed_bytes().
+ * In the native layout the 16 rows x 128 columns of W that one wavefront
+ * multiplies are contiguous, and each lane's codes are ordered so that the
+ * unpack to bf16 pairs is a shift and one and-or per pair.  Enqueued on
+ * `stream`; the inputs may be freed once it completes. */
+qmm_status qmm_prepack(const qmm_plan* plan, const uint32_t* w, const void* scales,
+                       const void* biases, void* codes_out, void* sb_out, void* stream);
+
+/* Device workspace that qmm_run needs for `rows` rows (split-K partial sums
+ * and per-tile tickets).  0 means none.  The workspace must be zero-filled
+ * before its first use; every completed qmm_run leaves its ticket words at
+ * zero again, so it can be reused by later calls of the same plan on the same
+ * stream.  Calls that overlap in time must not share a workspace. */
+size_t qmm_workspace_bytes(const qmm_plan* plan, int32_t rows);
+
+/* y[rows, N] = x[rows, K] . W^T with W given in the native layout.
+ *   x: x_dtype [rows, K] row-contiguous, 16-byte aligned;
+ *   y: x_dtype [rows, N] row-contiguous; only rows < `rows` are written;
+ *   workspace: >= qmm_workspace_bytes(plan, rows) bytes (may be NULL when
+ *   that is 0).
+ * 1 <= rows <= max_rows, else QMM_ERR_INVALID_ARG (the page's "no rows"). */
+qmm_status qmm_run(const qmm_plan* plan, const void* x, const void* codes, const void* sb,
+                   void* y, int32_t rows, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* qmm_run with a forced kernel family and launch shape, for tests and
+ * measurement.  ntw (output tiles per wavefront, 1..8) and splitk (>= 1)
+ * may be 0 for the plan's choice. */
+qmm_status qmm_run_ex(const qmm_plan* plan, int32_t variant, int32_t ntw, int32_t splitk,
+                      const void* x, const void* codes, const void* sb, void* y,
+                      int32_t rows, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace needed by qmm_run_ex with the same variant/ntw/splitk. */
+size_t qmm_workspace_bytes_ex(const qmm_plan* plan, int32_t variant, int32_t ntw,
+                              int32_t splitk, int32_t rows);
+
+/* Test hook: decode the native layout with the compute kernels' own unpack
+ * and write the codes q(n,k) as uint8 [N, K] (device buffer). */
+qmm_status qmm_debug_unpack(const qmm_plan* plan, const void* codes, uint8_t* codes_nk,
+                            void* stream);
+
+/* Launch counters of a plan (host memory). */
+qmm_status qmm_get_stats(const qmm_plan* plan, qmm_stats* out);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* qmm_last_error(void);
+
+/* Measurement hook: stream-read `bytes` (multiple of 16) of device memory at
+ * `buf` and write one uint32 per workgroup to `sink` (`grid` entries;
+ * grid = 0 picks 4096).  Used to measure the achievable HBM read rate. */
+qmm_status qmm_hbm_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H_ */

@@ -1,0 +1,70 @@
+"""Helpers for the GPU parity tests: run a problem through the C ABI and
+compare with the float64 oracle element by element."""
+import sys
+
+import numpy as np
+
+import oracle
+from bit_quantized_matmul_affine_amd import binding as b
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def y_to_f64(y_bits: np.ndarray, x_dtype: str) -> np.ndarray:
+    if x_dtype == "bf16":
+        return oracle.decode_bf16(y_bits)
+    return y_bits.astype(np.float64)
+
+
+class Runner:
+    """A problem on the device: plan, native weights, activations."""
+
+    def __init__(self, p, max_rows=None, device="cuda"):
+        import torch
+        self.p = p
+        self.lin = b.QuantizedLinear(p, max_rows=max_rows or p.M, device=device)
+        self.x = b.to_device(p.x, device)
+        torch.cuda.synchronize()
+
+    def run(self, rows=None, **kw):
+        import torch
+        rows = rows or self.p.M
+        y = self.lin(self.x[:rows], **kw)
+        torch.cuda.synchronize()
+        return b.to_numpy_bits(y)
+
+
+def check_against_oracle(p, y_bits, rows=None, sample=None, threads=8, label=""):
+    """Element-wise |y - y_ref| <= tol; sample=(count, seed) checks a random
+    subset computed one by one by the oracle."""
+    rows = rows or p.M
+    y = y_to_f64(y_bits, p.x_dtype)[:rows]
+    x = p.x[:rows]
+    sx, mw = oracle.bound_terms(p.bits, p.K, x, p.w, p.scales, p.biases)
+    c = oracle.tolerance_coefficient(p.x_dtype)
+    if sample is None:
+        ref = oracle.matmul(p.bits, p.K, x, p.w, p.scales, p.biases, threads=threads)
+        tol = c * np.outer(sx, mw) + 1e-6
+        err = np.abs(y - ref)
+        assert np.all(np.isfinite(y)), label + ": non-finite output"
+        worst = np.unravel_index(np.argmax(err / tol), err.shape)
+        ratio = float((err / tol)[worst])
+        assert ratio <= 1.0, "%s: err %.3g > tol %.3g at %s (ratio %.3f)" % (
+            label, err[worst], tol[worst], worst, ratio)
+        return ratio
+    count, seed = sample
+    rng = np.random.default_rng(seed)
+    ms = rng.integers(0, rows, count)
+    ns = rng.integers(0, p.N, count)
+    ref = oracle.matmul_at(p.bits, p.K, x, p.w, p.scales, p.biases, ms, ns)
+    tol = c * sx[ms] * mw[ns] + 1e-6
+    got = y[ms, ns]
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(y)), label + ": non-finite output"
+    i = int(np.argmax(err / tol))
+    ratio = float(err[i] / tol[i])
+    assert ratio <= 1.0, "%s: err %.3g > tol %.3g at (%d,%d)" % (label, err[i], tol[i], ms[i], ns[i])
+    return ratio

@@ -1,0 +1,99 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point include/qmm.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_matmul_affine_amd import binding as b
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qmm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for must in ("qmm_create", "qmm_run", "qmm_destroy", "qmm_prepack", "qmm_debug_unpack",
+                 "qmm_workspace_bytes", "qmm_last_error", "qmm_get_stats"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = b.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in b.SIGNATURES, name
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=7), b.QMM_ERR_INVALID_ARG),          # not an MLX width
+    (dict(bits=2), b.QMM_ERR_UNSUPPORTED),          # MLX width, no kernel here
+    (dict(bits=8), b.QMM_ERR_UNSUPPORTED),
+    (dict(group_size=48), b.QMM_ERR_INVALID_ARG),
+    (dict(group_size=128), b.QMM_ERR_UNSUPPORTED),
+    (dict(K=500), b.QMM_ERR_INVALID_ARG),           # not a multiple of the group
+    (dict(K=192), b.QMM_ERR_UNSUPPORTED),           # group-aligned, not 128-aligned
+    (dict(N=24), b.QMM_ERR_UNSUPPORTED),
+    (dict(N=0), b.QMM_ERR_INVALID_ARG),
+    (dict(max_rows=0), b.QMM_ERR_INVALID_ARG),
+    (dict(x_dtype="f16"), b.QMM_ERR_INVALID_ARG),
+])
+def test_create_rejects(kw, status):
+    args = dict(bits=4, K=512, N=512, max_rows=4, x_dtype="bf16", group_size=64)
+    args.update(kw)
+    if args["x_dtype"] == "f16":
+        d = b.QmmDesc(args["bits"], 64, args["K"], args["N"], args["max_rows"], 7, 1, 0)
+        h = ctypes.c_void_p()
+        assert b.lib().qmm_create(ctypes.byref(d), ctypes.byref(h)) == status
+        assert h.value is None
+        return
+    with pytest.raises(b.QmmError) as ei:
+        b.Plan(args["bits"], args["K"], args["N"], args["max_rows"], args["x_dtype"],
+               group_size=args["group_size"])
+    assert ei.value.status == status
+
+
+def test_create_accepts_every_workload_shape():
+    for bits, K, N in [(4, 512, 512), (4, 5120, 10240), (3, 5120, 10240), (4, 3840, 15360),
+                       (4, 15360, 3840), (4, 8192, 28672)]:
+        p = b.Plan(bits, K, N, 128, "bf16")
+        cb, sbb = p.packed_bytes()
+        assert cb == N * K * bits // 8          # same byte count as the MLX layout
+        assert sbb == 2 * N * (K // 64) * 2
+
+
+def test_run_validation_without_gpu():
+    L = b.lib()
+    p = b.Plan(3, 5120, 10240, 16, "bf16")
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+    # rows out of range: the page's "no rows" error
+    assert L.qmm_run(p.handle, fake, fake, fake, fake, 0, None, 0, None) == b.QMM_ERR_INVALID_ARG
+    assert L.qmm_run(p.handle, fake, fake, fake, fake, 17, None, 0, None) == b.QMM_ERR_INVALID_ARG
+    # NULL and misaligned pointers
+    assert L.qmm_run(p.handle, None, fake, fake, fake, 1, None, 0, None) == b.QMM_ERR_INVALID_ARG
+    assert L.qmm_run(p.handle, ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, 1, None, 0,
+                     None) == b.QMM_ERR_INVALID_ARG
+    # a forced K split needs a workspace
+    assert L.qmm_run_ex(p.handle, b.VARIANT_MFMA, 1, 4, fake, fake, fake, fake, 4, None, 0,
+                        None) == b.QMM_ERR_WORKSPACE
+    assert b"workspace" in L.qmm_last_error()
+    # MFMA takes bf16 activations only
+    pf = b.Plan(4, 512, 512, 1, "f32")
+    assert L.qmm_run_ex(pf.handle, b.VARIANT_MFMA, 0, 0, fake, fake, fake, fake, 1, None, 0,
+                        None) == b.QMM_ERR_UNSUPPORTED
+    assert L.qmm_run(None, fake, fake, fake, fake, 1, None, 0, None) == b.QMM_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_are_bounded():
+    """Partial sums only: far below the size of a materialized W."""
+    p = b.Plan(3, 5120, 10240, 64, "bf16")
+    for rows in (1, 9, 16, 32, 64):
+        ws = p.workspace_bytes(rows)
+        assert ws <= 16 * rows * 10240 * 4 + 65536
+        assert ws < 10240 * 5120 * 2 // 8

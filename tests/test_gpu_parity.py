@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bar: unpacked codes bit-exact; outputs within
+    |y - y_ref| <= c * sum_k|x(m,k)| * max_k|W(n,k)| + 1e-6,
+c = 1e-3 for f32 activations and 8e-3 for bf16 activations, element by element.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_matmul_affine_amd import binding as b
+from bit_quantized_matmul_affine_amd import synth
+from tests.gpu_util import Runner, check_against_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    b.lib()
+
+
+# ------------------------------------------------------------------ unpack
+
+@pytest.mark.parametrize("bits,K,N", [(3, 128, 16), (4, 128, 16), (3, 640, 48), (4, 384, 80)])
+def test_debug_unpack_small(bits, K, N):
+    say("debug_unpack", bits, K, N)
+    p = synth.small(21, bits=bits, K=K, N=N, M=1)
+    r = Runner(p)
+    got = r.lin.plan.debug_unpack(r.lin.codes).cpu().numpy()
+    assert np.array_equal(got, oracle.unpack(bits, K, N, p.w))
+
+
+@pytest.mark.parametrize("idx", [0, 1, 2, 3, 4])
+def test_debug_unpack_workloads(idx):
+    for p in synth.workload(idx, M=1) if idx == 2 else synth.workload(idx):
+        say("debug_unpack workload", idx, p.name)
+        r = Runner(p)
+        got = r.lin.plan.debug_unpack(r.lin.codes).cpu().numpy()
+        assert np.array_equal(got, oracle.unpack(p.bits, p.K, p.N, p.w)), p.name
+        del r
+
+
+def test_debug_unpack_extreme_words():
+    """All-ones and single-bit words: every code at its maximum, and each code
+    boundary, through the device unpack."""
+    for bits in (3, 4):
+        K, N = 256, 32
+        p = synth.small(1, bits=bits, K=K, N=N, M=1)
+        w = np.zeros_like(p.w)
+        w[0:16] = 0xFFFFFFFF
+        for n in range(16, 32):
+            w[n, :] = np.uint32(1) << np.uint32(n % 32)
+        p.w = w
+        r = Runner(p)
+        got = r.lin.plan.debug_unpack(r.lin.codes).cpu().numpy()
+        assert np.array_equal(got, oracle.unpack(bits, K, N, w))
+
+
+# ------------------------------------------------------------------ small parity
+
+SMALL = [
+    # bits, K, N, M, x_dtype, sb_dtype
+    (4, 128, 16, 1, "bf16", "bf16"),
+    (3, 128, 16, 1, "bf16", "bf16"),
+    (4, 640, 208, 3, "bf16", "bf16"),     # ragged tile blocks
+    (3, 640, 208, 5, "bf16", "bf16"),
+    (3, 1280, 96, 9, "bf16", "bf16"),
+    (4, 1280, 96, 16, "bf16", "bf16"),
+    (3, 512, 144, 17, "bf16", "bf16"),
+    (4, 384, 64, 33, "bf16", "bf16"),
+    (3, 768, 48, 64, "bf16", "bf16"),
+    (4, 256, 32, 100, "bf16", "bf16"),
+    (3, 256, 32, 130, "bf16", "bf16"),    # two MFMA row blocks
+    (4, 512, 64, 1, "f32", "f32"),
+    (3, 512, 64, 7, "f32", "f32"),
+    (4, 512, 64, 11, "f32", "f32"),       # two GEMV row blocks
+    (4, 512, 64, 2, "bf16", "f32"),
+    (3, 512, 64, 2, "f32", "bf16"),
+]
+
+
+def _variants(x_dtype, M):
+    out = ["gemv"]
+    if x_dtype == "bf16":
+        out.append("mfma")
+    return out
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "b%d_K%d_N%d_M%d_%s_%s" % c)
+def test_small_parity(case):
+    bits, K, N, M, xd, sd = case
+    p = synth.small(100 + M, bits=bits, K=K, N=N, M=M, x_dtype=xd, sb_dtype=sd)
+    r = Runner(p)
+    for v in _variants(xd, M):
+        for ntw, s in [(0, 0), (1, 1), (2, 2), (1, 3)]:
+            if s > K // 128:
+                continue
+            label = "%s %s ntw=%d S=%d" % (case, v, ntw, s)
+            say(label)
+            y = r.run(variant=v, ntw=ntw, splitk=s)
+            check_against_oracle(p, y, label=label)
+
+
+# ------------------------------------------------------------------ properties
+
+def test_determinism_and_row_independence():
+    p = synth.small(7, bits=3, K=2560, N=320, M=16)
+    r = Runner(p)
+    for v in ("mfma", "gemv"):
+        say("determinism", v)
+        a = r.run(variant=v, ntw=1, splitk=4)
+        b2 = r.run(variant=v, ntw=1, splitk=4)
+        assert np.array_equal(a, b2)
+        if v == "mfma":
+            a9 = r.run(rows=9, variant=v, ntw=1, splitk=4)
+            assert np.array_equal(a9[:9], a[:9])
+
+
+def test_rows_past_m_and_past_end_untouched():
+    import torch
+    p = synth.small(8, bits=4, K=512, N=64, M=5)
+    r = Runner(p, max_rows=8)
+    for v in ("mfma", "gemv"):
+        say("canary", v)
+        out = torch.full((9, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+        r.lin.plan.run(r.x[:5], r.lin.codes, r.lin.sb, out=out[:5], variant=v, splitk=2)
+        torch.cuda.synchronize()
+        o = out.float().cpu().numpy()
+        assert np.all(o[5:] == 7.0)
+        check_against_oracle(p, b.to_numpy_bits(out[:5]), label="canary " + v)
+
+
+def test_non_default_stream_and_workspace_reuse():
+    import torch
+    p = synth.small(9, bits=3, K=1024, N=128, M=16)
+    r = Runner(p, max_rows=16)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for rows in (16, 3, 9, 1, 16):   # tickets must be re-armed between calls
+            say("stream/workspace rows", rows)
+            y = r.lin.plan.run(r.x[:rows], r.lin.codes, r.lin.sb, variant="mfma", splitk=4,
+                               stream=s)
+            s.synchronize()
+            check_against_oracle(p.rows(rows), b.to_numpy_bits(y), label="rows %d" % rows)
+
+
+def test_stats_report_the_family_that_ran():
+    p = synth.small(10, bits=4, K=512, N=64, M=4)
+    r = Runner(p)
+    r.run(variant="gemv")
+    st = r.lin.plan.stats()
+    assert st["last_variant"] == "gemv" and st["launches"]["gemv"] >= 1
+    r.run(variant="mfma")
+    st = r.lin.plan.stats()
+    assert st["last_variant"] == "mfma" and st["launches"]["mfma"] >= 1
+
+
+# ------------------------------------------------------------------ workloads
+
+@pytest.mark.parametrize("variant", ["auto", "gemv"])
+def test_workload0_full(variant):
+    (p,) = synth.workload(0)
+    say("workload 0", variant)
+    r = Runner(p)
+    check_against_oracle(p, r.run(variant=variant), label="w0 " + variant)
+
+
+@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma"])
+def test_workload1_full(variant):
+    (p,) = synth.workload(1)
+    say("workload 1", variant)
+    r = Runner(p)
+    check_against_oracle(p, r.run(variant=variant), label="w1 " + variant)
+
+
+@pytest.mark.parametrize("rows", synth.C2_ROWS)
+def test_workload2_full(rows):
+    (p,) = synth.workload(2)
+    r = Runner(p, max_rows=64)
+    variants = ["auto", "mfma"] + (["gemv"] if rows <= 9 else [])
+    for v in variants:
+        say("workload 2 rows", rows, v)
+        check_against_oracle(p.rows(rows), r.run(rows=rows, variant=v), rows=rows,
+                             label="w2 M=%d %s" % (rows, v))
+
+
+def test_workload3_full():
+    for p in synth.workload(3):
+        r = Runner(p)
+        for v in ("auto", "gemv", "mfma"):
+            say("workload 3", p.name, v)
+            check_against_oracle(p, r.run(variant=v), label="w3 %s %s" % (p.name, v))
+        del r
+
+
+def test_workload4_sampled():
+    (p,) = synth.workload(4)
+    say("workload 4")
+    r = Runner(p)
+    y = r.run()
+    check_against_oracle(p, y, sample=(3000, 4), label="w4 sampled")
+    # every output row and column is finite and rows are distinct results
+    yf = oracle.decode_bf16(y)
+    assert np.all(np.isfinite(yf))
