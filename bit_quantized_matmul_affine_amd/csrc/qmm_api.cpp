@@ -139,6 +139,18 @@ size_t cfg_workspace(const qmm_plan* p, const Cfg& c, int rows) {
   return ticket_bytes(p) + (size_t)c.S * r * p->d.N * sizeof(float);
 }
 
+// Largest workspace any row block of a `rows`-row call needs (blocks of a
+// call run one after another on the stream and share the workspace).
+size_t call_workspace(const qmm_plan* p, int rows, int variant, int ntw, int s) {
+  const Cfg c = plan_config(p, rows, variant, ntw, s);
+  size_t need = 0;
+  for (int r0 = 0; r0 < rows; r0 += c.rows_per_launch) {
+    const int rb = std::min(c.rows_per_launch, rows - r0);
+    need = std::max(need, cfg_workspace(p, plan_config(p, rb, variant, ntw, s), rb));
+  }
+  return need;
+}
+
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 qmm_status check_plan(const qmm_plan* p) {
@@ -171,7 +183,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int s_req, 
   const int s_eff = s_req ? s_req : p->env_splitk;
   const int variant = pick_variant(p, rows, variant_req);
   const Cfg c = plan_config(p, rows, variant, ntw_eff, s_eff);
-  const size_t need = cfg_workspace(p, c, rows);
+  const size_t need = call_workspace(p, rows, variant, ntw_eff, s_eff);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -300,8 +312,7 @@ size_t qmm_workspace_bytes_ex(const qmm_plan* p, int32_t variant, int32_t ntw, i
                               int32_t rows) {
   if (!p || rows < 1) return 0;
   const int v = pick_variant(p, rows, variant);
-  const Cfg c = plan_config(p, rows, v, ntw ? ntw : p->env_ntw, splitk ? splitk : p->env_splitk);
-  return cfg_workspace(p, c, rows);
+  return call_workspace(p, rows, v, ntw ? ntw : p->env_ntw, splitk ? splitk : p->env_splitk);
 }
 
 size_t qmm_workspace_bytes(const qmm_plan* p, int32_t rows) {
