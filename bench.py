@@ -1,0 +1,205 @@
+"""Benchmark of the 3-bit group-64 affine matmul, K=5120 -> N=10240, at
+M = 1, 9, 16, 32, 64 activation rows on one MI355X.
+
+One step = one matmul at each of the five row counts (the whole hot path:
+native weights streamed from HBM, unpacked, dequantized, multiplied, reduced,
+written), each on a different copy of the weights: the copies form a ring of
+more than 1 GiB, four times the 256 MB Infinity Cache, so every matmul reads
+its weights cold from HBM.  Inputs are resident in device memory before the
+timed region starts; the one-time repack to the native layout is outside it.
+
+Prints one JSON line (stdout).  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+K, N, BITS = 5120, 10240, 3
+ROWS = (1, 9, 16, 32, 64)
+HBM_PEAK_GBPS = 8000.0      # MI355X published HBM3E read+write peak
+RING_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes() -> int:
+    return N * K * BITS // 8 + 2 * N * (K // 64) * 2
+
+
+def algorithmic_bytes(m: int) -> int:
+    """Bytes one matmul must move: weights once, activations once, output once."""
+    return weight_bytes() + m * K * 2 + m * N * 2
+
+
+def cpu_baseline(problem, seconds: float = 12.0):
+    """The float64 oracle on the host cores: one full step (all five row
+    counts, every output), repeated until about `seconds` have passed."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for m in ROWS:
+            p = problem.rows(m)
+            oracle.matmul(BITS, K, p.x, p.w, p.scales, p.biases, threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds or reps >= 5:
+            break
+    dt = time.perf_counter() - t0
+    gbps = reps * len(ROWS) * weight_bytes() / dt / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full step(s): all %d outputs at each of M=%s, float64 oracle, %.1f s"
+                      % (reps, N, ",".join(map(str, ROWS)), dt)}
+
+
+def measure_hbm(torch, binding, gib: int = 4, reps: int = 5):
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    best = 0.0
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        binding.hbm_probe(buf, grid=4096)
+        e.record()
+        e.synchronize()
+        best = max(best, buf.numel() / (s.elapsed_time(e) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--variant", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM read probe")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    from bit_quantized_matmul_affine_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log("drawing inputs")
+    (prob,) = synth.workload(2)               # M=64 draw; smaller M use its first rows
+    plan = binding.Plan(BITS, K, N, max(ROWS), "bf16", "bf16")
+    lin = binding.QuantizedLinear(prob, max_rows=max(ROWS))
+    ring = max(2, -(-RING_BYTES // weight_bytes()))
+    log("ring of %d weight copies (%.2f GiB)" % (ring, ring * weight_bytes() / 2**30))
+    copies = [(lin.codes.clone(), lin.sb.clone()) for _ in range(ring)]
+    del lin
+    x = binding.to_device(prob.x)             # [64, K] bf16
+    ys = {m: torch.empty(m, N, dtype=torch.bfloat16, device="cuda") for m in ROWS}
+    ws = plan.workspace(max(plan.workspace_bytes(m) for m in ROWS), x.device)
+    torch.cuda.synchronize()
+
+    probe = None
+    if not args.no_probe:
+        log("HBM read probe")
+        probe = measure_hbm(torch, binding)
+
+    counter = [0]
+
+    def one_step(events=None):
+        for j, m in enumerate(ROWS):
+            codes, sb = copies[counter[0] % ring]
+            counter[0] += 1
+            if events is not None:
+                events[j][0].record()
+            plan.run(x[:m], codes, sb, out=ys[m], variant=args.variant, workspace=ws)
+            if events is not None:
+                events[j][1].record()
+
+    log("warmup %d steps" % args.warmup)
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in ROWS] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        one_step(ev[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+
+    per = {}
+    for j, m in enumerate(ROWS):
+        d = sorted(ev[i][j][0].elapsed_time(ev[i][j][1]) * 1e3 for i in range(args.steps))
+        mean = sum(d) / len(d)
+        med = d[len(d) // 2]
+        per[str(m)] = {
+            "us_mean": round(mean, 3), "us_median": round(med, 3),
+            "us_p10": round(d[len(d) // 10], 3), "us_p90": round(d[(9 * len(d)) // 10], 3),
+            "weight_GBps": round(weight_bytes() / (mean * 1e-6) / 1e9, 1),
+            "algorithmic_GBps": round(algorithmic_bytes(m) / (mean * 1e-6) / 1e9, 1),
+            "frac_of_8TBps": round(algorithmic_bytes(m) / (mean * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "tflops": round(2.0 * m * N * K / (mean * 1e-6) / 1e12, 2),
+        }
+        if probe:
+            per[str(m)]["frac_of_measured_peak"] = round(
+                weight_bytes() / (mean * 1e-6) / 1e9 / probe, 4)
+    st = plan.stats()
+    dominant = max(ROWS, key=lambda m: per[str(m)]["us_mean"])
+    dom = per[str(dominant)]
+    achieved = algorithmic_bytes(dominant) / (dom["us_mean"] * 1e-6) / 1e9
+    value = len(ROWS) * weight_bytes() / (ms_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        log("oracle CPU baseline")
+        cpu = cpu_baseline(prob)
+
+    out = {
+        "metric": "weight-stream GB/s over the 3-bit 5120->10240 sweep M=1,9,16,32,64 "
+                  "(with us/matmul and % of HBM peak per M)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "3-bit group-64 affine qmm K=5120 N=10240, M in {1,9,16,32,64}, "
+                               "bf16 activations/scales/biases, cold weights (%d-copy ring)" % ring,
+                   "variant": args.variant},
+        "per_rows": per,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "M=%d (%s)" % (dominant, st["last_variant"]),
+                     "bytes_per_launch": algorithmic_bytes(dominant),
+                     "us_per_launch": dom["us_mean"]},
+        "hbm_read_probe_GBps": round(probe, 1) if probe else None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

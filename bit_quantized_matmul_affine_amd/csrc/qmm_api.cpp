@@ -97,10 +97,10 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int s_req
   if (variant == QMM_VARIANT_MFMA) {
     c.rows_per_launch = qmm::kMaxMfmaRows;
     const int r = std::min(rows, qmm::kMaxMfmaRows);
-    c.tile_rows = round_up_pow2((r + 15) / 16, 8);
+    c.tile_rows = round_up_pow2((r + 15) / 16, 4);
     int ntw = c.tile_rows <= 2 ? 2 : 1;
     if (ntw_req) ntw = ntw_req;
-    const int cap = c.tile_rows <= 2 ? 4 : (c.tile_rows == 4 ? 2 : 1);
+    const int cap = c.tile_rows <= 2 ? 4 : 2;
     c.ntw = std::min(ntw >= 4 ? 4 : (ntw >= 2 ? 2 : 1), cap);
   } else {
     c.rows_per_launch = qmm::kMaxGemvRows;

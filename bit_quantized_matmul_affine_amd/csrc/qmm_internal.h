@@ -13,7 +13,7 @@ constexpr int kTileN = 16;
 constexpr int kChunkK = 128;
 constexpr int kWaves = 4;            // wavefronts per workgroup
 constexpr int kBlockThreads = 64 * kWaves;
-constexpr int kMaxMfmaRows = 128;    // rows per MFMA launch (8 tiles of 16)
+constexpr int kMaxMfmaRows = 64;     // rows per MFMA launch (4 tiles of 16)
 constexpr int kMaxGemvRows = 8;      // rows per vector-ALU launch
 
 struct LaunchArgs {

@@ -664,7 +664,6 @@ static hipError_t mfma_dispatch(int mt, int ntw, const LaunchArgs& a, hipStream_
   QMM_MFMA(1, 1) QMM_MFMA(1, 2) QMM_MFMA(1, 4)
   QMM_MFMA(2, 1) QMM_MFMA(2, 2) QMM_MFMA(2, 4)
   QMM_MFMA(4, 1) QMM_MFMA(4, 2)
-  QMM_MFMA(8, 1)
 #undef QMM_MFMA
   return hipErrorInvalidValue;
 }
