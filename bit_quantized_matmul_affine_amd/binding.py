@@ -32,10 +32,11 @@ SIGNATURES = {
     "qmm_packed_bytes": (_c.c_int, [_P, _P, _P]),
     "qmm_prepack": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P]),
     "qmm_workspace_bytes": (_c.c_size_t, [_P, _c.c_int32]),
-    "qmm_workspace_bytes_ex": (_c.c_size_t, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32]),
+    "qmm_workspace_bytes_ex": (_c.c_size_t, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
+                                              _c.c_int32]),
     "qmm_run": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _P, _c.c_size_t, _P]),
-    "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P, _P,
-                              _c.c_int32, _P, _c.c_size_t, _P]),
+    "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P,
+                              _P, _c.c_int32, _P, _c.c_size_t, _P]),
     "qmm_debug_unpack": (_c.c_int, [_P, _P, _P, _P]),
     "qmm_get_stats": (_c.c_int, [_P, _P]),
     "qmm_last_error": (_c.c_char_p, []),
@@ -163,9 +164,10 @@ class Plan:
                                  _ptr(sb), _stream(stream)))
         return codes, sb
 
-    def workspace_bytes(self, rows: int, variant: int = 0, ntw: int = 0, splitk: int = 0) -> int:
-        if variant or ntw or splitk:
-            return lib().qmm_workspace_bytes_ex(self._h, variant, ntw, splitk, rows)
+    def workspace_bytes(self, rows: int, variant: int = 0, ntw: int = 0, kwaves: int = 0,
+                        splitk: int = 0) -> int:
+        if variant or ntw or kwaves or splitk:
+            return lib().qmm_workspace_bytes_ex(self._h, variant, ntw, kwaves, splitk, rows)
         return lib().qmm_workspace_bytes(self._h, rows)
 
     def workspace(self, nbytes: int, device):
@@ -180,19 +182,19 @@ class Plan:
             self._ws[key] = ws
         return ws
 
-    def run(self, x, codes, sb, out=None, variant="auto", ntw: int = 0, splitk: int = 0,
-            stream=None, workspace=None):
+    def run(self, x, codes, sb, out=None, variant="auto", ntw: int = 0, kwaves: int = 0,
+            splitk: int = 0, stream=None, workspace=None):
         """y = x . W^T; x is [..., K] on the device, y is [..., N] in x's dtype."""
         import torch
         rows = x.numel() // self.K
         if out is None:
             out = torch.empty(*x.shape[:-1], self.N, dtype=x.dtype, device=x.device)
         v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
-        need = self.workspace_bytes(rows, v, ntw, splitk)
-        ws = workspace if workspace is not None else self.workspace(need, x.device)
-        wsb = ws.numel() if ws is not None else 0
-        _check(lib().qmm_run_ex(self._h, v, ntw, splitk, _ptr(x), _ptr(codes), _ptr(sb),
-                                _ptr(out), rows, _ptr(ws), wsb, _stream(stream)))
+        if workspace is None:
+            workspace = self.workspace(self.workspace_bytes(rows, v, ntw, kwaves, splitk), x.device)
+        wsb = workspace.numel() if workspace is not None else 0
+        _check(lib().qmm_run_ex(self._h, v, ntw, kwaves, splitk, _ptr(x), _ptr(codes), _ptr(sb),
+                                _ptr(out), rows, _ptr(workspace), wsb, _stream(stream)))
         return out
 
     def debug_unpack(self, codes, stream=None):

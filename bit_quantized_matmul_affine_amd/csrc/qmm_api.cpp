@@ -43,7 +43,8 @@ struct Cfg {
   int rows_per_launch;
   int tile_rows;  // mt (MFMA, 16-row tiles of x) or mr (GEMV rows)
   int ntw;        // W tiles per wavefront
-  int S;          // K splits
+  int wk;         // wavefronts of a workgroup that split K (MFMA)
+  int S;          // K splits across workgroups
   int nTB;        // tile blocks
   size_t lds;     // dynamic LDS bytes (GEMV)
 };
@@ -54,14 +55,14 @@ struct qmm_plan {
   qmm_desc d;
   int nT, nC;
   int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
-  int env_ntw, env_splitk;
+  int env_ntw, env_splitk, env_kwaves;
   mutable std::atomic<uint64_t> launches[3];
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
 };
 
 namespace {
 
-constexpr int kTargetBlocks = 1024;   // about four workgroups per compute unit
+constexpr int kMinBlocks = 512;   // two workgroups per compute unit
 constexpr size_t kMaxGemvLds = 64 * 1024;
 
 int env_int(const char* name) {
@@ -90,37 +91,50 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
 }
 
 // Launch shape for one launch of `rows` rows (rows <= rows_per_launch).
-Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int s_req) {
+// ntw_req / wk_req / s_req: 0 = choose here.
+Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_req, int s_req) {
   Cfg c{};
   c.variant = variant;
   const int nT = p->nT, nC = p->nC;
+  auto pow2_floor = [](int v) { return v >= 4 ? 4 : (v >= 2 ? 2 : 1); };
+  int tiles_per_block;
   if (variant == QMM_VARIANT_MFMA) {
     c.rows_per_launch = qmm::kMaxMfmaRows;
     const int r = std::min(rows, qmm::kMaxMfmaRows);
     c.tile_rows = round_up_pow2((r + 15) / 16, 4);
-    int ntw = c.tile_rows <= 2 ? 2 : 1;
+    // defaults (measured on the 3-bit 5120->10240 workload): K split over
+    // the workgroup's four waves; two W tiles per wave once the activation
+    // block is long enough for the reuse to pay
+    int ntw = r <= 1 ? 1 : 2, wk = c.tile_rows <= 2 ? 4 : 2;
     if (ntw_req) ntw = ntw_req;
-    const int cap = c.tile_rows <= 2 ? 4 : 2;
-    c.ntw = std::min(ntw >= 4 ? 4 : (ntw >= 2 ? 2 : 1), cap);
+    if (wk_req) wk = wk_req;
+    c.ntw = std::min(pow2_floor(ntw), c.tile_rows <= 1 ? 4 : 2);
+    c.wk = pow2_floor(wk);
+    tiles_per_block = (qmm::kWaves / c.wk) * c.ntw;
   } else {
     c.rows_per_launch = qmm::kMaxGemvRows;
     const int r = std::min(rows, qmm::kMaxGemvRows);
     c.tile_rows = round_up_pow2(r, 8);
-    int ntw = c.tile_rows == 1 ? 2 : 1;
+    int ntw = 1;
     if (ntw_req) ntw = ntw_req;
     const int cap = c.tile_rows == 1 ? 4 : (c.tile_rows <= 4 ? 2 : 1);
-    c.ntw = std::min(ntw >= 4 ? 4 : (ntw >= 2 ? 2 : 1), cap);
+    c.ntw = std::min(pow2_floor(ntw), cap);
+    c.wk = 1;
+    tiles_per_block = qmm::kWaves * c.ntw;
   }
-  c.nTB = (nT + qmm::kWaves * c.ntw - 1) / (qmm::kWaves * c.ntw);
+  c.nTB = (nT + tiles_per_block - 1) / tiles_per_block;
   int S;
   if (s_req) {
     S = s_req;
   } else {
-    S = (kTargetBlocks + c.nTB - 1) / c.nTB;
+    // A K split across workgroups needs a device-scope release per workgroup
+    // (an L2 write-back on this chip), which costs more than it gains unless
+    // the grid would otherwise leave most compute units idle.
+    S = c.nTB >= kMinBlocks / 8 ? 1 : (kMinBlocks / 8 + c.nTB - 1) / c.nTB;
     // partial sums cost S*rows*N*8 bytes of traffic: keep S*rows bounded
     const int r = std::min(rows, c.rows_per_launch);
     S = std::min(S, std::max(1, 64 / std::max(1, r)));
-    S = std::min(S, std::max(1, nC / 2));
+    S = std::min(S, std::max(1, nC / (2 * c.wk)));
   }
   S = std::max(1, std::min(S, nC));
   if (variant == QMM_VARIANT_GEMV) {
@@ -141,12 +155,12 @@ size_t cfg_workspace(const qmm_plan* p, const Cfg& c, int rows) {
 
 // Largest workspace any row block of a `rows`-row call needs (blocks of a
 // call run one after another on the stream and share the workspace).
-size_t call_workspace(const qmm_plan* p, int rows, int variant, int ntw, int s) {
-  const Cfg c = plan_config(p, rows, variant, ntw, s);
+size_t call_workspace(const qmm_plan* p, int rows, int variant, int ntw, int wk, int s) {
+  const Cfg c = plan_config(p, rows, variant, ntw, wk, s);
   size_t need = 0;
   for (int r0 = 0; r0 < rows; r0 += c.rows_per_launch) {
     const int rb = std::min(c.rows_per_launch, rows - r0);
-    need = std::max(need, cfg_workspace(p, plan_config(p, rb, variant, ntw, s), rb));
+    need = std::max(need, cfg_workspace(p, plan_config(p, rb, variant, ntw, wk, s), rb));
   }
   return need;
 }
@@ -163,7 +177,8 @@ qmm_status hip_fail(hipError_t e, const char* what) {
               hipGetErrorString(e));
 }
 
-qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int s_req, const void* x,
+qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req, int s_req,
+                    const void* x,
                     const void* codes, const void* sb, void* y, int32_t rows, void* ws,
                     size_t ws_bytes, void* stream) {
   if (qmm_status st = check_plan(p)) return st;
@@ -177,13 +192,14 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int s_req, 
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
   if (variant_req == QMM_VARIANT_MFMA && p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
-  if (ntw_req < 0 || ntw_req > 8 || s_req < 0)
-    return fail(QMM_ERR_INVALID_ARG, "ntw must be 0..8 and splitk >= 0");
+  if (ntw_req < 0 || ntw_req > 8 || s_req < 0 || wk_req < 0 || wk_req > qmm::kWaves)
+    return fail(QMM_ERR_INVALID_ARG, "ntw must be 0..8, kwaves 0..4 and splitk >= 0");
   const int ntw_eff = ntw_req ? ntw_req : p->env_ntw;
+  const int wk_eff = wk_req ? wk_req : p->env_kwaves;
   const int s_eff = s_req ? s_req : p->env_splitk;
   const int variant = pick_variant(p, rows, variant_req);
-  const Cfg c = plan_config(p, rows, variant, ntw_eff, s_eff);
-  const size_t need = call_workspace(p, rows, variant, ntw_eff, s_eff);
+  const Cfg c = plan_config(p, rows, variant, ntw_eff, wk_eff, s_eff);
+  const size_t need = call_workspace(p, rows, variant, ntw_eff, wk_eff, s_eff);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -195,7 +211,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int s_req, 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   for (int r0 = 0; r0 < rows; r0 += c.rows_per_launch) {
     const int rb = std::min(c.rows_per_launch, rows - r0);
-    const Cfg cb = plan_config(p, rb, variant, ntw_eff, s_eff);
+    const Cfg cb = plan_config(p, rb, variant, ntw_eff, wk_eff, s_eff);
     qmm::LaunchArgs a{};
     a.x = static_cast<const char*>(x) + (size_t)r0 * p->d.K * xe;
     a.codes = static_cast<const uint32_t*>(codes);
@@ -214,7 +230,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int s_req, 
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
     if (variant == QMM_VARIANT_MFMA)
-      e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, a, st);
+      e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, st);
     else
       e = qmm::launch_gemv(p->d.bits, xf, sf, cb.tile_rows, cb.ntw, a, cb.lds, st);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
@@ -225,8 +241,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int s_req, 
     p->last_grid = cb.nTB * cb.S;
   }
   if (getenv("QMM_LOG"))
-    fprintf(stderr, "qmm: rows=%d variant=%d ntw=%d splitk=%d grid=%d\n", rows, variant, c.ntw,
-            c.S, c.nTB * c.S);
+    fprintf(stderr, "qmm: rows=%d variant=%d ntw=%d kwaves=%d splitk=%d grid=%d\n", rows,
+            variant, c.ntw, c.wk, c.S, c.nTB * c.S);
   return QMM_OK;
 }
 
@@ -273,6 +289,7 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
   }
   p->env_ntw = env_int("QMM_NTW");
   p->env_splitk = env_int("QMM_SPLITK");
+  p->env_kwaves = env_int("QMM_KWAVES");
   for (auto& l : p->launches) l = 0;
   p->last_variant = 0;
   p->last_ntw = 0;
@@ -308,32 +325,33 @@ qmm_status qmm_prepack(const qmm_plan* p, const uint32_t* w, const void* scales,
   return QMM_OK;
 }
 
-size_t qmm_workspace_bytes_ex(const qmm_plan* p, int32_t variant, int32_t ntw, int32_t splitk,
-                              int32_t rows) {
+size_t qmm_workspace_bytes_ex(const qmm_plan* p, int32_t variant, int32_t ntw, int32_t kwaves,
+                              int32_t splitk, int32_t rows) {
   if (!p || rows < 1) return 0;
   const int v = pick_variant(p, rows, variant);
-  return call_workspace(p, rows, v, ntw ? ntw : p->env_ntw, splitk ? splitk : p->env_splitk);
+  return call_workspace(p, rows, v, ntw ? ntw : p->env_ntw, kwaves ? kwaves : p->env_kwaves,
+                        splitk ? splitk : p->env_splitk);
 }
 
 size_t qmm_workspace_bytes(const qmm_plan* p, int32_t rows) {
   if (!p || rows < 1) return 0;
-  size_t need = qmm_workspace_bytes_ex(p, QMM_VARIANT_AUTO, 0, 0, rows);
+  size_t need = qmm_workspace_bytes_ex(p, QMM_VARIANT_AUTO, 0, 0, 0, rows);
   if (p->d.x_dtype == QMM_BF16) {
-    need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_GEMV, 0, 0, rows));
-    need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_MFMA, 0, 0, rows));
+    need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_GEMV, 0, 0, 0, rows));
+    need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_MFMA, 0, 0, 0, rows));
   }
   return need;
 }
 
 qmm_status qmm_run(const qmm_plan* p, const void* x, const void* codes, const void* sb, void* y,
                    int32_t rows, void* ws, size_t ws_bytes, void* stream) {
-  return run_impl(p, QMM_VARIANT_AUTO, 0, 0, x, codes, sb, y, rows, ws, ws_bytes, stream);
+  return run_impl(p, QMM_VARIANT_AUTO, 0, 0, 0, x, codes, sb, y, rows, ws, ws_bytes, stream);
 }
 
-qmm_status qmm_run_ex(const qmm_plan* p, int32_t variant, int32_t ntw, int32_t splitk,
-                      const void* x, const void* codes, const void* sb, void* y, int32_t rows,
-                      void* ws, size_t ws_bytes, void* stream) {
-  return run_impl(p, variant, ntw, splitk, x, codes, sb, y, rows, ws, ws_bytes, stream);
+qmm_status qmm_run_ex(const qmm_plan* p, int32_t variant, int32_t ntw, int32_t kwaves,
+                      int32_t splitk, const void* x, const void* codes, const void* sb, void* y,
+                      int32_t rows, void* ws, size_t ws_bytes, void* stream) {
+  return run_impl(p, variant, ntw, kwaves, splitk, x, codes, sb, y, rows, ws, ws_bytes, stream);
 }
 
 qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, void* stream) {

@@ -35,7 +35,7 @@ hipError_t launch_repack(int bits, bool sb_f32, const uint32_t* w, const void* s
                          hipStream_t st);
 hipError_t launch_debug_unpack(int bits, const uint32_t* codes, uint8_t* out, int N, int K,
                                hipStream_t st);
-hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, const LaunchArgs& a,
+hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, int wk, const LaunchArgs& a,
                        hipStream_t st);
 hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const LaunchArgs& a,
                        size_t lds_bytes, hipStream_t st);

@@ -67,20 +67,41 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 // Scales/biases: block b holds 16 rows x {s_g0, s_g1, b_g0, b_g1}.
 // ---------------------------------------------------------------------------
 
+// v_and_or_b32 with the mask in a VGPR and the or-value in an SGPR.  gfx9
+// VOP3 instructions take no literal and read at most one scalar, so the
+// compiler splits (x & m) | c with two constants into two instructions; this
+// keeps it to one.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_v, uint32_t or_s) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask_v), "s"(or_s));
+  return r;
+}
+
 template <int BITS>
-__device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* P) {
+__device__ __forceinline__ uint32_t pair_mask_vgpr() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(m) : "i"(BITS == 4 ? 0x000F000F : 0x00070007));
+  return m;
+}
+
+// 16 pairs of bf16 values 128+q from one lane's BITS words.  mask_v must hold
+// pair_mask_vgpr<BITS>().
+template <int BITS>
+__device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* P, uint32_t mask_v) {
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) P[4 * j + t] = ((w[j] >> (4 * t)) & 0x000F000Fu) | 0x43004300u;
+      for (int t = 0; t < 4; ++t) P[4 * j + t] = and_or(w[j] >> (4 * t), mask_v, 0x43004300u);
   } else {
 #pragma unroll
     for (int j = 0; j < 3; ++j)
 #pragma unroll
-      for (int t = 0; t < 5; ++t) P[5 * j + t] = ((w[j] >> (3 * t)) & 0x00070007u) | 0x43004300u;
-    P[15] = ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0x00020002u) |
-            ((w[2] >> 13) & 0x00040004u) | 0x43004300u;
+      for (int t = 0; t < 5; ++t) P[5 * j + t] = and_or(w[j] >> (3 * t), mask_v, 0x43004300u);
+    // pair 15: bit b of each code sits in bit 15 / bit 31 of word b
+    const uint32_t b01 = ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0xFFFEFFFEu);
+    const uint32_t b012 = (b01 & 0x00030003u) | ((w[2] >> 13) & 0xFFFCFFFCu);
+    P[15] = and_or(b012, mask_v, 0x43004300u);
   }
 }
 
@@ -178,7 +199,7 @@ __global__ void __launch_bounds__(256) debug_unpack_kernel(const uint32_t* __res
   uint32_t w[BITS], P[16];
 #pragma unroll
   for (int j = 0; j < BITS; ++j) w[j] = codes[blk * 64 * BITS + lane * BITS + j];
-  unpack_pairs<BITS>(w, P);
+  unpack_pairs<BITS>(w, P, pair_mask_vgpr<BITS>());
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
     const int gp = p >> 3, u = p & 7;
@@ -231,15 +252,14 @@ __device__ __forceinline__ void store_y(void* y, long idx, float v) {
 template <bool Y_F32>
 __device__ void fold_partials(const LaunchArgs& a, int tb, int n0, int n1) {
   __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
+  __syncthreads();  // this workgroup's partial stores are complete
   if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&a.tickets[tb], 1u);
-    s_last = (old == (uint32_t)(a.S - 1));
+    __threadfence();  // publish them device-wide: one release per workgroup
+    s_last = atomicAdd(&a.tickets[tb], 1u) == (uint32_t)(a.S - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
+  __threadfence();  // acquire the other workgroups' partials
   const int width = n1 - n0;
   const long plane = (long)a.M * a.N;
   for (int idx = threadIdx.x; idx < a.M * width; idx += blockDim.x) {
@@ -252,20 +272,40 @@ __device__ void fold_partials(const LaunchArgs& a, int tb, int n0, int n1) {
   if (threadIdx.x == 0) atomicExch(&a.tickets[tb], 0u);
 }
 
+// Chunks of one workgroup's K split handed to wave wk of WK: c0+wk, c0+wk+WK, ...
+struct ChunkRange {
+  int c0, step, count;
+  __device__ __forceinline__ int at(int j) const { return c0 + j * step; }
+};
+
+__device__ __forceinline__ ChunkRange wave_chunks(int c0, int c1, int wk, int WK) {
+  ChunkRange cr;
+  cr.c0 = c0 + wk;
+  cr.step = WK;
+  cr.count = c1 - c0 > wk ? (c1 - c0 - wk + WK - 1) / WK : 0;
+  return cr;
+}
+
 // ---------------------------------------------------------------------------
-// MFMA kernel (bf16 activations).  Workgroup = 4 wavefronts; wavefront w owns
-// NTW consecutive tiles of W (16 rows each) and, for the workgroup's K split,
-// multiplies them by MT tiles of 16 activation rows.
+// MFMA kernel (bf16 activations).  Workgroup = 4 wavefronts arranged as
+// WT = 4/WK tile groups x WK K-groups.  Wave (wt, wk) multiplies NTW tiles of
+// W (16 rows each) by MT tiles of 16 activation rows over every WK-th chunk
+// of the workgroup's K split; the WK partial tiles are added through LDS in
+// order wk = 0, 1, ...  Loads run D chunks ahead in a statically indexed
+// ring, so several chunks of weights are in flight per wave.
 // ---------------------------------------------------------------------------
-template <int BITS, int MT, int NTW, typename ST>
+template <int BITS, int MT, int NTW, int WK, int D, typename ST>
 __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
+  constexpr int WT = kWaves / WK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wt = wave / WK, wk = wave - wt * WK;
   const int r = lane & 15, kg = lane >> 4;
   const int item = xcd_item(blockIdx.x, a.nTB * a.S);
   const int tb = item / a.S, s = item - tb * a.S;
   const int nT = a.N / kTileN, nC = a.K / kChunkK;
   const int c0 = (int)((long)s * nC / a.S), c1 = (int)((long)(s + 1) * nC / a.S);
-  const int tile0 = (tb * kWaves + wave) * NTW;
+  const int tile0 = (tb * WT + wt) * NTW;
+  const ChunkRange cr = wave_chunks(c0, c1, wk, WK);
   const uint16_t* __restrict__ x = reinterpret_cast<const uint16_t*>(a.x);
   const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
 
@@ -275,7 +315,7 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (tile0 < nT && c0 < c1) {
+  if (tile0 < nT && cr.count > 0) {
     bool tvalid[NTW];
     const uint32_t* cptr[NTW];
     const ST* sptr[NTW];
@@ -286,103 +326,115 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
       cptr[nt] = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
       sptr[nt] = sbp + ((long)t * nC * kTileN + r) * 4;
     }
+    // Rows past the last activation row read the last row; their outputs are
+    // never stored.
     const uint16_t* xrow[MT];
-    bool xvalid[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = 16 * mt + r;
-      xvalid[mt] = m < a.M;
-      xrow[mt] = x + (long)(xvalid[mt] ? m : 0) * a.ldx + 16 * kg;
+      const int m = min(16 * mt + r, a.M - 1);
+      xrow[mt] = x + (long)m * a.ldx + 16 * kg;
     }
+    const uint32_t mask_v = pair_mask_vgpr<BITS>();
     const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    uint32_t W[NTW][BITS];
-    SBPair<ST> SBv[NTW];
-    u32x4 A[MT][4];
-    auto load_chunk = [&](int c, uint32_t (&Wd)[NTW][BITS], SBPair<ST> (&Sd)[NTW],
-                          u32x4 (&Ad)[MT][4]) {
+    uint32_t W[D][NTW][BITS];
+    SBPair<ST> SBv[D][NTW];
+    u32x4 A[D][MT][4];
+    auto load = [&](int j, int d) {
+      const int c = cr.at(j);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const uint32_t* p = cptr[nt] + (long)c * 64 * BITS;
 #pragma unroll
-        for (int j = 0; j < BITS; ++j) Wd[nt][j] = __builtin_nontemporal_load(p + j);
-        Sd[nt].load(sptr[nt] + (long)c * kTileN * 4);
+        for (int q = 0; q < BITS; ++q) W[d][nt][q] = __builtin_nontemporal_load(p + q);
+        SBv[d][nt].load(sptr[nt] + (long)c * kTileN * 4);
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // step t: group g' = t>>1, half h = t&1 -> 8 values at 64g' + 16kg + 8h
-          const u32x4* p = reinterpret_cast<const u32x4*>(xrow[mt] + (long)kChunkK * c +
-                                                          64 * (t >> 1) + 8 * (t & 1));
-          Ad[mt][t] = xvalid[mt] ? *p : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int t = 0; t < 4; ++t)  // step t: group g' = t>>1, half h = t&1
+          A[d][mt][t] = *reinterpret_cast<const u32x4*>(xrow[mt] + (long)kChunkK * c +
+                                                        64 * (t >> 1) + 8 * (t & 1));
     };
-    load_chunk(c0, W, SBv, A);
-    for (int c = c0; c < c1; ++c) {
-      uint32_t Wn[NTW][BITS];
-      SBPair<ST> Sn[NTW];
-      u32x4 An[MT][4];
-      if (c + 1 < c1) load_chunk(c + 1, Wn, Sn, An);
-
+    auto compute = [&](int d) {
       // sum_k x_k of each group, replicated in every column
       f32x4 EX[MT][2];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, A[mt][2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0,
-              0, 0);
-          EX[mt][gp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, A[mt][2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e,
+          const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, A[d][mt][2 * gp]), __builtin_bit_cast(bf16x8, ones), zero,
               0, 0, 0);
+          EX[mt][gp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, A[d][mt][2 * gp + 1]), __builtin_bit_cast(bf16x8, ones),
+              e, 0, 0, 0);
         }
-
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         if (!tvalid[nt]) continue;
         uint32_t P[16];
-        unpack_pairs<BITS>(W[nt], P);
+        unpack_pairs<BITS>(W[d][nt], P, mask_v);
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          const float sc = SBv[nt].s(gp);
-          const float bp = SBv[nt].b(gp) - 128.f * sc;
+          const float sc = SBv[d][nt].s(gp);
+          const float bp = SBv[d][nt].b(gp) - 128.f * sc;
           const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
           const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, A[mt][2 * gp]), __builtin_bit_cast(bf16x8, B0), zero,
+            f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, A[d][mt][2 * gp]), __builtin_bit_cast(bf16x8, B0), zero,
                 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[mt][2 * gp + 1]),
-                                                        __builtin_bit_cast(bf16x8, B1), d, 0, 0, 0);
+            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, A[d][mt][2 * gp + 1]), __builtin_bit_cast(bf16x8, B1), dd,
+                0, 0, 0);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               if (16 * mt + q < a.M)
-                acc[nt][mt][q] = fmaf(sc, d[q], fmaf(bp, EX[mt][gp][q], acc[nt][mt][q]));
+                acc[nt][mt][q] = fmaf(sc, dd[q], fmaf(bp, EX[mt][gp][q], acc[nt][mt][q]));
           }
         }
       }
-      if (c + 1 < c1) {
+    };
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
+    for (int d = 0; d < D; ++d)
+      if (d < cr.count) load(d, d);
+    for (int j0 = 0; j0 < cr.count; j0 += D) {
 #pragma unroll
-          for (int j = 0; j < BITS; ++j) W[nt][j] = Wn[nt][j];
-          SBv[nt] = Sn[nt];
+      for (int d = 0; d < D; ++d) {
+        if (j0 + d < cr.count) {
+          compute(d);
+          if (j0 + d + D < cr.count) load(j0 + d + D, d);
         }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) A[mt][t] = An[mt][t];
       }
     }
   }
 
+  if constexpr (WK > 1) {
+    __shared__ f32x4 red[WK - 1][WT][NTW * MT][64];
+    if (wk > 0) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[wk - 1][wt][nt * MT + mt][lane] = acc[nt][mt];
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 1; w < WK; ++w)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[nt][mt] += red[w - 1][wt][nt * MT + mt][lane];
+    }
+  }
+
   // Output: lane holds column n = 16*tile + r, rows m = 16*mt + 4*kg + q.
+  const bool writer = wk == 0 && tile0 < nT;
   if (a.S == 1) {
-    if (tile0 >= nT) return;
+    if (!writer) return;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       if (tile0 + nt >= nT) continue;
@@ -397,7 +449,7 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
     }
     return;
   }
-  if (tile0 < nT) {
+  if (writer) {
     float* part = a.part + (long)s * a.M * a.N;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
@@ -412,16 +464,18 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
         }
     }
   }
-  const int n0 = tb * kWaves * NTW * kTileN;
-  const int n1 = min(a.N, n0 + kWaves * NTW * kTileN);
+  const int n0 = tb * WT * NTW * kTileN;
+  const int n1 = min(a.N, n0 + WT * NTW * kTileN);
   fold_partials<false>(a, tb, n0, n1);
 }
 
 // ---------------------------------------------------------------------------
 // Vector-ALU kernel: up to MR activation rows per pass, activations of the
 // workgroup's K split staged in LDS together with per-(row, group, quarter)
-// sums.  Lane (r, kg) accumulates its quarter of each group; the four
-// quarters are added with cross-lane shuffles at the end.
+// sums.  Each of the 4 wavefronts owns NTW tiles; lane (r, kg) accumulates
+// its quarter of each group with v_dot2_f32_bf16 on (128+q, x) pairs, and the
+// four quarters are added with cross-lane shuffles at the end.  Weight loads
+// run D chunks ahead in a statically indexed ring.
 // ---------------------------------------------------------------------------
 template <bool X_F32>
 using XStore = typename std::conditional<X_F32, float, uint16_t>::type;
@@ -432,6 +486,7 @@ size_t gemv_lds_bytes(bool x_f32, int mr, int kslice) {
 
 template <int BITS, int MR, int NTW, bool X_F32, typename ST>
 __global__ void __launch_bounds__(kBlockThreads) gemv_kernel(LaunchArgs a) {
+  constexpr int D = 4;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   using XT = XStore<X_F32>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -442,9 +497,40 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_kernel(LaunchArgs a) {
   const int c0 = (int)((long)s * nC / a.S), c1 = (int)((long)(s + 1) * nC / a.S);
   const int ks = (c1 - c0) * kChunkK, gs = ks / 64;
   const int tile0 = (tb * kWaves + wave) * NTW;
+  const int nchunks = c1 - c0;
   const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
-  XT* xs = reinterpret_cast<XT*>(lds);                                   // [MR][ks]
+  XT* xs = reinterpret_cast<XT*>(lds);                                       // [MR][ks]
   float* xq = reinterpret_cast<float*>(lds + (size_t)MR * ks * sizeof(XT));  // [MR][gs][4]
+
+  bool tvalid[NTW];
+  const uint32_t* cptr[NTW];
+  const ST* sptr[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int t = tile0 + nt < nT ? tile0 + nt : nT - 1;
+    tvalid[nt] = tile0 + nt < nT;
+    cptr[nt] = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
+    sptr[nt] = sbp + ((long)t * nC * kTileN + r) * 4;
+  }
+  uint32_t W[D][NTW][BITS];
+  SBPair<ST> SBv[D][NTW];
+  auto load = [&](int j, int d) {
+    const int c = c0 + j;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const uint32_t* p = cptr[nt] + (long)c * 64 * BITS;
+#pragma unroll
+      for (int q = 0; q < BITS; ++q) W[d][nt][q] = __builtin_nontemporal_load(p + q);
+      SBv[d][nt].load(sptr[nt] + (long)c * kTileN * 4);
+    }
+  };
+  const bool active = tile0 < nT && nchunks > 0;
+  // First weight loads go out before the activation staging.
+  if (active) {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < nchunks) load(d, d);
+  }
 
   // Stage the activation slice, 16 bytes per thread per step.
   {
@@ -480,44 +566,19 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_kernel(LaunchArgs a) {
 #pragma unroll
     for (int m = 0; m < MR; ++m) acc[nt][m] = 0.f;
 
-  if (tile0 < nT && c0 < c1) {
-    bool tvalid[NTW];
-    const uint32_t* cptr[NTW];
-    const ST* sptr[NTW];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int t = tile0 + nt < nT ? tile0 + nt : nT - 1;
-      tvalid[nt] = tile0 + nt < nT;
-      cptr[nt] = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
-      sptr[nt] = sbp + ((long)t * nC * kTileN + r) * 4;
-    }
-    uint32_t W[NTW][BITS];
-    SBPair<ST> SBv[NTW];
-    auto load_chunk = [&](int c, uint32_t (&Wd)[NTW][BITS], SBPair<ST> (&Sd)[NTW]) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const uint32_t* p = cptr[nt] + (long)c * 64 * BITS;
-#pragma unroll
-        for (int j = 0; j < BITS; ++j) Wd[nt][j] = __builtin_nontemporal_load(p + j);
-        Sd[nt].load(sptr[nt] + (long)c * kTileN * 4);
-      }
-    };
-    load_chunk(c0, W, SBv);
-    for (int c = c0; c < c1; ++c) {
-      uint32_t Wn[NTW][BITS];
-      SBPair<ST> Sn[NTW];
-      if (c + 1 < c1) load_chunk(c + 1, Wn, Sn);
-      const int cl = c - c0;
+  if (active) {
+    const uint32_t mask_v = pair_mask_vgpr<BITS>();
+    auto compute = [&](int j, int d) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         if (!tvalid[nt]) continue;
         uint32_t P[16];
-        unpack_pairs<BITS>(W[nt], P);
+        unpack_pairs<BITS>(W[d][nt], P, mask_v);
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          const float sc = SBv[nt].s(gp);
-          const float bp = SBv[nt].b(gp) - 128.f * sc;
-          const int kl = kChunkK * cl + 64 * gp + 16 * kg;  // lane's 16 columns
+          const float sc = SBv[d][nt].s(gp);
+          const float bp = SBv[d][nt].b(gp) - 128.f * sc;
+          const int kl = kChunkK * j + 64 * gp + 16 * kg;  // lane's 16 columns
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
             if (m >= a.M) break;
@@ -546,17 +607,18 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_kernel(LaunchArgs a) {
                       __builtin_bit_cast(bf16x2, xw[e]), dot, false);
               }
             }
-            const float xsum = xq[((long)m * gs + 2 * cl + gp) * 4 + kg];
+            const float xsum = xq[((long)m * gs + 2 * j + gp) * 4 + kg];
             acc[nt][m] = fmaf(sc, dot, fmaf(bp, xsum, acc[nt][m]));
           }
         }
       }
-      if (c + 1 < c1) {
+    };
+    for (int j0 = 0; j0 < nchunks; j0 += D) {
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-          for (int j = 0; j < BITS; ++j) W[nt][j] = Wn[nt][j];
-          SBv[nt] = Sn[nt];
+      for (int d = 0; d < D; ++d) {
+        if (j0 + d < nchunks) {
+          compute(j0 + d, d);
+          if (j0 + d + D < nchunks) load(j0 + d + D, d);
         }
       }
     }
@@ -654,24 +716,28 @@ hipError_t launch_debug_unpack(int bits, const uint32_t* codes, uint8_t* out, in
 }
 
 template <int BITS, typename ST>
-static hipError_t mfma_dispatch(int mt, int ntw, const LaunchArgs& a, hipStream_t st) {
+static hipError_t mfma_dispatch(int mt, int ntw, int wk, const LaunchArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)(a.nTB * a.S);
-#define QMM_MFMA(MTV, NTV)                                                    \
-  if (mt == MTV && ntw == NTV) {                                              \
-    mfma_kernel<BITS, MTV, NTV, ST><<<grid, kBlockThreads, 0, st>>>(a);      \
-    return hipGetLastError();                                                 \
+#define QMM_MFMA(MTV, NTV, WKV, DV)                                                  \
+  if (mt == MTV && ntw == NTV && wk == WKV) {                                        \
+    mfma_kernel<BITS, MTV, NTV, WKV, DV, ST><<<grid, kBlockThreads, 0, st>>>(a);     \
+    return hipGetLastError();                                                        \
   }
-  QMM_MFMA(1, 1) QMM_MFMA(1, 2) QMM_MFMA(1, 4)
-  QMM_MFMA(2, 1) QMM_MFMA(2, 2) QMM_MFMA(2, 4)
-  QMM_MFMA(4, 1) QMM_MFMA(4, 2)
+  QMM_MFMA(1, 1, 1, 4) QMM_MFMA(1, 1, 2, 4) QMM_MFMA(1, 1, 4, 4)
+  QMM_MFMA(1, 2, 1, 4) QMM_MFMA(1, 2, 2, 4) QMM_MFMA(1, 2, 4, 4)
+  QMM_MFMA(1, 4, 1, 3) QMM_MFMA(1, 4, 2, 3) QMM_MFMA(1, 4, 4, 3)
+  QMM_MFMA(2, 1, 1, 3) QMM_MFMA(2, 1, 2, 3) QMM_MFMA(2, 1, 4, 3)
+  QMM_MFMA(2, 2, 1, 3) QMM_MFMA(2, 2, 2, 3) QMM_MFMA(2, 2, 4, 3)
+  QMM_MFMA(4, 1, 1, 2) QMM_MFMA(4, 1, 2, 2) QMM_MFMA(4, 1, 4, 2)
+  QMM_MFMA(4, 2, 1, 2) QMM_MFMA(4, 2, 2, 2) QMM_MFMA(4, 2, 4, 2)
 #undef QMM_MFMA
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, const LaunchArgs& a,
+hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, int wk, const LaunchArgs& a,
                        hipStream_t st) {
-  if (bits == 3) return sb_f32 ? mfma_dispatch<3, float>(mt, ntw, a, st) : mfma_dispatch<3, uint16_t>(mt, ntw, a, st);
-  return sb_f32 ? mfma_dispatch<4, float>(mt, ntw, a, st) : mfma_dispatch<4, uint16_t>(mt, ntw, a, st);
+  if (bits == 3) return sb_f32 ? mfma_dispatch<3, float>(mt, ntw, wk, a, st) : mfma_dispatch<3, uint16_t>(mt, ntw, wk, a, st);
+  return sb_f32 ? mfma_dispatch<4, float>(mt, ntw, wk, a, st) : mfma_dispatch<4, uint16_t>(mt, ntw, wk, a, st);
 }
 
 template <int BITS, bool XF, typename ST>

@@ -132,15 +132,18 @@ qmm_status qmm_run(const qmm_plan* plan, const void* x, const void* codes, const
                    void* stream);
 
 /* qmm_run with a forced kernel family and launch shape, for tests and
- * measurement.  ntw (output tiles per wavefront, 1..8) and splitk (>= 1)
- * may be 0 for the plan's choice. */
-qmm_status qmm_run_ex(const qmm_plan* plan, int32_t variant, int32_t ntw, int32_t splitk,
-                      const void* x, const void* codes, const void* sb, void* y,
-                      int32_t rows, void* workspace, size_t workspace_bytes, void* stream);
+ * measurement.  ntw: tiles of 16 rows of W per wavefront (1, 2, 4);
+ * kwaves: wavefronts of a workgroup that split K between them (1, 2, 4;
+ * MFMA family only); splitk: workgroups that split K, folded through the
+ * workspace (>= 1).  Each may be 0 for the plan's choice. */
+qmm_status qmm_run_ex(const qmm_plan* plan, int32_t variant, int32_t ntw, int32_t kwaves,
+                      int32_t splitk, const void* x, const void* codes, const void* sb,
+                      void* y, int32_t rows, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
-/* Workspace needed by qmm_run_ex with the same variant/ntw/splitk. */
+/* Workspace needed by qmm_run_ex with the same variant/ntw/kwaves/splitk. */
 size_t qmm_workspace_bytes_ex(const qmm_plan* plan, int32_t variant, int32_t ntw,
-                              int32_t splitk, int32_t rows);
+                              int32_t kwaves, int32_t splitk, int32_t rows);
 
 /* Test hook: decode the native layout with the compute kernels' own unpack
  * and write the codes q(n,k) as uint8 [N, K] (device buffer). */

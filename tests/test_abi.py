@@ -80,12 +80,12 @@ def test_run_validation_without_gpu():
     assert L.qmm_run(p.handle, ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, 1, None, 0,
                      None) == b.QMM_ERR_INVALID_ARG
     # a forced K split needs a workspace
-    assert L.qmm_run_ex(p.handle, b.VARIANT_MFMA, 1, 4, fake, fake, fake, fake, 4, None, 0,
+    assert L.qmm_run_ex(p.handle, b.VARIANT_MFMA, 1, 1, 4, fake, fake, fake, fake, 4, None, 0,
                         None) == b.QMM_ERR_WORKSPACE
     assert b"workspace" in L.qmm_last_error()
     # MFMA takes bf16 activations only
     pf = b.Plan(4, 512, 512, 1, "f32")
-    assert L.qmm_run_ex(pf.handle, b.VARIANT_MFMA, 0, 0, fake, fake, fake, fake, 1, None, 0,
+    assert L.qmm_run_ex(pf.handle, b.VARIANT_MFMA, 0, 0, 0, fake, fake, fake, fake, 1, None, 0,
                         None) == b.QMM_ERR_UNSUPPORTED
     assert L.qmm_run(None, fake, fake, fake, fake, 1, None, 0, None) == b.QMM_ERR_INVALID_ARG
 
