@@ -84,6 +84,9 @@ def main() -> int:
     ap.add_argument("--variant", default="auto", choices=["auto", "gemv", "mfma"])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read probe")
+    ap.add_argument("--probe-only", action="store_true",
+                    help="only run the HBM read probe on a 1 GiB buffer five times (a kernel of "
+                         "known traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
@@ -96,6 +99,11 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.probe_only:
+        gbps = measure_hbm(torch, binding, gib=1)
+        print(json.dumps({"probe_bytes_per_launch": 1 << 30, "launches": 5,
+                          "best_GBps": round(gbps, 1)}), flush=True)
+        return 0
     log("drawing inputs")
     (prob,) = synth.workload(2)               # M=64 draw; smaller M use its first rows
     plan = binding.Plan(BITS, K, N, max(ROWS), "bf16", "bf16")

@@ -46,7 +46,7 @@ struct Cfg {
   int wk;         // wavefronts of a workgroup that split K (MFMA)
   int S;          // K splits across workgroups
   int nTB;        // tile blocks
-  size_t lds;     // dynamic LDS bytes (GEMV)
+  size_t lds;     // dynamic LDS bytes (GEMV, STREAM)
 };
 
 }  // namespace
@@ -56,7 +56,7 @@ struct qmm_plan {
   int nT, nC;
   int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
   int env_ntw, env_splitk, env_kwaves;
-  mutable std::atomic<uint64_t> launches[3];
+  mutable std::atomic<uint64_t> launches[4];
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
 };
 
@@ -82,11 +82,29 @@ size_t ticket_bytes(const qmm_plan* p) {
 
 // Pick the kernel family.  Vector-ALU for f32 activations (the MFMA path takes
 // bf16 operands) and, for bf16, wherever it is measured faster.
+bool stream_shape(const qmm_plan* p, int* nw, int* cpw) {
+  const int nC = p->nC;
+  // (waves, chunks per wave): four waves for short K, eight from 16 chunks
+  const int opts[][2] = {{4, 2}, {4, 4}, {8, 4}, {8, 5}, {8, 8}, {16, 8}};
+  for (const auto& o : opts) {
+    if (nC < 16 && o[0] != 4) continue;
+    if (nC >= 16 && o[0] == 4) continue;
+    if (nC <= o[0] * o[1]) {
+      *nw = o[0];
+      *cpw = o[1];
+      return true;
+    }
+  }
+  return false;
+}
+
 int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
   if (p->force_variant) return p->force_variant;
-  (void)rows;
+  int nw, cpw;
+  if (rows <= 16 && stream_shape(p, &nw, &cpw) && qmm::stream_fits(nw, rows, (int)p->d.K))
+    return QMM_VARIANT_STREAM;
   return QMM_VARIANT_MFMA;
 }
 
@@ -98,6 +116,19 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
   const int nT = p->nT, nC = p->nC;
   auto pow2_floor = [](int v) { return v >= 4 ? 4 : (v >= 2 ? 2 : 1); };
   int tiles_per_block;
+  if (variant == QMM_VARIANT_STREAM) {
+    c.rows_per_launch = 16;
+    c.tile_rows = 1;
+    int nw = 8, cpw = 8;
+    stream_shape(p, &nw, &cpw);
+    c.wk = nw;
+    c.ntw = cpw;  // chunks per wave for this family
+    c.nTB = nT;
+    const int r = std::min(rows, 16);
+    c.lds = qmm::stream_lds_bytes(nw, r, (int)p->d.K);
+    c.S = 1;
+    return c;
+  }
   if (variant == QMM_VARIANT_MFMA) {
     c.rows_per_launch = qmm::kMaxMfmaRows;
     const int r = std::min(rows, qmm::kMaxMfmaRows);
@@ -187,11 +218,18 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   if (!x || !codes || !sb || !y) return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(sb, 16) || !aligned(y, 4))
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
-  if (variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GEMV &&
-      variant_req != QMM_VARIANT_MFMA)
+  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_STREAM)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
-  if (variant_req == QMM_VARIANT_MFMA && p->d.x_dtype != QMM_BF16)
+  if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM) &&
+      p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
+  if (variant_req == QMM_VARIANT_STREAM) {
+    int nw, cpw;
+    if (!stream_shape(p, &nw, &cpw) || !qmm::stream_fits(nw, std::min(rows, 16), (int)p->d.K))
+      return fail(QMM_ERR_UNSUPPORTED,
+                  "the streaming kernel needs K <= 16384 and rows*K*2 bytes of activations "
+                  "to fit its LDS budget");
+  }
   if (ntw_req < 0 || ntw_req > 8 || s_req < 0 || wk_req < 0 || wk_req > qmm::kWaves)
     return fail(QMM_ERR_INVALID_ARG, "ntw must be 0..8, kwaves 0..4 and splitk >= 0");
   const int ntw_eff = ntw_req ? ntw_req : p->env_ntw;
@@ -229,7 +267,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (variant == QMM_VARIANT_MFMA)
+    if (variant == QMM_VARIANT_STREAM)
+      e = qmm::launch_stream(p->d.bits, sf, cb.wk, cb.ntw, a, cb.lds, st);
+    else if (variant == QMM_VARIANT_MFMA)
       e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, st);
     else
       e = qmm::launch_gemv(p->d.bits, xf, sf, cb.tile_rows, cb.ntw, a, cb.lds, st);
@@ -286,6 +326,7 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
   if (const char* v = getenv("QMM_FORCE_VARIANT")) {
     if (!strcmp(v, "gemv")) p->force_variant = QMM_VARIANT_GEMV;
     if (!strcmp(v, "mfma")) p->force_variant = QMM_VARIANT_MFMA;
+    if (!strcmp(v, "stream")) p->force_variant = QMM_VARIANT_STREAM;
   }
   p->env_ntw = env_int("QMM_NTW");
   p->env_splitk = env_int("QMM_SPLITK");
@@ -368,7 +409,7 @@ qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, 
 qmm_status qmm_get_stats(const qmm_plan* p, qmm_stats* out) {
   if (qmm_status st = check_plan(p)) return st;
   if (!out) return fail(QMM_ERR_INVALID_ARG, "out is NULL");
-  for (int i = 0; i < 3; ++i) out->launches[i] = p->launches[i].load();
+  for (int i = 0; i < 4; ++i) out->launches[i] = p->launches[i].load();
   out->last_variant = p->last_variant;
   out->last_ntw = p->last_ntw;
   out->last_splitk = p->last_splitk;

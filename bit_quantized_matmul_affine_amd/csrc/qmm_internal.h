@@ -39,6 +39,10 @@ hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, int wk, const Lau
                        hipStream_t st);
 hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const LaunchArgs& a,
                        size_t lds_bytes, hipStream_t st);
+hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
+                         size_t lds_bytes, hipStream_t st);
+size_t stream_lds_bytes(int nw, int M, int K);
+bool stream_fits(int nw, int M, int K);
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 
 // Bytes of LDS the vector-ALU kernel needs for `mr` rows over `kslice` columns.

@@ -470,6 +470,134 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Streaming MFMA kernel for short activation blocks (rows * K <= NW * 4096,
+// at most 16 rows).  One workgroup owns one tile of W (16 rows) and all of K;
+// its NW wavefronts take every NW-th chunk.  Order of work in a wave:
+//   1. its share of the activation block (global -> registers);
+//   2. the loads of ALL its weight chunks (at most CPW), so a compute unit's
+//      whole share of W is in flight at once;
+//   3. activations -> LDS, barrier (the wait covers only step 1: loads retire
+//      in issue order, so step 2 stays in flight);
+//   4. per chunk, in arrival order: unpack, MFMA, per-group scale.
+// MQ = accumulator registers that can hold a live row (1, 2 or 4).  The NW
+// partial tiles are added through LDS in wave order.
+// ---------------------------------------------------------------------------
+// Activation vectors (16 bytes) staged per thread: enough for rows*K/8 vectors
+// when the block has at least 512 threads and rows*K <= 4096 * (bucket rows).
+template <int MQ>
+struct StreamXVec { static constexpr int value = MQ == 1 ? 2 : (MQ == 2 ? 4 : 8); };
+
+template <int BITS, int NW, int CPW, int MQ, typename ST>
+__global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
+  constexpr int XV = StreamXVec<MQ>::value;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r = lane & 15, kg = lane >> 4;
+  const int tile = blockIdx.x;
+  const int nC = a.K / kChunkK;
+  const int count = nC > w ? (nC - w + NW - 1) / NW : 0;  // chunks w, w+NW, ...
+  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
+  const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);  // [M][K]
+
+  // 1. activation block, 16 bytes per vector; indices past the end repeat
+  //    the last vector (same value stored twice), so no branches
+  const int kv = a.K / 8, vecs = a.M * kv;
+  u32x4 xv[XV];
+  int xidx[XV];
+#pragma unroll
+  for (int i = 0; i < XV; ++i) {
+    xidx[i] = min((int)threadIdx.x + i * NW * 64, vecs - 1);
+    const int m = xidx[i] / kv, v = xidx[i] - m * kv;
+    xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)m * a.ldx + 8 * v);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. all weight loads of this wave; slots past `count` re-read the wave's
+  //    last chunk and are discarded below
+  const uint32_t* cbase = a.codes + ((long)tile * nC) * 64 * BITS + lane * BITS;
+  const ST* sbase = sbp + ((long)tile * nC * kTileN + r) * 4;
+  const int clast = w + (count > 0 ? count - 1 : 0) * NW;
+  uint32_t W[CPW][BITS];
+  SBPair<ST> SBv[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int c = min(w + j * NW, clast);
+    const uint32_t* p = cbase + (long)c * 64 * BITS;
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) W[j][q] = __builtin_nontemporal_load(p + q);
+    SBv[j].load(sbase + (long)c * kTileN * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. activations to LDS
+#pragma unroll
+  for (int i = 0; i < XV; ++i) *reinterpret_cast<u32x4*>(xs + 8 * xidx[i]) = xv[i];
+  __syncthreads();
+
+  // 4. compute in load order; rows past the last one read the last row
+  //    (never stored)
+  const uint16_t* xrow = xs + (long)min(r, a.M - 1) * a.K + 16 * kg;
+  const uint32_t mask_v = pair_mask_vgpr<BITS>();
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = zero;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int c = min(w + j * NW, clast);
+    const bool live = j < count;
+    u32x4 A[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      A[t] = *reinterpret_cast<const u32x4*>(xrow + (long)kChunkK * c + 64 * (t >> 1) + 8 * (t & 1));
+    uint32_t P[16];
+    unpack_pairs<BITS>(W[j], P, mask_v);
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0, 0, 0);
+      const f32x4 ex = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
+      const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
+      const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
+      f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
+      dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
+                                                   __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
+      const float sc = SBv[j].s(gp);
+      const float bp = SBv[j].b(gp) - 128.f * sc;
+#pragma unroll
+      for (int q = 0; q < MQ; ++q) {
+        const float v = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[q]));
+        acc[q] = live ? v : acc[q];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 5. add the NW partial tiles in wave order and store rows < M
+  f32x4* red = reinterpret_cast<f32x4*>(lds + (size_t)a.M * a.K * 2);  // [NW-1][64]
+  if (w > 0) red[(w - 1) * 64 + lane] = acc;
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int i = 1; i < NW; ++i) acc += red[(i - 1) * 64 + lane];
+  const int n = tile * kTileN + r;
+#pragma unroll
+  for (int q = 0; q < MQ; ++q) {
+    const int m = 4 * kg + q;
+    if (m < a.M) store_y<false>(a.y, (long)m * a.ldy + n, acc[q]);
+  }
+}
+
+size_t stream_lds_bytes(int nw, int M, int K) { return (size_t)M * K * 2 + (size_t)(nw - 1) * 64 * 16; }
+bool stream_fits(int nw, int M, int K) {
+  const int xv = M == 1 ? 2 : (M == 2 ? 4 : 8);
+  return M <= 16 && (long)M * K <= (long)nw * 64 * xv * 8 &&
+         stream_lds_bytes(nw, M, K) <= 64 * 1024;
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU kernel: up to MR activation rows per pass, activations of the
 // workgroup's K split staged in LDS together with per-(row, group, quarter)
 // sums.  Each of the 4 wavefronts owns NTW tiles; lane (r, kg) accumulates
@@ -765,6 +893,35 @@ hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const
   }
   if (x_f32) return sb_f32 ? gemv_dispatch<4, true, float>(mr, ntw, a, lds_bytes, st) : gemv_dispatch<4, true, uint16_t>(mr, ntw, a, lds_bytes, st);
   return sb_f32 ? gemv_dispatch<4, false, float>(mr, ntw, a, lds_bytes, st) : gemv_dispatch<4, false, uint16_t>(mr, ntw, a, lds_bytes, st);
+}
+
+template <int BITS, typename ST, int MQ>
+static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_t lds,
+                                     hipStream_t st) {
+  const unsigned grid = (unsigned)(a.N / kTileN);
+#define QMM_STREAM(NWV, CPWV)                                                            \
+  if (nw == NWV && cpw == CPWV) {                                                        \
+    stream_kernel<BITS, NWV, CPWV, MQ, ST><<<grid, NWV * 64, lds, st>>>(a);             \
+    return hipGetLastError();                                                            \
+  }
+  QMM_STREAM(4, 2) QMM_STREAM(4, 4) QMM_STREAM(8, 4) QMM_STREAM(8, 5) QMM_STREAM(8, 8)
+  QMM_STREAM(16, 8)
+#undef QMM_STREAM
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, typename ST>
+static hipError_t stream_dispatch(int nw, int cpw, const LaunchArgs& a, size_t lds,
+                                  hipStream_t st) {
+  if (a.M == 1) return stream_dispatch_mq<BITS, ST, 1>(nw, cpw, a, lds, st);
+  if (a.M == 2) return stream_dispatch_mq<BITS, ST, 2>(nw, cpw, a, lds, st);
+  return stream_dispatch_mq<BITS, ST, 4>(nw, cpw, a, lds, st);
+}
+
+hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
+                         size_t lds_bytes, hipStream_t st) {
+  if (bits == 3) return sb_f32 ? stream_dispatch<3, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<3, uint16_t>(nw, cpw, a, lds_bytes, st);
+  return sb_f32 ? stream_dispatch<4, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<4, uint16_t>(nw, cpw, a, lds_bytes, st);
 }
 
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {

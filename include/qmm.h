@@ -60,8 +60,11 @@ typedef enum { QMM_F32 = 0, QMM_BF16 = 1 } qmm_dtype;
 /* Kernel families (qmm_run picks one; qmm_run_ex can force one). */
 typedef enum {
   QMM_VARIANT_AUTO = 0,
-  QMM_VARIANT_GEMV = 1,  /* vector-ALU kernel, activations staged in LDS; 1..8 rows per pass */
-  QMM_VARIANT_MFMA = 2   /* matrix-core kernel (bf16 in, f32 accumulate); bf16 activations only */
+  QMM_VARIANT_GEMV = 1,   /* vector-ALU kernel, activations staged in LDS; 1..8 rows per pass */
+  QMM_VARIANT_MFMA = 2,   /* blocked matrix-core kernel (bf16 in, f32 accumulate), 1..64 rows
+                             per pass; bf16 activations only */
+  QMM_VARIANT_STREAM = 3  /* matrix-core kernel for 1..16 rows: one workgroup per 16 rows of W,
+                             all of a wave's weight loads issued up front; bf16 activations */
 } qmm_variant;
 
 /* Shape and format of one projection.  bits: 3 or 4 (other MLX widths are
@@ -83,7 +86,7 @@ typedef struct {
 typedef struct qmm_plan qmm_plan;
 
 typedef struct {
-  uint64_t launches[3];   /* indexed by qmm_variant: kernels run per family */
+  uint64_t launches[4];   /* indexed by qmm_variant: kernels run per family */
   int32_t last_variant;   /* family of the last qmm_run */
   int32_t last_ntw;       /* output tiles (16 rows of W each) per wavefront */
   int32_t last_splitk;    /* K splits folded through the workspace */

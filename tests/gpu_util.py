@@ -13,6 +13,16 @@ def say(*a):
     sys.stdout.flush()
 
 
+def stream_ok(K: int, rows: int) -> bool:
+    """Whether the streaming kernel takes a block of `rows` rows at this K
+    (activation block staged in LDS)."""
+    rows = min(rows, 16)
+    nC = K // 128
+    nw = 4 if nC < 16 else (8 if nC <= 64 else 16)
+    xv = {1: 2, 2: 4}.get(rows, 8)
+    return nC <= 128 and rows * K <= nw * 64 * xv * 8 and rows * K * 2 + (nw - 1) * 1024 <= 65536
+
+
 def y_to_f64(y_bits: np.ndarray, x_dtype: str) -> np.ndarray:
     if x_dtype == "bf16":
         return oracle.decode_bf16(y_bits)

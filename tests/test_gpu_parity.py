@@ -10,7 +10,7 @@ import pytest
 import oracle
 from bit_quantized_matmul_affine_amd import binding as b
 from bit_quantized_matmul_affine_amd import synth
-from tests.gpu_util import Runner, check_against_oracle, say
+from tests.gpu_util import Runner, check_against_oracle, say, stream_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -83,10 +83,10 @@ SMALL = [
 ]
 
 
-def _variants(x_dtype, M):
+def _variants(x_dtype, M, K):
     out = ["gemv"]
     if x_dtype == "bf16":
-        out.append("mfma")
+        out += ["mfma"] + (["stream"] if stream_ok(K, M) else [])
     return out
 
 
@@ -95,28 +95,30 @@ def test_small_parity(case):
     bits, K, N, M, xd, sd = case
     p = synth.small(100 + M, bits=bits, K=K, N=N, M=M, x_dtype=xd, sb_dtype=sd)
     r = Runner(p)
-    for v in _variants(xd, M):
-        for ntw, s in [(0, 0), (1, 1), (2, 2), (1, 3)]:
+    for v in _variants(xd, M, K):
+        shapes = [(0, 0, 0)] if v == "stream" else [(0, 0, 0), (1, 1, 1), (2, 2, 2), (1, 4, 3),
+                                                    (2, 4, 1), (4, 1, 2)]
+        for ntw, kw, s in shapes:
             if s > K // 128:
                 continue
-            label = "%s %s ntw=%d S=%d" % (case, v, ntw, s)
+            label = "%s %s ntw=%d kwaves=%d S=%d" % (case, v, ntw, kw, s)
             say(label)
-            y = r.run(variant=v, ntw=ntw, splitk=s)
+            y = r.run(variant=v, ntw=ntw, kwaves=kw, splitk=s)
             check_against_oracle(p, y, label=label)
 
 
 # ------------------------------------------------------------------ properties
 
 def test_determinism_and_row_independence():
-    p = synth.small(7, bits=3, K=2560, N=320, M=16)
+    p = synth.small(7, bits=3, K=1024, N=320, M=16)
     r = Runner(p)
-    for v in ("mfma", "gemv"):
+    for v, ntw, kw, s in (("mfma", 1, 2, 4), ("mfma", 2, 4, 1), ("gemv", 1, 0, 4), ("stream", 0, 0, 0)):
         say("determinism", v)
-        a = r.run(variant=v, ntw=1, splitk=4)
-        b2 = r.run(variant=v, ntw=1, splitk=4)
+        a = r.run(variant=v, ntw=ntw, kwaves=kw, splitk=s)
+        b2 = r.run(variant=v, ntw=ntw, kwaves=kw, splitk=s)
         assert np.array_equal(a, b2)
-        if v == "mfma":
-            a9 = r.run(rows=9, variant=v, ntw=1, splitk=4)
+        if v in ("mfma", "stream"):
+            a9 = r.run(rows=9, variant=v, ntw=ntw, kwaves=kw, splitk=s)
             assert np.array_equal(a9[:9], a[:9])
 
 
@@ -124,7 +126,7 @@ def test_rows_past_m_and_past_end_untouched():
     import torch
     p = synth.small(8, bits=4, K=512, N=64, M=5)
     r = Runner(p, max_rows=8)
-    for v in ("mfma", "gemv"):
+    for v in ("mfma", "gemv", "stream"):
         say("canary", v)
         out = torch.full((9, 64), 7.0, dtype=torch.bfloat16, device="cuda")
         r.lin.plan.run(r.x[:5], r.lin.codes, r.lin.sb, out=out[:5], variant=v, splitk=2)
@@ -148,6 +150,15 @@ def test_non_default_stream_and_workspace_reuse():
             check_against_oracle(p.rows(rows), b.to_numpy_bits(y), label="rows %d" % rows)
 
 
+def test_stream_rejects_blocks_too_long_for_lds():
+    p = synth.small(11, bits=3, K=5120, N=32, M=16)
+    r = Runner(p)
+    with pytest.raises(b.QmmError) as ei:
+        r.run(variant="stream")
+    assert ei.value.status == b.QMM_ERR_UNSUPPORTED
+    check_against_oracle(p, r.run(), label="auto falls back")   # auto picks another family
+
+
 def test_stats_report_the_family_that_ran():
     p = synth.small(10, bits=4, K=512, N=64, M=4)
     r = Runner(p)
@@ -157,6 +168,9 @@ def test_stats_report_the_family_that_ran():
     r.run(variant="mfma")
     st = r.lin.plan.stats()
     assert st["last_variant"] == "mfma" and st["launches"]["mfma"] >= 1
+    r.run()  # 4 rows: the streaming kernel serves short blocks by default
+    st = r.lin.plan.stats()
+    assert st["last_variant"] == "stream" and st["launches"]["stream"] >= 1
 
 
 # ------------------------------------------------------------------ workloads
@@ -169,7 +183,7 @@ def test_workload0_full(variant):
     check_against_oracle(p, r.run(variant=variant), label="w0 " + variant)
 
 
-@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma"])
+@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma", "stream"])
 def test_workload1_full(variant):
     (p,) = synth.workload(1)
     say("workload 1", variant)
@@ -181,7 +195,8 @@ def test_workload1_full(variant):
 def test_workload2_full(rows):
     (p,) = synth.workload(2)
     r = Runner(p, max_rows=64)
-    variants = ["auto", "mfma"] + (["gemv"] if rows <= 9 else [])
+    variants = ["auto", "mfma"] + (["gemv"] if rows <= 9 else []) + (
+        ["stream"] if stream_ok(p.K, rows) else [])
     for v in variants:
         say("workload 2 rows", rows, v)
         check_against_oracle(p.rows(rows), r.run(rows=rows, variant=v), rows=rows,
@@ -191,7 +206,7 @@ def test_workload2_full(rows):
 def test_workload3_full():
     for p in synth.workload(3):
         r = Runner(p)
-        for v in ("auto", "gemv", "mfma"):
+        for v in ("auto", "gemv", "mfma") + (("stream",) if stream_ok(p.K, p.M) else ()):
             say("workload 3", p.name, v)
             check_against_oracle(p, r.run(variant=v), label="w3 %s %s" % (p.name, v))
         del r
