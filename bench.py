@@ -52,13 +52,34 @@ def cpu_baseline(problem, seconds: float = 12.0):
             p = problem.rows(m)
             oracle.matmul(BITS, K, p.x, p.w, p.scales, p.biases, threads=threads)
         reps += 1
-        if time.perf_counter() - t0 >= seconds or reps >= 5:
+        if time.perf_counter() - t0 >= seconds or reps >= 200:
             break
     dt = time.perf_counter() - t0
     gbps = reps * len(ROWS) * weight_bytes() / dt / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "%d full step(s): all %d outputs at each of M=%s, float64 oracle, %.1f s"
                       % (reps, N, ",".join(map(str, ROWS)), dt)}
+
+
+def measured_traffic(rows: int):
+    """HBM bytes per launch of the kernel that serves `rows` rows, from the
+    committed FETCH_SIZE/WRITE_SIZE measurement, or None when the kernel
+    source has changed since it was taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, "bit_quantized_matmul_affine_amd", "csrc", "qmm_kernels.hip"),
+                  "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return None
+    if rec.get("kernel_source_sha256_16") != h:
+        return None
+    for k in rec["kernels"].values():
+        if str(k["rows"]) == str(rows):
+            return int(k["hbm_bytes"])
+    return None
 
 
 def measure_hbm(torch, binding, gib: int = 4, reps: int = 5):
@@ -223,7 +244,7 @@ def main() -> int:
         "per_rows": per,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(dominant),
                      "kernel": "M=%d (%s)" % (dominant, dom["launch"]["last_variant"]),
                      "bytes_per_launch": algorithmic_bytes(dominant),
                      "us_per_launch": dom["us_mean"]},
