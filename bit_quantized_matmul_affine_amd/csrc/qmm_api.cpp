@@ -46,7 +46,9 @@ struct Cfg {
   int wk;         // wavefronts of a workgroup that split K (MFMA)
   int S;          // K splits across workgroups
   int nTB;        // tile blocks
-  size_t lds;     // dynamic LDS bytes (GEMV, STREAM)
+  size_t lds;     // dynamic LDS bytes (GEMV, STREAM, PERSIST)
+  int grid;       // PERSIST, RESIDENT: workgroups
+  int cpw;        // RESIDENT: chunks of K per wave
 };
 
 }  // namespace
@@ -56,13 +58,28 @@ struct qmm_plan {
   int nT, nC;
   int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
   int env_ntw, env_splitk, env_kwaves;
-  mutable std::atomic<uint64_t> launches[4];
+  mutable std::atomic<uint64_t> launches[6];
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
 };
 
 namespace {
 
 constexpr int kMinBlocks = 512;   // two workgroups per compute unit
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load();
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cached[dev] = v;
+  }
+  return v;
+}
 constexpr size_t kMaxGemvLds = 64 * 1024;
 
 int env_int(const char* name) {
@@ -98,6 +115,13 @@ bool stream_shape(const qmm_plan* p, int* nw, int* cpw) {
   return false;
 }
 
+// Whether a block of `rows` (<= 16) rows fits the resident kernel's LDS.
+bool resident_fits(const qmm_plan* p, int rows) {
+  return (size_t)rows * p->d.K * 2 <= qmm::kMaxLdsBytes && qmm::resident_cpw(1, p->nC) > 0 &&
+         qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(4)) > 0 &&
+         qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(1)) > 0;
+}
+
 int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
@@ -116,6 +140,41 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
   const int nT = p->nT, nC = p->nC;
   auto pow2_floor = [](int v) { return v >= 4 ? 4 : (v >= 2 ? 2 : 1); };
   int tiles_per_block;
+  if (variant == QMM_VARIANT_PERSIST) {
+    c.rows_per_launch = qmm::kMaxMfmaRows;
+    const int r = std::min(rows, qmm::kMaxMfmaRows);
+    c.tile_rows = round_up_pow2((r + 15) / 16, 4);
+    const int rc = c.tile_rows == 1 ? 8 : 4;
+    c.wk = (c.tile_rows == 1 && wk_req == 8) ? 8 : 4;  // compute waves
+    c.grid = std::min(device_cus(), nT);
+    const int tm_cap = c.tile_rows == 1 ? 4 : 3;
+    int tm = (nT + c.grid - 1) / c.grid;
+    if (ntw_req) tm = ntw_req;
+    c.ntw = std::max(1, std::min(tm, tm_cap));
+    c.nTB = c.grid;
+    c.S = 1;
+    c.lds = qmm::persist_lds_bytes(c.tile_rows, rc);
+    return c;
+  }
+  if (variant == QMM_VARIANT_RESIDENT) {
+    // as few tile slots as fill every compute unit once; fewer where no
+    // built shape covers this K with that many slots
+    c.rows_per_launch = 16;
+    c.tile_rows = 1;
+    const int g = std::min(device_cus(), nT);
+    int tm = std::min(4, (nT + g - 1) / g);
+    if (ntw_req) tm = std::max(1, std::min(ntw_req, 4));
+    while (tm > 1 && qmm::resident_cpw(tm, nC) == 0) --tm;
+    c.ntw = tm;
+    c.cpw = qmm::resident_cpw(tm, nC);
+    c.wk = qmm::resident_waves(tm);
+    c.grid = (nT + tm - 1) / tm;
+    c.nTB = c.grid;
+    c.S = 1;
+    const int r = std::min(rows, 16);
+    c.lds = std::max((size_t)r * p->d.K * 2, (size_t)c.wk * 64 * 16);
+    return c;
+  }
   if (variant == QMM_VARIANT_STREAM) {
     c.rows_per_launch = 16;
     c.tile_rows = 1;
@@ -218,9 +277,10 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   if (!x || !codes || !sb || !y) return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(sb, 16) || !aligned(y, 4))
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
-  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_STREAM)
+  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_RESIDENT)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
-  if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM) &&
+  if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM ||
+       variant_req == QMM_VARIANT_PERSIST || variant_req == QMM_VARIANT_RESIDENT) &&
       p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
   if (variant_req == QMM_VARIANT_STREAM) {
@@ -230,8 +290,12 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
                   "the streaming kernel needs K <= 16384 and rows*K*2 bytes of activations "
                   "to fit its LDS budget");
   }
-  if (ntw_req < 0 || ntw_req > 8 || s_req < 0 || wk_req < 0 || wk_req > qmm::kWaves)
-    return fail(QMM_ERR_INVALID_ARG, "ntw must be 0..8, kwaves 0..4 and splitk >= 0");
+  if (variant_req == QMM_VARIANT_RESIDENT && !resident_fits(p, std::min(rows, 16)))
+    return fail(QMM_ERR_UNSUPPORTED,
+                "the resident kernel needs rows*K*2 bytes of activations (rows capped at 16) "
+                "to fit one compute unit's 160 KB of LDS");
+  if (ntw_req < 0 || ntw_req > 8 || s_req < 0 || wk_req < 0 || wk_req > 8)
+    return fail(QMM_ERR_INVALID_ARG, "ntw must be 0..8, kwaves 0..8 and splitk >= 0");
   const int ntw_eff = ntw_req ? ntw_req : p->env_ntw;
   const int wk_eff = wk_req ? wk_req : p->env_kwaves;
   const int s_eff = s_req ? s_req : p->env_splitk;
@@ -267,7 +331,13 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (variant == QMM_VARIANT_STREAM)
+    if (variant == QMM_VARIANT_RESIDENT)
+      e = qmm::launch_resident(p->d.bits, sf, cb.ntw, cb.cpw,
+                               qmm::resident_stage_vectors(rb, (int)p->d.K, cb.wk), a, cb.grid,
+                               cb.lds, st);
+    else if (variant == QMM_VARIANT_PERSIST)
+      e = qmm::launch_persist(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, cb.grid, cb.lds, st);
+    else if (variant == QMM_VARIANT_STREAM)
       e = qmm::launch_stream(p->d.bits, sf, cb.wk, cb.ntw, a, cb.lds, st);
     else if (variant == QMM_VARIANT_MFMA)
       e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, st);
@@ -278,7 +348,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     p->last_variant = variant;
     p->last_ntw = cb.ntw;
     p->last_splitk = cb.S;
-    p->last_grid = cb.nTB * cb.S;
+    p->last_grid = (variant == QMM_VARIANT_PERSIST || variant == QMM_VARIANT_RESIDENT) ? cb.grid : cb.nTB * cb.S;
   }
   if (getenv("QMM_LOG"))
     fprintf(stderr, "qmm: rows=%d variant=%d ntw=%d kwaves=%d splitk=%d grid=%d\n", rows,
@@ -327,6 +397,8 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
     if (!strcmp(v, "gemv")) p->force_variant = QMM_VARIANT_GEMV;
     if (!strcmp(v, "mfma")) p->force_variant = QMM_VARIANT_MFMA;
     if (!strcmp(v, "stream")) p->force_variant = QMM_VARIANT_STREAM;
+    if (!strcmp(v, "persist")) p->force_variant = QMM_VARIANT_PERSIST;
+    if (!strcmp(v, "resident")) p->force_variant = QMM_VARIANT_RESIDENT;
   }
   p->env_ntw = env_int("QMM_NTW");
   p->env_splitk = env_int("QMM_SPLITK");
@@ -409,7 +481,7 @@ qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, 
 qmm_status qmm_get_stats(const qmm_plan* p, qmm_stats* out) {
   if (qmm_status st = check_plan(p)) return st;
   if (!out) return fail(QMM_ERR_INVALID_ARG, "out is NULL");
-  for (int i = 0; i < 4; ++i) out->launches[i] = p->launches[i].load();
+  for (int i = 0; i < 6; ++i) out->launches[i] = p->launches[i].load();
   out->last_variant = p->last_variant;
   out->last_ntw = p->last_ntw;
   out->last_splitk = p->last_splitk;

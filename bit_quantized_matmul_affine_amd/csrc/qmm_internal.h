@@ -43,6 +43,17 @@ hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArg
                          size_t lds_bytes, hipStream_t st);
 size_t stream_lds_bytes(int nw, int M, int K);
 bool stream_fits(int nw, int M, int K);
+hipError_t launch_persist(int bits, bool sb_f32, int mt, int tm, int nwc, const LaunchArgs& a,
+                          int grid, size_t lds_bytes, hipStream_t st);
+size_t persist_lds_bytes(int mt, int rc);
+hipError_t launch_resident(int bits, bool sb_f32, int tm, int cpw, int xv, const LaunchArgs& a,
+                           int grid, size_t lds_bytes, hipStream_t st);
+// Chunks per wave of the resident kernel built for `tm` tile slots that
+// covers nC chunks of K, or 0 if none does.
+int resident_cpw(int tm, int nC);
+int resident_stage_vectors(int M, int K, int nw);
+inline int resident_waves(int tm) { return tm == 4 ? 16 : 12; }
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 
 // Bytes of LDS the vector-ALU kernel needs for `mr` rows over `kslice` columns.

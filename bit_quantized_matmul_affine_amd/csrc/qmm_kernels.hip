@@ -598,6 +598,377 @@ bool stream_fits(int nw, int M, int K) {
 }
 
 // ---------------------------------------------------------------------------
+// Persistent MFMA kernel for longer activation blocks.  One workgroup per
+// compute unit; workgroup g owns tiles g, g+G, g+2G, ... (at most TM at a
+// time; more are taken in passes).  K is walked in rounds of RC chunks:
+//   * NWL loader waves copy the next round's activation slice (16*MT rows x
+//     RC*128 columns) into registers, form the per-(row, group) sums with
+//     8-lane shuffles, and write both to the idle one of two LDS buffers; the
+//     copy is issued and retired within one round, so its registers are
+//     never live across a barrier;
+//   * NWC compute waves: wave w takes chunks j*RC + w + NWC*i (i < RC/NWC) of
+//     every owned tile; its weight loads run DR rounds ahead in a statically
+//     indexed ring;
+//   * loader and compute waves keep separate in-order load queues, so neither
+//     waits on the other's loads; one barrier per round; partial tiles are
+//     added across compute waves through LDS in wave order after a pass.
+// Rows >= M of a slice repeat row M-1 (their outputs are never stored).
+// ---------------------------------------------------------------------------
+template <int BITS, int MT, int RC, int NWC, int NWL, int TM, int DR, typename ST>
+__global__ void __launch_bounds__((NWC + NWL) * 64) persist_kernel(LaunchArgs a) {
+  constexpr int CPW = RC / NWC;           // chunks per compute wave per round
+  constexpr int XROW = RC * kChunkK + 8;  // padded LDS row, bf16 elements
+  constexpr int GR = 2 * RC;              // groups per round
+  constexpr int ROWS = 16 * MT;
+  constexpr int SV = ROWS * RC * 16;      // 16-byte vectors per slice
+  static_assert(SV % (NWL * 64) == 0, "slice must split evenly over loader lanes");
+  constexpr int LV = SV / (NWL * 64);     // vectors per loader lane
+  constexpr size_t XBUF = (size_t)ROWS * XROW;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  uint16_t* xbuf = reinterpret_cast<uint16_t*>(lds);                      // [2][ROWS][XROW]
+  float* xsum = reinterpret_cast<float*>(lds + (size_t)2 * XBUF * 2);     // [2][GR][ROWS]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool loader = wave >= NWC;
+  const int lt = threadIdx.x - NWC * 64;  // loader thread index
+  const int w = wave;                     // compute wave index
+  const int r = lane & 15, kg = lane >> 4;
+  const int G = gridDim.x;
+  const int nT = a.N / kTileN, nC = a.K / kChunkK;
+  const int nR = (nC + RC - 1) / RC;
+  const int M = a.M;
+  const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
+  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  // Loader: slice j -> LDS buffer b, with group sums.  Consecutive loader
+  // lanes hold consecutive 16-byte vectors of a row, so the 8 vectors of a
+  // group sit on 8 aligned lanes.
+  auto copy_slice = [&](int j, int b) {
+    u32x4 xv[LV];
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int idx = lt + i * NWL * 64;
+      const int row = idx / (RC * 16), v = idx - row * (RC * 16);
+      const int col = min(j * RC * kChunkK + 8 * v, a.K - 8);
+      xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)min(row, M - 1) * a.ldx + col);
+    }
+    uint16_t* dst = xbuf + (size_t)b * XBUF;
+    float* sdst = xsum + (size_t)b * GR * ROWS;
+#pragma unroll
+    for (int i = 0; i < LV; ++i) {
+      const int idx = lt + i * NWL * 64;
+      const int row = idx / (RC * 16), v = idx - row * (RC * 16);
+      *reinterpret_cast<u32x4*>(dst + (size_t)row * XROW + 8 * v) = xv[i];
+      float sm = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sm += __uint_as_float(xv[i][e] << 16);
+        sm += __uint_as_float(xv[i][e] & 0xFFFF0000u);
+      }
+      sm += __shfl_xor(sm, 1);
+      sm += __shfl_xor(sm, 2);
+      sm += __shfl_xor(sm, 4);
+      if ((lane & 7) == 0) sdst[(v >> 3) * ROWS + row] = sm;
+    }
+  };
+
+  // Compute waves: weight ring of DR rounds.
+  uint32_t W[DR][CPW][TM][BITS];
+  SBPair<ST> SBv[DR][CPW][TM];
+  f32x4 acc[TM][MT];
+  const uint32_t mask_v = pair_mask_vgpr<BITS>();
+
+  for (int pass_t0 = blockIdx.x; pass_t0 < nT; pass_t0 += G * TM) {
+    int tiles[TM];
+    int ntl = 0;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int t = pass_t0 + i * G;
+      tiles[i] = t < nT ? t : nT - 1;
+      ntl += t < nT ? 1 : 0;
+    }
+    auto load_round = [&](int j, int d) {
+#pragma unroll
+      for (int u = 0; u < CPW; ++u) {
+        const int c = min(j * RC + w + NWC * u, nC - 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const uint32_t* p = a.codes + (((long)tiles[i] * nC + c) * 64 + lane) * BITS;
+#pragma unroll
+          for (int q = 0; q < BITS; ++q) W[d][u][i][q] = __builtin_nontemporal_load(p + q);
+          SBv[d][u][i].load(sbp + (((long)tiles[i] * nC + c) * kTileN + r) * 4);
+        }
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[i][mt] = zero;
+
+    if (loader) {
+      copy_slice(0, 0);
+    } else {
+#pragma unroll
+      for (int d = 0; d < DR; ++d)
+        if (d < nR) load_round(d, d);
+    }
+    __syncthreads();
+
+    for (int j0 = 0; j0 < nR; j0 += DR) {
+#pragma unroll
+      for (int d = 0; d < DR; ++d) {
+        const int j = j0 + d;
+        if (j < nR) {
+          const int b = j & 1;
+          if (loader) {
+            if (j + 1 < nR) copy_slice(j + 1, b ^ 1);
+          } else {
+            const float* sb_ = xsum + (size_t)b * GR * ROWS;
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) {
+              const int cl = w + NWC * u;  // chunk within the round
+              if (j * RC + cl < nC) {
+                const uint16_t* xb = xbuf + (size_t)b * XBUF + 128 * cl + 16 * kg;
+                if constexpr (MT == 1) {
+                  u32x4 A[4];
+#pragma unroll
+                  for (int t = 0; t < 4; ++t)
+                    A[t] = *reinterpret_cast<const u32x4*>(xb + (size_t)r * XROW + 64 * (t >> 1) +
+                                                           8 * (t & 1));
+                  f32x4 ex[2];
+#pragma unroll
+                  for (int gp = 0; gp < 2; ++gp)
+                    ex[gp] = *reinterpret_cast<const f32x4*>(sb_ + (2 * cl + gp) * ROWS + 4 * kg);
+#pragma unroll
+                  for (int i = 0; i < TM; ++i) {
+                    if (i < ntl) {
+                      uint32_t P[16];
+                      unpack_pairs<BITS>(W[d][u][i], P, mask_v);
+#pragma unroll
+                      for (int gp = 0; gp < 2; ++gp) {
+                        const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
+                        const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
+                        f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0),
+                            zero, 0, 0, 0);
+                        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, A[2 * gp + 1]),
+                            __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
+                        const float sc = SBv[d][u][i].s(gp);
+                        const float bp = SBv[d][u][i].b(gp) - 128.f * sc;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                          acc[i][0][q] = fmaf(sc, dd[q], fmaf(bp, ex[gp][q], acc[i][0][q]));
+                      }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                  }
+                } else {
+                  uint32_t P[TM][16];
+#pragma unroll
+                  for (int i = 0; i < TM; ++i) unpack_pairs<BITS>(W[d][u][i], P[i], mask_v);
+#pragma unroll
+                  for (int mt = 0; mt < MT; ++mt) {
+                    u32x4 A[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                      A[t] = *reinterpret_cast<const u32x4*>(xb + (size_t)(16 * mt + r) * XROW +
+                                                             64 * (t >> 1) + 8 * (t & 1));
+#pragma unroll
+                    for (int gp = 0; gp < 2; ++gp) {
+                      const f32x4 ex = *reinterpret_cast<const f32x4*>(
+                          sb_ + (2 * cl + gp) * ROWS + 16 * mt + 4 * kg);
+#pragma unroll
+                      for (int i = 0; i < TM; ++i) {
+                        if (i < ntl) {
+                          const u32x4 B0 = {P[i][8 * gp + 0], P[i][8 * gp + 1], P[i][8 * gp + 2], P[i][8 * gp + 3]};
+                          const u32x4 B1 = {P[i][8 * gp + 4], P[i][8 * gp + 5], P[i][8 * gp + 6], P[i][8 * gp + 7]};
+                          f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                              __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0),
+                              zero, 0, 0, 0);
+                          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                              __builtin_bit_cast(bf16x8, A[2 * gp + 1]),
+                              __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
+                          const float sc = SBv[d][u][i].s(gp);
+                          const float bp = SBv[d][u][i].b(gp) - 128.f * sc;
+#pragma unroll
+                          for (int q = 0; q < 4; ++q)
+                            acc[i][mt][q] = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[i][mt][q]));
+                        }
+                      }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                  }
+                }
+              }
+            }
+            if (j + DR < nR) load_round(j + DR, d);
+          }
+          __syncthreads();
+        }
+      }
+    }
+
+    // Fold the NWC partial tiles (LDS reused: activations are dead now).
+    f32x4* red = reinterpret_cast<f32x4*>(lds);  // [TM][MT][NWC][64]
+    if (!loader) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) red[((i * MT + mt) * NWC + w) * 64 + lane] = acc[i][mt];
+    }
+    __syncthreads();
+    if (!loader) {
+      for (int job = w; job < TM * MT; job += NWC) {
+        const int i = job / MT, mt = job - i * MT;
+        if (i >= ntl) continue;
+        f32x4 s = red[((i * MT + mt) * NWC + 0) * 64 + lane];
+        for (int v = 1; v < NWC; ++v) s += red[((i * MT + mt) * NWC + v) * 64 + lane];
+        const int n = tiles[i] * kTileN + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = 16 * mt + 4 * kg + q;
+          if (m < M) store_y<false>(a.y, (long)m * a.ldy + n, s[q]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+size_t persist_lds_bytes(int mt, int rc) {
+  return (size_t)2 * 16 * mt * (rc * kChunkK + 8) * 2 + (size_t)2 * 2 * rc * 16 * mt * 4;
+}
+
+// ---------------------------------------------------------------------------
+// Resident MFMA kernel for blocks of up to 16 activation rows whose whole
+// activation block fits in LDS (rows*K*2 <= 160 KB).  One workgroup per
+// compute unit; workgroup g owns tiles g, g+G, ... (TM slots, one pass).
+//   1. every thread loads its XV vectors of the activation block, then every
+//      wave issues the loads of all (at most CPW) chunks it will use, then
+//      the activations go to LDS; one barrier.  Loads retire in issue order,
+//      so the wait for the activations retires no weight load;
+//   2. wave v works on tile slot v / WPT and on the chunks kpart, kpart+WPT,
+//      ... of K (kpart = v % WPT) with no further barrier or wait on memory
+//      other than its own weights;
+//   3. the WPT partial tiles of each tile are added through LDS (reusing the
+//      activation space) in K-part order.
+// LDS holds row m's 16-byte vector v at position v ^ (m & 15), so the 16 rows
+// an A-fragment read touches fall on distinct banks without padding.
+// ---------------------------------------------------------------------------
+template <int BITS, int NW, int TM, int CPW, int XV, typename ST>
+__global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
+  constexpr int WPT = NW / TM;
+  static_assert(NW % TM == 0, "waves must split evenly over tile slots");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);  // [M][K/8] swizzled vectors
+  const int lane = threadIdx.x & 63, v = threadIdx.x >> 6;
+  const int r = lane & 15, kg = lane >> 4;
+  const int slot = v / WPT, kpart = v - slot * WPT;
+  const int G = gridDim.x;
+  const int nT = a.N / kTileN, nC = a.K / kChunkK;
+  const int M = a.M;
+  const int kv = a.K / 8;  // vectors per activation row
+  const int tile = blockIdx.x + slot * G;
+  const bool active = tile < nT;
+  const int t = active ? tile : nT - 1;
+  // chunks of this wave (the host guarantees count <= CPW)
+  const int count = nC > kpart ? (nC - kpart + WPT - 1) / WPT : 0;
+  // last chunk this wave reads; a wave with no chunks (nC < WPT) reads chunk 0
+  const int clast = count > 0 ? kpart + (count - 1) * WPT : 0;
+  const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
+  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
+
+  // 1a. activation loads (indices past the end repeat the last vector)
+  const int vecs = M * kv;
+  u32x4 xv[XV];
+  int xi[XV];
+#pragma unroll
+  for (int i = 0; i < XV; ++i) {
+    xi[i] = min((int)threadIdx.x + i * NW * 64, vecs - 1);
+    const int m = xi[i] / kv, c = xi[i] - m * kv;
+    xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)m * a.ldx + 8 * c);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 1b. every weight load of this wave (chunks past the last repeat it)
+  const uint32_t* cbase = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
+  const ST* sbase = sbp + ((long)t * nC * kTileN + r) * 4;
+  uint32_t W[CPW][BITS];
+  SBPair<ST> SBv[CPW];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int c = min(kpart + j * WPT, clast);
+    const uint32_t* p = cbase + (long)c * 64 * BITS;
+#pragma unroll
+    for (int q = 0; q < BITS; ++q) W[j][q] = __builtin_nontemporal_load(p + q);
+    SBv[j].load(sbase + (long)c * kTileN * 4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 1c. activations to LDS
+#pragma unroll
+  for (int i = 0; i < XV; ++i) {
+    const int m = xi[i] / kv, c = xi[i] - m * kv;
+    xs[(long)m * kv + (c ^ (m & 15))] = xv[i];
+  }
+  __syncthreads();
+
+  // 2. this wave's chunks
+  const int xm = min(r, M - 1);
+  const u32x4* xrow = xs + (long)xm * kv;
+  const int sw = xm & 15;
+  const uint32_t mask_v = pair_mask_vgpr<BITS>();
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc = zero;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const bool live = j < count;
+    const int c = min(kpart + j * WPT, clast);
+    u32x4 A[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)  // vector of (chunk c, group q>>1, quarter kg, half q&1)
+      A[q] = xrow[(16 * c + 8 * (q >> 1) + 2 * kg + (q & 1)) ^ sw];
+    uint32_t P[16];
+    unpack_pairs<BITS>(W[j], P, mask_v);
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0, 0, 0);
+      const f32x4 ex = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
+      const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
+      const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
+      f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
+      dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
+                                                   __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
+      const float s0 = SBv[j].s(gp);
+      const float sc = live ? s0 : 0.f;
+      const float bp = live ? SBv[j].b(gp) - 128.f * s0 : 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[q]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 3. fold the WPT partial tiles of each slot in K-part order
+  __syncthreads();  // activations are dead from here on
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [NW][64]
+  red[v * 64 + lane] = acc;
+  __syncthreads();
+  if (kpart != 0 || !active) return;
+  for (int i = 1; i < WPT; ++i) acc += red[(v + i) * 64 + lane];
+  const int n = tile * kTileN + r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = 4 * kg + q;
+    if (m < M) store_y<false>(a.y, (long)m * a.ldy + n, acc[q]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU kernel: up to MR activation rows per pass, activations of the
 // workgroup's K split staged in LDS together with per-(row, group, quarter)
 // sums.  Each of the 4 wavefronts owns NTW tiles; lane (r, kg) accumulates
@@ -922,6 +1293,91 @@ hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArg
                          size_t lds_bytes, hipStream_t st) {
   if (bits == 3) return sb_f32 ? stream_dispatch<3, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<3, uint16_t>(nw, cpw, a, lds_bytes, st);
   return sb_f32 ? stream_dispatch<4, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<4, uint16_t>(nw, cpw, a, lds_bytes, st);
+}
+
+template <int BITS, typename ST>
+static hipError_t persist_dispatch(int mt, int tm, int nwc, const LaunchArgs& a, int grid,
+                                   size_t lds, hipStream_t st) {
+#define QMM_PERSIST(MTV, RCV, NWCV, TMV, DRV)                                                    \
+  if (mt == MTV && tm == TMV && nwc == NWCV) {                                                   \
+    auto* kfn = &persist_kernel<BITS, MTV, RCV, NWCV, 4, TMV, DRV, ST>;                          \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                       \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);    \
+    if (e != hipSuccess) return e;                                                               \
+    kfn<<<grid, (NWCV + 4) * 64, lds, st>>>(a);                                                  \
+    return hipGetLastError();                                                                    \
+  }
+  QMM_PERSIST(1, 8, 4, 1, 2) QMM_PERSIST(1, 8, 4, 2, 2) QMM_PERSIST(1, 8, 4, 3, 2) QMM_PERSIST(1, 8, 4, 4, 2)
+  QMM_PERSIST(1, 8, 8, 1, 2) QMM_PERSIST(1, 8, 8, 2, 2)
+  QMM_PERSIST(2, 4, 4, 1, 2) QMM_PERSIST(2, 4, 4, 2, 2) QMM_PERSIST(2, 4, 4, 3, 2)
+  QMM_PERSIST(4, 4, 4, 1, 2) QMM_PERSIST(4, 4, 4, 2, 2) QMM_PERSIST(4, 4, 4, 3, 2)
+#undef QMM_PERSIST
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_persist(int bits, bool sb_f32, int mt, int tm, int nwc, const LaunchArgs& a,
+                          int grid, size_t lds_bytes, hipStream_t st) {
+  if (bits == 3) return sb_f32 ? persist_dispatch<3, float>(mt, tm, nwc, a, grid, lds_bytes, st) : persist_dispatch<3, uint16_t>(mt, tm, nwc, a, grid, lds_bytes, st);
+  return sb_f32 ? persist_dispatch<4, float>(mt, tm, nwc, a, grid, lds_bytes, st) : persist_dispatch<4, uint16_t>(mt, tm, nwc, a, grid, lds_bytes, st);
+}
+
+template <int BITS, typename ST, int NW, int TM, int CPW>
+static hipError_t resident_launch_xv(int xv, const LaunchArgs& a, int grid, size_t lds,
+                                     hipStream_t st) {
+#define QMM_RES(XVV)                                                                          \
+  if (xv == XVV) {                                                                            \
+    auto* kfn = &resident_kernel<BITS, NW, TM, CPW, XVV, ST>;                                 \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                    \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (e != hipSuccess) return e;                                                            \
+    kfn<<<grid, NW * 64, lds, st>>>(a);                                                       \
+    return hipGetLastError();                                                                 \
+  }
+  QMM_RES(2) QMM_RES(4) QMM_RES(8) QMM_RES(14)
+#undef QMM_RES
+  return hipErrorInvalidValue;
+}
+
+// (tile slots, waves, chunks per wave) shapes of the resident kernel.
+#define QMM_RESIDENT_SHAPES(X) X(1, 12, 4) X(1, 12, 8) X(1, 12, 11) X(2, 12, 7) X(2, 12, 11) \
+  X(3, 12, 10) X(4, 16, 10)
+
+int resident_cpw(int tm, int nC) {
+  const int nw = resident_waves(tm), wpt = nw / tm;
+  const int need = (nC + wpt - 1) / wpt;
+  int best = 0;
+#define QMM_PICK(T, W, C) if (T == tm && C >= need && (best == 0 || C < best)) best = C;
+  QMM_RESIDENT_SHAPES(QMM_PICK)
+#undef QMM_PICK
+  return best;
+}
+
+template <int BITS, typename ST>
+static hipError_t resident_dispatch(int tm, int cpw, int xv, const LaunchArgs& a, int grid,
+                                    size_t lds, hipStream_t st) {
+#define QMM_GO(T, W, C) \
+  if (tm == T && cpw == C) return resident_launch_xv<BITS, ST, W, T, C>(xv, a, grid, lds, st);
+  QMM_RESIDENT_SHAPES(QMM_GO)
+#undef QMM_GO
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_resident(int bits, bool sb_f32, int tm, int cpw, int xv, const LaunchArgs& a,
+                           int grid, size_t lds_bytes, hipStream_t st) {
+  if (bits == 3)
+    return sb_f32 ? resident_dispatch<3, float>(tm, cpw, xv, a, grid, lds_bytes, st)
+                  : resident_dispatch<3, uint16_t>(tm, cpw, xv, a, grid, lds_bytes, st);
+  return sb_f32 ? resident_dispatch<4, float>(tm, cpw, xv, a, grid, lds_bytes, st)
+                : resident_dispatch<4, uint16_t>(tm, cpw, xv, a, grid, lds_bytes, st);
+}
+
+// 16-byte activation vectors each thread stages (2, 4, 8 or 14), or 0 if
+// the block is too large.
+int resident_stage_vectors(int M, int K, int nw) {
+  const long vecs = (long)M * K / 8;
+  for (int xv : {2, 4, 8, 14})
+    if (vecs <= (long)xv * nw * 64) return xv;
+  return 0;
 }
 
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {

@@ -23,6 +23,12 @@ def stream_ok(K: int, rows: int) -> bool:
     return nC <= 128 and rows * K <= nw * 64 * xv * 8 and rows * K * 2 + (nw - 1) * 1024 <= 65536
 
 
+def resident_ok(K: int, rows: int) -> bool:
+    """Whether the resident kernel takes a block of `rows` rows at this K
+    (the whole activation block of up to 16 rows in one compute unit's LDS)."""
+    return min(rows, 16) * K * 2 <= 160 * 1024
+
+
 def y_to_f64(y_bits: np.ndarray, x_dtype: str) -> np.ndarray:
     if x_dtype == "bf16":
         return oracle.decode_bf16(y_bits)

@@ -10,7 +10,7 @@ import pytest
 import oracle
 from bit_quantized_matmul_affine_amd import binding as b
 from bit_quantized_matmul_affine_amd import synth
-from tests.gpu_util import Runner, check_against_oracle, say, stream_ok
+from tests.gpu_util import Runner, check_against_oracle, resident_ok, say, stream_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -86,7 +86,8 @@ SMALL = [
 def _variants(x_dtype, M, K):
     out = ["gemv"]
     if x_dtype == "bf16":
-        out += ["mfma"] + (["stream"] if stream_ok(K, M) else [])
+        out += ["mfma", "persist"] + (["stream"] if stream_ok(K, M) else []) + (
+            ["resident"] if resident_ok(K, M) else [])
     return out
 
 
@@ -96,8 +97,9 @@ def test_small_parity(case):
     p = synth.small(100 + M, bits=bits, K=K, N=N, M=M, x_dtype=xd, sb_dtype=sd)
     r = Runner(p)
     for v in _variants(xd, M, K):
-        shapes = [(0, 0, 0)] if v == "stream" else [(0, 0, 0), (1, 1, 1), (2, 2, 2), (1, 4, 3),
-                                                    (2, 4, 1), (4, 1, 2)]
+        shapes = {"stream": [(0, 0, 0)], "persist": [(0, 0, 0), (1, 0, 0), (2, 0, 0), (3, 0, 0)],
+                  "resident": [(0, 0, 0), (1, 0, 0), (2, 0, 0), (3, 0, 0), (4, 0, 0)]}.get(
+            v, [(0, 0, 0), (1, 1, 1), (2, 2, 2), (1, 4, 3), (2, 4, 1), (4, 1, 2)])
         for ntw, kw, s in shapes:
             if s > K // 128:
                 continue
@@ -112,12 +114,13 @@ def test_small_parity(case):
 def test_determinism_and_row_independence():
     p = synth.small(7, bits=3, K=1024, N=320, M=16)
     r = Runner(p)
-    for v, ntw, kw, s in (("mfma", 1, 2, 4), ("mfma", 2, 4, 1), ("gemv", 1, 0, 4), ("stream", 0, 0, 0)):
+    for v, ntw, kw, s in (("mfma", 1, 2, 4), ("mfma", 2, 4, 1), ("gemv", 1, 0, 4), ("stream", 0, 0, 0),
+                          ("persist", 0, 0, 0), ("resident", 0, 0, 0)):
         say("determinism", v)
         a = r.run(variant=v, ntw=ntw, kwaves=kw, splitk=s)
         b2 = r.run(variant=v, ntw=ntw, kwaves=kw, splitk=s)
         assert np.array_equal(a, b2)
-        if v in ("mfma", "stream"):
+        if v in ("mfma", "stream", "persist", "resident"):
             a9 = r.run(rows=9, variant=v, ntw=ntw, kwaves=kw, splitk=s)
             assert np.array_equal(a9[:9], a[:9])
 
@@ -126,7 +129,7 @@ def test_rows_past_m_and_past_end_untouched():
     import torch
     p = synth.small(8, bits=4, K=512, N=64, M=5)
     r = Runner(p, max_rows=8)
-    for v in ("mfma", "gemv", "stream"):
+    for v in ("mfma", "gemv", "stream", "persist", "resident"):
         say("canary", v)
         out = torch.full((9, 64), 7.0, dtype=torch.bfloat16, device="cuda")
         r.lin.plan.run(r.x[:5], r.lin.codes, r.lin.sb, out=out[:5], variant=v, splitk=2)
@@ -148,6 +151,15 @@ def test_non_default_stream_and_workspace_reuse():
                                stream=s)
             s.synchronize()
             check_against_oracle(p.rows(rows), b.to_numpy_bits(y), label="rows %d" % rows)
+
+
+def test_resident_rejects_blocks_too_long_for_lds():
+    p = synth.small(13, bits=4, K=6144, N=32, M=16)   # 16*6144*2 bytes > 160 KB
+    r = Runner(p)
+    with pytest.raises(b.QmmError) as ei:
+        r.run(variant="resident")
+    assert ei.value.status == b.QMM_ERR_UNSUPPORTED
+    check_against_oracle(p, r.run(rows=13, variant="resident"), rows=13, label="13 rows fit")
 
 
 def test_stream_rejects_blocks_too_long_for_lds():
@@ -183,7 +195,7 @@ def test_workload0_full(variant):
     check_against_oracle(p, r.run(variant=variant), label="w0 " + variant)
 
 
-@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma", "stream"])
+@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma", "stream", "persist", "resident"])
 def test_workload1_full(variant):
     (p,) = synth.workload(1)
     say("workload 1", variant)
@@ -195,7 +207,7 @@ def test_workload1_full(variant):
 def test_workload2_full(rows):
     (p,) = synth.workload(2)
     r = Runner(p, max_rows=64)
-    variants = ["auto", "mfma"] + (["gemv"] if rows <= 9 else []) + (
+    variants = ["auto", "mfma", "persist", "resident"] + (["gemv"] if rows <= 9 else []) + (
         ["stream"] if stream_ok(p.K, rows) else [])
     for v in variants:
         say("workload 2 rows", rows, v)
@@ -206,18 +218,30 @@ def test_workload2_full(rows):
 def test_workload3_full():
     for p in synth.workload(3):
         r = Runner(p)
-        for v in ("auto", "gemv", "mfma") + (("stream",) if stream_ok(p.K, p.M) else ()):
+        for v in ("auto", "gemv", "mfma", "persist") + (("stream",) if stream_ok(p.K, p.M) else ()) + (
+                ("resident",) if resident_ok(p.K, p.M) else ()):
             say("workload 3", p.name, v)
             check_against_oracle(p, r.run(variant=v), label="w3 %s %s" % (p.name, v))
         del r
 
 
-def test_workload4_sampled():
-    (p,) = synth.workload(4)
-    say("workload 4")
+def test_persist_multiple_passes_and_partial_rounds():
+    """More tiles than workgroups (tile passes) and a K that is not a whole
+    number of rounds."""
+    p = synth.small(12, bits=3, K=640, N=4160, M=20)
     r = Runner(p)
-    y = r.run()
-    check_against_oracle(p, y, sample=(3000, 4), label="w4 sampled")
+    for tm in (1, 2):
+        say("persist passes tm", tm)
+        check_against_oracle(p, r.run(variant="persist", ntw=tm), label="persist tm=%d" % tm)
+
+
+@pytest.mark.parametrize("variant", ["auto", "persist"])
+def test_workload4_sampled(variant):
+    (p,) = synth.workload(4)
+    say("workload 4", variant)
+    r = Runner(p)
+    y = r.run(variant=variant)
+    check_against_oracle(p, y, sample=(3000, 4), label="w4 sampled " + variant)
     # every output row and column is finite and rows are distinct results
     yf = oracle.decode_bf16(y)
     assert np.all(np.isfinite(yf))
