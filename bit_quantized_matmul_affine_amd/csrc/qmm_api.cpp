@@ -58,7 +58,7 @@ struct qmm_plan {
   int nT, nC;
   int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
   int env_ntw, env_splitk, env_kwaves;
-  mutable std::atomic<uint64_t> launches[6];
+  mutable std::atomic<uint64_t> launches[7];
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
 };
 
@@ -122,13 +122,25 @@ bool resident_fits(const qmm_plan* p, int rows) {
          qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(1)) > 0;
 }
 
+bool slab_fits(const qmm_plan* p) {
+  return qmm::slab_slices(2, p->nC) > 0 && qmm::slab_slices(4, p->nC) > 0;
+}
+
 int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
   if (p->force_variant) return p->force_variant;
+  // Measured on the 3-bit 5120->10240 sweep: the streaming kernel while the
+  // activation block fits its LDS budget, the resident kernel while each
+  // thread stages at most eight activation vectors (beyond that it spills),
+  // the slab kernel for longer blocks where it is built for this K.
   int nw, cpw;
   if (rows <= 16 && stream_shape(p, &nw, &cpw) && qmm::stream_fits(nw, rows, (int)p->d.K))
     return QMM_VARIANT_STREAM;
+  if (rows <= 16 && resident_fits(p, rows) &&
+      qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(1)) <= 8)
+    return QMM_VARIANT_RESIDENT;
+  if (slab_fits(p)) return QMM_VARIANT_SLAB;
   return QMM_VARIANT_MFMA;
 }
 
@@ -173,6 +185,19 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.S = 1;
     const int r = std::min(rows, 16);
     c.lds = std::max((size_t)r * p->d.K * 2, (size_t)c.wk * 64 * 16);
+    return c;
+  }
+  if (variant == QMM_VARIANT_SLAB) {
+    c.rows_per_launch = qmm::kMaxMfmaRows;
+    const int r = std::min(rows, qmm::kMaxMfmaRows);
+    c.tile_rows = r <= 32 ? 2 : 4;
+    c.cpw = qmm::slab_slices(c.tile_rows, nC);
+    c.ntw = qmm::kSlabTiles;
+    c.wk = 4;
+    c.grid = (nT + qmm::kSlabTiles - 1) / qmm::kSlabTiles;
+    c.nTB = c.grid;
+    c.S = 1;
+    c.lds = qmm::slab_lds_bytes(c.tile_rows);
     return c;
   }
   if (variant == QMM_VARIANT_STREAM) {
@@ -277,10 +302,11 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   if (!x || !codes || !sb || !y) return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(sb, 16) || !aligned(y, 4))
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
-  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_RESIDENT)
+  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_SLAB)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
   if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM ||
-       variant_req == QMM_VARIANT_PERSIST || variant_req == QMM_VARIANT_RESIDENT) &&
+       variant_req == QMM_VARIANT_PERSIST || variant_req == QMM_VARIANT_RESIDENT ||
+       variant_req == QMM_VARIANT_SLAB) &&
       p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
   if (variant_req == QMM_VARIANT_STREAM) {
@@ -294,6 +320,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     return fail(QMM_ERR_UNSUPPORTED,
                 "the resident kernel needs rows*K*2 bytes of activations (rows capped at 16) "
                 "to fit one compute unit's 160 KB of LDS");
+  if (variant_req == QMM_VARIANT_SLAB && !slab_fits(p))
+    return fail(QMM_ERR_UNSUPPORTED, "the slab kernel is built for K = 5120 and 8192 (K=%lld)",
+                (long long)p->d.K);
   if (ntw_req < 0 || ntw_req > 8 || s_req < 0 || wk_req < 0 || wk_req > 8)
     return fail(QMM_ERR_INVALID_ARG, "ntw must be 0..8, kwaves 0..8 and splitk >= 0");
   const int ntw_eff = ntw_req ? ntw_req : p->env_ntw;
@@ -331,7 +360,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (variant == QMM_VARIANT_RESIDENT)
+    if (variant == QMM_VARIANT_SLAB)
+      e = qmm::launch_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, a, cb.grid, cb.lds, st);
+    else if (variant == QMM_VARIANT_RESIDENT)
       e = qmm::launch_resident(p->d.bits, sf, cb.ntw, cb.cpw,
                                qmm::resident_stage_vectors(rb, (int)p->d.K, cb.wk), a, cb.grid,
                                cb.lds, st);
@@ -348,7 +379,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     p->last_variant = variant;
     p->last_ntw = cb.ntw;
     p->last_splitk = cb.S;
-    p->last_grid = (variant == QMM_VARIANT_PERSIST || variant == QMM_VARIANT_RESIDENT) ? cb.grid : cb.nTB * cb.S;
+    p->last_grid = (variant == QMM_VARIANT_PERSIST || variant == QMM_VARIANT_RESIDENT ||
+                    variant == QMM_VARIANT_SLAB)
+                       ? cb.grid : cb.nTB * cb.S;
   }
   if (getenv("QMM_LOG"))
     fprintf(stderr, "qmm: rows=%d variant=%d ntw=%d kwaves=%d splitk=%d grid=%d\n", rows,
@@ -399,6 +432,7 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
     if (!strcmp(v, "stream")) p->force_variant = QMM_VARIANT_STREAM;
     if (!strcmp(v, "persist")) p->force_variant = QMM_VARIANT_PERSIST;
     if (!strcmp(v, "resident")) p->force_variant = QMM_VARIANT_RESIDENT;
+    if (!strcmp(v, "slab")) p->force_variant = QMM_VARIANT_SLAB;
   }
   p->env_ntw = env_int("QMM_NTW");
   p->env_splitk = env_int("QMM_SPLITK");
@@ -481,7 +515,7 @@ qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, 
 qmm_status qmm_get_stats(const qmm_plan* p, qmm_stats* out) {
   if (qmm_status st = check_plan(p)) return st;
   if (!out) return fail(QMM_ERR_INVALID_ARG, "out is NULL");
-  for (int i = 0; i < 6; ++i) out->launches[i] = p->launches[i].load();
+  for (int i = 0; i < 7; ++i) out->launches[i] = p->launches[i].load();
   out->last_variant = p->last_variant;
   out->last_ntw = p->last_ntw;
   out->last_splitk = p->last_splitk;

@@ -52,6 +52,13 @@ hipError_t launch_resident(int bits, bool sb_f32, int tm, int cpw, int xv, const
 // covers nC chunks of K, or 0 if none does.
 int resident_cpw(int tm, int nC);
 int resident_stage_vectors(int M, int K, int nw);
+// Slab kernel: tile slots per workgroup, slices of K built for `mt` row tiles
+// (0 if none covers nC chunks), dynamic LDS bytes.
+constexpr int kSlabTiles = 3;
+int slab_slices(int mt, int nC);
+size_t slab_lds_bytes(int mt);
+hipError_t launch_slab(int bits, bool sb_f32, int mt, int ns, const LaunchArgs& a, int grid,
+                       size_t lds_bytes, hipStream_t st);
 inline int resident_waves(int tm) { return tm == 4 ? 16 : 12; }
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);

@@ -969,6 +969,205 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Slab kernel for 17..64 activation rows.  One workgroup per compute unit
+// owning TM tiles of W; K is walked in NS slices of four chunks (512 k).
+//   * four loader waves copy activation slices straight from global memory
+//     into a ring of RB LDS slots (LDS-direct loads: no registers), running
+//     up to RB-1 slices ahead; they wait only on their own loads;
+//   * 4*TM compute waves: wave (i, kp) owns tile slot i and chunk kp of every
+//     slice, keeps its weight loads DR slices ahead in a register ring, and
+//     forms the per-group activation sums with an all-ones MFMA;
+//   * one barrier per slice; the slice loop is unrolled, so every wait on
+//     memory is an exact count and no wave waits on another's loads.
+// An LDS slot holds [16*MT rows][64 vectors of 16 bytes]; row m keeps its
+// vector v at v ^ (m & 15) (16 rows reading one column hit distinct banks).
+// Rows >= M repeat row M-1 (their outputs are never stored).  The four
+// partial tiles of each tile are added through LDS in K order at the end.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter limited to N (N <= 63).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// wait_vm<n * RPL>() for a count n in 0..C known once the caller is unrolled.
+template <int RPL, int C>
+__device__ __forceinline__ void wait_slices(int n) {
+  if constexpr (C <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= C)
+      wait_vm<C * RPL>();
+    else
+      wait_slices<RPL, C - 1>(n);
+  }
+}
+
+// s_waitcnt for every outstanding LDS access (vector-memory counter untouched).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int BITS, int MT, int TM, int NS, int RB, int DR, typename ST>
+__global__ void __launch_bounds__((TM * 4 + 4) * 64) slab_kernel(LaunchArgs a) {
+  constexpr int KP = 4, NWC = TM * KP, NWL = 4;
+  constexpr int ROWS = 16 * MT;
+  constexpr int SK = KP * kChunkK;  // k per slice
+  constexpr int SLOT = ROWS * 64;   // vectors per slot
+  constexpr int RPL = ROWS / NWL;   // rows per loader wave per slice
+  constexpr int NB = RB < NS ? RB : NS;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  u32x4* xs = reinterpret_cast<u32x4*>(lds);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nT = a.N / kTileN, nC = a.K / kChunkK;
+  const int M = a.M;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  if (wave >= NWC) {
+    // ---- loader waves
+    const int lw = wave - NWC;
+    const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
+    auto issue = [&](int s) {
+      u32x4* slot = xs + (s % RB) * SLOT;
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) {
+        const int m = lw + i * NWL;
+        const int v = lane ^ (m & 15);
+        const int col = min(s * SK + 8 * v, a.K - 8);
+        const uint16_t* src = xg + (long)min(m, M - 1) * a.ldx + col;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)src,
+            (__attribute__((address_space(3))) void*)(slot + m * 64), 16, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < NB; ++s) issue(s);
+    wait_vm<(NB - 1) * RPL>();
+    wg_barrier();
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      // after barrier j every compute wave is done with slice j-1
+      if (j >= 1 && j - 1 + RB < NS) issue(j - 1 + RB);
+      if (j + 1 < NS) {
+        // slices issued after slice j+1 may stay in flight
+        const int last = min(j >= 1 ? j - 1 + RB : RB - 1, NS - 1);
+        wait_slices<RPL, RB - 2>(last - (j + 1));
+      }
+      wg_barrier();
+    }
+  } else {
+    // ---- compute waves
+    const int slot_i = wave / KP, kp = wave - slot_i * KP;
+    const int r = lane & 15, kg = lane >> 4;
+    const int tile = blockIdx.x + slot_i * gridDim.x;
+    const bool active = tile < nT;
+    const int t = active ? tile : nT - 1;
+    const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
+    const uint32_t* cbase = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
+    const ST* sbase = sbp + ((long)t * nC * kTileN + r) * 4;
+    uint32_t W[DR][BITS];
+    SBPair<ST> SBv[DR];
+    auto load = [&](int s, int d) {
+      const int c = min(s * KP + kp, nC - 1);
+      const uint32_t* p = cbase + (long)c * 64 * BITS;
+#pragma unroll
+      for (int q = 0; q < BITS; ++q) W[d][q] = __builtin_nontemporal_load(p + q);
+      SBv[d].load(sbase + (long)c * kTileN * 4);
+    };
+#pragma unroll
+    for (int d = 0; d < DR; ++d)
+      if (d < NS) load(d, d);
+    const uint32_t mask_v = pair_mask_vgpr<BITS>();
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = zero;
+    wg_barrier();
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int d = j % DR;
+      const bool live = j * KP + kp < nC;
+      const u32x4* slot = xs + (j % RB) * SLOT;
+      uint32_t P[16];
+      unpack_pairs<BITS>(W[d], P, mask_v);
+      float sc[2], bp[2];
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const float s0 = SBv[d].s(gp);
+        sc[gp] = live ? s0 : 0.f;
+        bp[gp] = live ? SBv[d].b(gp) - 128.f * s0 : 0.f;
+      }
+      // every activation read of the slice is issued before its first MFMA
+      constexpr int MA = MT <= 2 ? MT : 1;  // m-tiles whose fragments are read together
+#pragma unroll
+      for (int m0 = 0; m0 < MT; m0 += MA) {
+        u32x4 A[MA][4];
+#pragma unroll
+        for (int mi = 0; mi < MA; ++mi) {
+          const u32x4* xrow = slot + (16 * (m0 + mi) + r) * 64;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)  // vector of (chunk kp, group q>>1, quarter kg, half q&1)
+            A[mi][q] = xrow[(16 * kp + 8 * (q >> 1) + 2 * kg + (q & 1)) ^ r];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mi = 0; mi < MA; ++mi) {
+          const int mt = m0 + mi;
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, A[mi][2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0,
+                0, 0);
+            const f32x4 ex = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, A[mi][2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e, 0,
+                0, 0);
+            const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
+            const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
+            f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, A[mi][2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0,
+                0);
+            dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[mi][2 * gp + 1]),
+                                                         __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              acc[mt][q] = fmaf(sc[gp], dd[q], fmaf(bp[gp], ex[q], acc[mt][q]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (j + DR < NS) load(j + DR, d);
+      wait_lds();
+      wg_barrier();
+    }
+    // fold the KP partial tiles of this tile slot in K order (slots are dead)
+    f32x4* red = reinterpret_cast<f32x4*>(lds);  // [TM][MT][KP][64]
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[((slot_i * MT + mt) * KP + kp) * 64 + lane] = acc[mt];
+    __syncthreads();
+    if (kp != 0 || !active) return;
+    const int n = tile * kTileN + r;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 v = acc[mt];
+#pragma unroll
+      for (int i = 1; i < KP; ++i) v += red[((slot_i * MT + mt) * KP + i) * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = 16 * mt + 4 * kg + q;
+        if (m < M) store_y<false>(a.y, (long)m * a.ldy + n, v[q]);
+      }
+    }
+    return;
+  }
+  __syncthreads();  // loader waves: partner of the compute waves' fold barrier
+}
+
+// ---------------------------------------------------------------------------
 // Vector-ALU kernel: up to MR activation rows per pass, activations of the
 // workgroup's K split staged in LDS together with per-(row, group, quarter)
 // sums.  Each of the 4 wavefronts owns NTW tiles; lane (r, kg) accumulates
@@ -1378,6 +1577,45 @@ int resident_stage_vectors(int M, int K, int nw) {
   for (int xv : {2, 4, 8, 14})
     if (vecs <= (long)xv * nw * 64) return xv;
   return 0;
+}
+
+// (row tiles, slices of 512 k) shapes of the slab kernel; three tile slots.
+#define QMM_SLAB_SHAPES(X) X(2, 10) X(2, 16) X(4, 10) X(4, 16)
+
+int slab_slices(int mt, int nC) {
+  const int ns = (nC + 3) / 4;
+#define QMM_HAS(MTV, NSV) if (mt == MTV && ns == NSV) return ns;
+  QMM_SLAB_SHAPES(QMM_HAS)
+#undef QMM_HAS
+  return 0;
+}
+
+size_t slab_lds_bytes(int mt) { return (size_t)(mt == 4 ? 2 : 4) * 16 * mt * 1024; }
+
+template <int BITS, typename ST>
+static hipError_t slab_dispatch(int mt, int ns, const LaunchArgs& a, int grid, size_t lds,
+                                hipStream_t st) {
+#define QMM_SLAB(MTV, NSV)                                                                    \
+  if (mt == MTV && ns == NSV) {                                                               \
+    auto* kfn = &slab_kernel<BITS, MTV, kSlabTiles, NSV, (MTV == 4 ? 2 : 4), 4, ST>;          \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                    \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (e != hipSuccess) return e;                                                            \
+    kfn<<<grid, (kSlabTiles * 4 + 4) * 64, lds, st>>>(a);                                     \
+    return hipGetLastError();                                                                 \
+  }
+  QMM_SLAB_SHAPES(QMM_SLAB)
+#undef QMM_SLAB
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_slab(int bits, bool sb_f32, int mt, int ns, const LaunchArgs& a, int grid,
+                       size_t lds_bytes, hipStream_t st) {
+  if (bits == 3)
+    return sb_f32 ? slab_dispatch<3, float>(mt, ns, a, grid, lds_bytes, st)
+                  : slab_dispatch<3, uint16_t>(mt, ns, a, grid, lds_bytes, st);
+  return sb_f32 ? slab_dispatch<4, float>(mt, ns, a, grid, lds_bytes, st)
+                : slab_dispatch<4, uint16_t>(mt, ns, a, grid, lds_bytes, st);
 }
 
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {

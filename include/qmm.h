@@ -68,10 +68,14 @@ typedef enum {
   QMM_VARIANT_PERSIST = 4, /* matrix-core kernel, 1..64 rows per pass: one workgroup per compute
                               unit owning several 16-row tiles of W, activations streamed through
                               LDS by dedicated loader waves; bf16 activations */
-  QMM_VARIANT_RESIDENT = 5 /* matrix-core kernel for 1..16 rows whose activation block fits in
-                              one compute unit's LDS (rows*K*2 <= 160 KB): one workgroup per
-                              compute unit, activations staged once, its waves split the K of
-                              up to four 16-row tiles of W; bf16 activations */
+  QMM_VARIANT_RESIDENT = 5, /* matrix-core kernel for 1..16 rows whose activation block fits in
+                               one compute unit's LDS (rows*K*2 <= 160 KB): one workgroup per
+                               compute unit, activations staged once, its waves split the K of
+                               up to four 16-row tiles of W; bf16 activations */
+  QMM_VARIANT_SLAB = 6      /* matrix-core kernel for 17..64 rows per pass: one workgroup per
+                               compute unit owning three 16-row tiles of W, activations streamed
+                               through an LDS ring in slices of 512 columns by loader waves;
+                               built for K = 5120 and 8192; bf16 activations */
 } qmm_variant;
 
 /* Shape and format of one projection.  bits: 3 or 4 (other MLX widths are
@@ -93,7 +97,7 @@ typedef struct {
 typedef struct qmm_plan qmm_plan;
 
 typedef struct {
-  uint64_t launches[6];   /* indexed by qmm_variant: kernels run per family */
+  uint64_t launches[7];   /* indexed by qmm_variant: kernels run per family */
   int32_t last_variant;   /* family of the last qmm_run */
   int32_t last_ntw;       /* output tiles (16 rows of W each) per wavefront */
   int32_t last_splitk;    /* K splits folded through the workspace */

@@ -207,7 +207,7 @@ def test_workload1_full(variant):
 def test_workload2_full(rows):
     (p,) = synth.workload(2)
     r = Runner(p, max_rows=64)
-    variants = ["auto", "mfma", "persist", "resident"] + (["gemv"] if rows <= 9 else []) + (
+    variants = ["auto", "mfma", "persist", "resident", "slab"] + (["gemv"] if rows <= 9 else []) + (
         ["stream"] if stream_ok(p.K, rows) else [])
     for v in variants:
         say("workload 2 rows", rows, v)
@@ -225,6 +225,36 @@ def test_workload3_full():
         del r
 
 
+SLAB = [
+    # bits, K, N, M, sb_dtype: ragged tile slots (N/16 not a multiple of 3), both row-tile
+    # widths, two row blocks, f32 scales
+    (3, 5120, 208, 17, "bf16"),
+    (4, 5120, 208, 32, "bf16"),
+    (3, 5120, 176, 33, "bf16"),
+    (4, 5120, 48, 64, "f32"),
+    (3, 5120, 80, 100, "bf16"),
+    (4, 8192, 112, 40, "bf16"),
+    (3, 8192, 64, 9, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SLAB, ids=lambda c: "b%d_K%d_N%d_M%d_%s" % c)
+def test_slab_parity(case):
+    bits, K, N, M, sd = case
+    p = synth.small(300 + M, bits=bits, K=K, N=N, M=M, sb_dtype=sd)
+    r = Runner(p)
+    say("slab", case)
+    check_against_oracle(p, r.run(variant="slab"), label="slab %s" % (case,))
+
+
+def test_slab_rejects_unbuilt_k():
+    p = synth.small(14, bits=4, K=1024, N=32, M=20)
+    r = Runner(p)
+    with pytest.raises(b.QmmError) as ei:
+        r.run(variant="slab")
+    assert ei.value.status == b.QMM_ERR_UNSUPPORTED
+
+
 def test_persist_multiple_passes_and_partial_rounds():
     """More tiles than workgroups (tile passes) and a K that is not a whole
     number of rounds."""
@@ -235,7 +265,7 @@ def test_persist_multiple_passes_and_partial_rounds():
         check_against_oracle(p, r.run(variant="persist", ntw=tm), label="persist tm=%d" % tm)
 
 
-@pytest.mark.parametrize("variant", ["auto", "persist"])
+@pytest.mark.parametrize("variant", ["auto", "persist", "slab"])
 def test_workload4_sampled(variant):
     (p,) = synth.workload(4)
     say("workload 4", variant)
