@@ -77,7 +77,7 @@ def measured_traffic(rows: int):
     if rec.get("kernel_source_sha256_16") != h:
         return None
     for k in rec["kernels"].values():
-        if str(k["rows"]) == str(rows):
+        if rows in k["rows"]:
             return int(k["hbm_bytes"])
     return None
 
