@@ -123,7 +123,8 @@ bool resident_fits(const qmm_plan* p, int rows) {
 }
 
 bool slab_fits(const qmm_plan* p) {
-  return qmm::slab_slices(2, p->nC) > 0 && qmm::slab_slices(4, p->nC) > 0;
+  return qmm::slab_slices(1, p->nC) > 0 && qmm::slab_slices(2, p->nC) > 0 &&
+         qmm::slab_slices(4, p->nC) > 0;
 }
 
 int pick_variant(const qmm_plan* p, int rows, int forced) {
@@ -131,16 +132,16 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (forced) return forced;
   if (p->force_variant) return p->force_variant;
   // Measured on the 3-bit 5120->10240 sweep: the streaming kernel while the
-  // activation block fits its LDS budget, the resident kernel while each
-  // thread stages at most eight activation vectors (beyond that it spills),
-  // the slab kernel for longer blocks where it is built for this K.
+  // activation block fits its LDS budget, then the slab kernel where it is
+  // built for this K; elsewhere the resident kernel while each thread stages
+  // at most eight activation vectors (beyond that it spills), else MFMA.
   int nw, cpw;
   if (rows <= 16 && stream_shape(p, &nw, &cpw) && qmm::stream_fits(nw, rows, (int)p->d.K))
     return QMM_VARIANT_STREAM;
+  if (slab_fits(p)) return QMM_VARIANT_SLAB;
   if (rows <= 16 && resident_fits(p, rows) &&
       qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(1)) <= 8)
     return QMM_VARIANT_RESIDENT;
-  if (slab_fits(p)) return QMM_VARIANT_SLAB;
   return QMM_VARIANT_MFMA;
 }
 
@@ -190,7 +191,7 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
   if (variant == QMM_VARIANT_SLAB) {
     c.rows_per_launch = qmm::kMaxMfmaRows;
     const int r = std::min(rows, qmm::kMaxMfmaRows);
-    c.tile_rows = r <= 32 ? 2 : 4;
+    c.tile_rows = r <= 16 ? 1 : (r <= 32 ? 2 : 4);
     c.cpw = qmm::slab_slices(c.tile_rows, nC);
     c.ntw = qmm::kSlabTiles;
     c.wk = 4;

@@ -1030,7 +1030,7 @@ __global__ void __launch_bounds__((TM * 4 + 4) * 64) slab_kernel(LaunchArgs a) {
 
   if (wave >= NWC) {
     // ---- loader waves
-    const int lw = wave - NWC;
+    const int lw = __builtin_amdgcn_readfirstlane(wave - NWC);  // wave-uniform
     const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
     auto issue = [&](int s) {
       u32x4* slot = xs + (s % RB) * SLOT;
@@ -1062,7 +1062,8 @@ __global__ void __launch_bounds__((TM * 4 + 4) * 64) slab_kernel(LaunchArgs a) {
     }
   } else {
     // ---- compute waves
-    const int slot_i = wave / KP, kp = wave - slot_i * KP;
+    const int slot_i = __builtin_amdgcn_readfirstlane(wave / KP);  // wave-uniform
+    const int kp = __builtin_amdgcn_readfirstlane(wave - slot_i * KP);
     const int r = lane & 15, kg = lane >> 4;
     const int tile = blockIdx.x + slot_i * gridDim.x;
     const bool active = tile < nT;
@@ -1103,7 +1104,7 @@ __global__ void __launch_bounds__((TM * 4 + 4) * 64) slab_kernel(LaunchArgs a) {
         bp[gp] = live ? SBv[d].b(gp) - 128.f * s0 : 0.f;
       }
       // every activation read of the slice is issued before its first MFMA
-      constexpr int MA = MT <= 2 ? MT : 1;  // m-tiles whose fragments are read together
+      constexpr int MA = MT <= 2 ? MT : 2;  // m-tiles whose fragments are read together
 #pragma unroll
       for (int m0 = 0; m0 < MT; m0 += MA) {
         u32x4 A[MA][4];
@@ -1580,7 +1581,7 @@ int resident_stage_vectors(int M, int K, int nw) {
 }
 
 // (row tiles, slices of 512 k) shapes of the slab kernel; three tile slots.
-#define QMM_SLAB_SHAPES(X) X(2, 10) X(2, 16) X(4, 10) X(4, 16)
+#define QMM_SLAB_SHAPES(X) X(1, 10) X(1, 16) X(2, 10) X(2, 16) X(4, 10) X(4, 16)
 
 int slab_slices(int mt, int nC) {
   const int ns = (nC + 3) / 4;
@@ -1590,14 +1591,16 @@ int slab_slices(int mt, int nC) {
   return 0;
 }
 
-size_t slab_lds_bytes(int mt) { return (size_t)(mt == 4 ? 2 : 4) * 16 * mt * 1024; }
+// LDS ring slots per row-tile count: 128 KB of activations in every case.
+static constexpr int slab_ring(int mt) { return mt == 4 ? 2 : (mt == 2 ? 4 : 8); }
+size_t slab_lds_bytes(int mt) { return (size_t)slab_ring(mt) * 16 * mt * 1024; }
 
 template <int BITS, typename ST>
 static hipError_t slab_dispatch(int mt, int ns, const LaunchArgs& a, int grid, size_t lds,
                                 hipStream_t st) {
 #define QMM_SLAB(MTV, NSV)                                                                    \
   if (mt == MTV && ns == NSV) {                                                               \
-    auto* kfn = &slab_kernel<BITS, MTV, kSlabTiles, NSV, (MTV == 4 ? 2 : 4), 4, ST>;          \
+    auto* kfn = &slab_kernel<BITS, MTV, kSlabTiles, NSV, slab_ring(MTV), MTV == 4 ? 3 : 4, ST>; \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                    \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                            \
