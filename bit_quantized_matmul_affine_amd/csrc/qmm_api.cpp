@@ -46,8 +46,8 @@ struct Cfg {
   int wk;         // wavefronts of a workgroup that split K (MFMA)
   int S;          // K splits across workgroups
   int nTB;        // tile blocks
-  size_t lds;     // dynamic LDS bytes (GEMV, STREAM, PERSIST)
-  int grid;       // PERSIST, RESIDENT: workgroups
+  size_t lds;     // dynamic LDS bytes (GEMV, STREAM, RESIDENT, SLAB)
+  int grid;       // RESIDENT, SLAB: workgroups
   int cpw;        // RESIDENT: chunks of K per wave
 };
 
@@ -58,7 +58,7 @@ struct qmm_plan {
   int nT, nC;
   int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
   int env_ntw, env_splitk, env_kwaves;
-  mutable std::atomic<uint64_t> launches[7];
+  mutable std::atomic<uint64_t> launches[6];
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
 };
 
@@ -153,22 +153,6 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
   const int nT = p->nT, nC = p->nC;
   auto pow2_floor = [](int v) { return v >= 4 ? 4 : (v >= 2 ? 2 : 1); };
   int tiles_per_block;
-  if (variant == QMM_VARIANT_PERSIST) {
-    c.rows_per_launch = qmm::kMaxMfmaRows;
-    const int r = std::min(rows, qmm::kMaxMfmaRows);
-    c.tile_rows = round_up_pow2((r + 15) / 16, 4);
-    const int rc = c.tile_rows == 1 ? 8 : 4;
-    c.wk = (c.tile_rows == 1 && wk_req == 8) ? 8 : 4;  // compute waves
-    c.grid = std::min(device_cus(), nT);
-    const int tm_cap = c.tile_rows == 1 ? 4 : 3;
-    int tm = (nT + c.grid - 1) / c.grid;
-    if (ntw_req) tm = ntw_req;
-    c.ntw = std::max(1, std::min(tm, tm_cap));
-    c.nTB = c.grid;
-    c.S = 1;
-    c.lds = qmm::persist_lds_bytes(c.tile_rows, rc);
-    return c;
-  }
   if (variant == QMM_VARIANT_RESIDENT) {
     // as few tile slots as fill every compute unit once; fewer where no
     // built shape covers this K with that many slots
@@ -306,7 +290,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_SLAB)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
   if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM ||
-       variant_req == QMM_VARIANT_PERSIST || variant_req == QMM_VARIANT_RESIDENT ||
+       variant_req == QMM_VARIANT_RESIDENT ||
        variant_req == QMM_VARIANT_SLAB) &&
       p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
@@ -367,8 +351,6 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
       e = qmm::launch_resident(p->d.bits, sf, cb.ntw, cb.cpw,
                                qmm::resident_stage_vectors(rb, (int)p->d.K, cb.wk), a, cb.grid,
                                cb.lds, st);
-    else if (variant == QMM_VARIANT_PERSIST)
-      e = qmm::launch_persist(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, cb.grid, cb.lds, st);
     else if (variant == QMM_VARIANT_STREAM)
       e = qmm::launch_stream(p->d.bits, sf, cb.wk, cb.ntw, a, cb.lds, st);
     else if (variant == QMM_VARIANT_MFMA)
@@ -380,8 +362,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     p->last_variant = variant;
     p->last_ntw = cb.ntw;
     p->last_splitk = cb.S;
-    p->last_grid = (variant == QMM_VARIANT_PERSIST || variant == QMM_VARIANT_RESIDENT ||
-                    variant == QMM_VARIANT_SLAB)
+    p->last_grid = (variant == QMM_VARIANT_RESIDENT || variant == QMM_VARIANT_SLAB)
                        ? cb.grid : cb.nTB * cb.S;
   }
   if (getenv("QMM_LOG"))
@@ -431,7 +412,6 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
     if (!strcmp(v, "gemv")) p->force_variant = QMM_VARIANT_GEMV;
     if (!strcmp(v, "mfma")) p->force_variant = QMM_VARIANT_MFMA;
     if (!strcmp(v, "stream")) p->force_variant = QMM_VARIANT_STREAM;
-    if (!strcmp(v, "persist")) p->force_variant = QMM_VARIANT_PERSIST;
     if (!strcmp(v, "resident")) p->force_variant = QMM_VARIANT_RESIDENT;
     if (!strcmp(v, "slab")) p->force_variant = QMM_VARIANT_SLAB;
   }
@@ -516,7 +496,7 @@ qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, 
 qmm_status qmm_get_stats(const qmm_plan* p, qmm_stats* out) {
   if (qmm_status st = check_plan(p)) return st;
   if (!out) return fail(QMM_ERR_INVALID_ARG, "out is NULL");
-  for (int i = 0; i < 7; ++i) out->launches[i] = p->launches[i].load();
+  for (int i = 0; i < 6; ++i) out->launches[i] = p->launches[i].load();
   out->last_variant = p->last_variant;
   out->last_ntw = p->last_ntw;
   out->last_splitk = p->last_splitk;

@@ -43,9 +43,6 @@ hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArg
                          size_t lds_bytes, hipStream_t st);
 size_t stream_lds_bytes(int nw, int M, int K);
 bool stream_fits(int nw, int M, int K);
-hipError_t launch_persist(int bits, bool sb_f32, int mt, int tm, int nwc, const LaunchArgs& a,
-                          int grid, size_t lds_bytes, hipStream_t st);
-size_t persist_lds_bytes(int mt, int rc);
 hipError_t launch_resident(int bits, bool sb_f32, int tm, int cpw, int xv, const LaunchArgs& a,
                            int grid, size_t lds_bytes, hipStream_t st);
 // Chunks per wave of the resident kernel built for `tm` tile slots that

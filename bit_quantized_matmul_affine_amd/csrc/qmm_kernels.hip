@@ -19,11 +19,11 @@
 //     affine-split-mma.ts fold ("columns below M only").
 //
 // What is ours (gfx950, not the pages' Metal design):
-//   * Codes become bf16 values 128+q with one and-or per PAIR of codes:
-//     (w >> shift) & mask | 0x43004300 (bf16 0x4300 is 128.0 and q < 128 fits
-//     in the 7 mantissa bits exactly).  The 128 offset is removed per group
-//     through the factored form: for one group,
-//         sum_k (s*q_k + b) x_k = s * sum_k (128+q_k) x_k + (b - 128 s) * sum_k x_k.
+//   * Codes become bf16 values 128+q (or 128+8q) with one and-or per PAIR of
+//     codes: (w >> shift) & mask | 0x43004300 (bf16 0x4300 is 128.0 and the
+//     code fits the 7 mantissa bits exactly).  The offset is removed per group
+//     through the factored form: for one group with values v_k = 128 + f q_k,
+//         sum_k (s*q_k + b) x_k = (s/f) sum_k v_k x_k + (b - (128/f) s) sum_k x_k.
 //   * A one-time repack ("native layout") makes every wavefront load 768 or
 //     1024 contiguous bytes per instruction and hands each lane exactly the
 //     codes its MFMA operand needs.  Byte count is unchanged.
@@ -60,63 +60,104 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 // and (g', 2u+1) in the high 16 bits after the unpack:
 //   4-bit: pair p = 4j + t sits in word j, low code at bits [4t, 4t+4),
 //          high code at bits [16+4t, 16+4t+4).
-//   3-bit: pair p = 5j + t (p < 15) sits in word j, low code at bits
-//          [3t, 3t+3), high code at bits [16+3t, 16+3t+3); pair 15 keeps bit
-//          b of its low code in bit 15 of word b and bit b of its high code in
-//          bit 31 of word b (b = 0,1,2).
+//   3-bit: each word holds five fields f = 0..4 (low code at bits
+//          [3f, 3f+3), high code at [16+3f, 16+3f+3)) and one bit at 15 / 31.
+//          Pairs 0..7 (group 0) are f0, f2, f4 of word 0, f0, f2, f4 of
+//          word 1, f0, f2 of word 2; pairs 8..14 (group 1) are f1, f3 of
+//          words 0, 1, 2 and f4 of word 2; pair 15 keeps bit b of its low
+//          code in bit 15 of word b and bit b of its high code in bit 31.
 // Scales/biases: block b holds 16 rows x {s_g0, s_g1, b_g0, b_g1}.
 // ---------------------------------------------------------------------------
 
-// v_and_or_b32 with the mask in a VGPR and the or-value in an SGPR.  gfx9
-// VOP3 instructions take no literal and read at most one scalar, so the
-// compiler splits (x & m) | c with two constants into two instructions; this
-// keeps it to one.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_v, uint32_t or_s) {
+// v_and_or_b32 with the mask in an SGPR and the or-value 0x43004300 in a
+// VGPR.  gfx9 VOP3 instructions take no literal and read at most one scalar,
+// so the compiler splits (x & m) | c with two constants into two
+// instructions; this keeps it to one, and the three masks of the 3-bit layout
+// cost scalar registers only.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_s, uint32_t or_v) {
   uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(mask_v), "s"(or_s));
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask_s), "v"(or_v));
   return r;
 }
 
+// The or-value of unpack_pairs, held in a VGPR.
+struct PairMasks {
+  uint32_t orv;
+};
 template <int BITS>
-__device__ __forceinline__ uint32_t pair_mask_vgpr() {
-  uint32_t m;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(m) : "i"(BITS == 4 ? 0x000F000F : 0x00070007));
-  return m;
+__device__ __forceinline__ PairMasks pair_mask_vgpr() {
+  PairMasks k;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(k.orv) : "s"(0x43004300u));
+  return k;
 }
 
-// 16 pairs of bf16 values 128+q from one lane's BITS words.  mask_v must hold
-// pair_mask_vgpr<BITS>().
+// 16 pairs of bf16 values from one lane's BITS words; pair p = 8g' + u holds
+// codes (g', 2u) in its low half and (g', 2u+1) in its high half.
+//   4-bit: pair p = 4j + t is field t (bits 4t / 16+4t) of word j; value 128+q.
+//   3-bit: a word holds five fields f = 0..4 at bits 3f / 16+3f, plus bit 15 /
+//   bit 31.  Group 0 (pairs 0..7) uses fields placed at mantissa bits 0..2
+//   (value 128+q): f0 and f2 of every word and f4 of words 0 and 1.  Group 1
+//   (pairs 8..15) uses fields placed at mantissa bits 3..5 (value 128+8q):
+//   f1 and f3 of every word, f4 of word 2, and the pair whose code bit b sits
+//   in bit 15 / bit 31 of word b.  Fields f0/f1 need no shift and f2/f3 share
+//   one, so 32 codes cost 6 shifts, 15 and-ors and 7 instructions for the
+//   split pair.  group_affine() folds the factor 8 into the group's scale.
 template <int BITS>
-__device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* P, uint32_t mask_v) {
+__device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* P, const PairMasks& k) {
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) P[4 * j + t] = and_or(w[j] >> (4 * t), mask_v, 0x43004300u);
+      for (int t = 0; t < 4; ++t) P[4 * j + t] = and_or(w[j] >> (4 * t), 0x000F000Fu, k.orv);
   } else {
+    constexpr uint32_t m0 = 0x00070007u, m3 = 0x00380038u;
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-#pragma unroll
-      for (int t = 0; t < 5; ++t) P[5 * j + t] = and_or(w[j] >> (3 * t), mask_v, 0x43004300u);
-    // pair 15: bit b of each code sits in bit 15 / bit 31 of word b
-    const uint32_t b01 = ((w[0] >> 15) & 0x00010001u) | ((w[1] >> 14) & 0xFFFEFFFEu);
-    const uint32_t b012 = (b01 & 0x00030003u) | ((w[2] >> 13) & 0xFFFCFFFCu);
-    P[15] = and_or(b012, mask_v, 0x43004300u);
+    for (int j = 0; j < 3; ++j) {
+      const uint32_t w6 = w[j] >> 6;
+      P[j < 2 ? 3 * j : 6] = and_or(w[j], m0, k.orv);      // f0 -> group 0
+      P[j < 2 ? 3 * j + 1 : 7] = and_or(w6, m0, k.orv);    // f2 -> group 0
+      P[8 + 2 * j] = and_or(w[j], m3, k.orv);              // f1 -> group 1
+      P[9 + 2 * j] = and_or(w6, m3, k.orv);                // f3 -> group 1
+      if (j < 2)
+        P[3 * j + 2] = and_or(w[j] >> 12, m0, k.orv);      // f4 -> group 0
+      else
+        P[14] = and_or(w[j] >> 9, m3, k.orv);              // f4 -> group 1
+    }
+    // pair 15 (group 1): bit b of each code sits in bit 15 / bit 31 of word b
+    const uint32_t b0 = (w[0] >> 12) & 0x00080008u;
+    const uint32_t b1 = (w[1] >> 11) & 0x00100010u;
+    const uint32_t b2 = and_or(w[2] >> 10, 0x00200020u, k.orv);
+    P[15] = b0 | b1 | b2;
   }
+}
+
+// Per-group factors for the values unpack_pairs produces: with v = 128 + f*q
+// (f = 1, or 8 for group 1 of the 3-bit layout),
+//   sum_k (s*q_k + b) x_k = (s/f) * sum_k v_k x_k + (b - (128/f) s) * sum_k x_k.
+struct Affine {
+  float sc, bp;
+};
+template <int BITS>
+__device__ __forceinline__ Affine group_affine(int gp, float s, float b) {
+  const bool c3 = BITS == 3 && gp == 1;
+  return Affine{c3 ? s * 0.125f : s, b - (c3 ? 16.f : 128.f) * s};
 }
 
 // Inverse of unpack_pairs for one code: OR code q of (g', i) into w.
 template <int BITS>
 __device__ __forceinline__ void place_code(uint32_t* w, int gp, int i, uint32_t q) {
-  const int p = 8 * gp + (i >> 1), half = i & 1;
+  const int p = 8 * gp + (i >> 1), half = 16 * (i & 1);
   if constexpr (BITS == 4) {
-    w[p >> 2] |= q << (16 * half + 4 * (p & 3));
+    w[p >> 2] |= q << (half + 4 * (p & 3));
   } else {
+    // (word, field) of pair p, see unpack_pairs
+    static constexpr int8_t kWord[15] = {0, 0, 0, 1, 1, 1, 2, 2, 0, 0, 1, 1, 2, 2, 2};
+    static constexpr int8_t kField[15] = {0, 2, 4, 0, 2, 4, 0, 2, 1, 3, 1, 3, 1, 3, 4};
     if (p < 15) {
-      w[p / 5] |= q << (16 * half + 3 * (p % 5));
+      w[kWord[p]] |= q << (half + 3 * kField[p]);
     } else {
 #pragma unroll
-      for (int b = 0; b < 3; ++b) w[b] |= ((q >> b) & 1u) << (half ? 31 : 15);
+      for (int b = 0; b < 3; ++b) w[b] |= ((q >> b) & 1u) << (half + 15);
     }
   }
 }
@@ -204,8 +245,9 @@ __global__ void __launch_bounds__(256) debug_unpack_kernel(const uint32_t* __res
   for (int p = 0; p < 16; ++p) {
     const int gp = p >> 3, u = p & 7;
     const long k = (long)kChunkK * c + 64 * gp + 16 * kg + 2 * u;
-    out[(long)n * K + k] = (uint8_t)((P[p] & 0xFFFFu) - 0x4300u);
-    out[(long)n * K + k + 1] = (uint8_t)((P[p] >> 16) - 0x4300u);
+    const int sh = (BITS == 3 && gp == 1) ? 3 : 0;  // group 1 of the 3-bit layout holds 8q
+    out[(long)n * K + k] = (uint8_t)(((P[p] & 0xFFFFu) - 0x4300u) >> sh);
+    out[(long)n * K + k + 1] = (uint8_t)(((P[p] >> 16) - 0x4300u) >> sh);
   }
 }
 
@@ -334,7 +376,7 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
       const int m = min(16 * mt + r, a.M - 1);
       xrow[mt] = x + (long)m * a.ldx + 16 * kg;
     }
-    const uint32_t mask_v = pair_mask_vgpr<BITS>();
+    const PairMasks mask_v = pair_mask_vgpr<BITS>();
     const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 pairs
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
@@ -378,8 +420,8 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
         unpack_pairs<BITS>(W[d][nt], P, mask_v);
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          const float sc = SBv[d][nt].s(gp);
-          const float bp = SBv[d][nt].b(gp) - 128.f * sc;
+          const Affine af = group_affine<BITS>(gp, SBv[d][nt].s(gp), SBv[d][nt].b(gp));
+          const float sc = af.sc, bp = af.bp;
           const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
           const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
 #pragma unroll
@@ -538,7 +580,7 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   // 4. compute in load order; rows past the last one read the last row
   //    (never stored)
   const uint16_t* xrow = xs + (long)min(r, a.M - 1) * a.K + 16 * kg;
-  const uint32_t mask_v = pair_mask_vgpr<BITS>();
+  const PairMasks mask_v = pair_mask_vgpr<BITS>();
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc = zero;
@@ -564,8 +606,8 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
           __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
       dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
                                                    __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
-      const float sc = SBv[j].s(gp);
-      const float bp = SBv[j].b(gp) - 128.f * sc;
+      const Affine af = group_affine<BITS>(gp, SBv[j].s(gp), SBv[j].b(gp));
+      const float sc = af.sc, bp = af.bp;
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
         const float v = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[q]));
@@ -597,248 +639,6 @@ bool stream_fits(int nw, int M, int K) {
          stream_lds_bytes(nw, M, K) <= 64 * 1024;
 }
 
-// ---------------------------------------------------------------------------
-// Persistent MFMA kernel for longer activation blocks.  One workgroup per
-// compute unit; workgroup g owns tiles g, g+G, g+2G, ... (at most TM at a
-// time; more are taken in passes).  K is walked in rounds of RC chunks:
-//   * NWL loader waves copy the next round's activation slice (16*MT rows x
-//     RC*128 columns) into registers, form the per-(row, group) sums with
-//     8-lane shuffles, and write both to the idle one of two LDS buffers; the
-//     copy is issued and retired within one round, so its registers are
-//     never live across a barrier;
-//   * NWC compute waves: wave w takes chunks j*RC + w + NWC*i (i < RC/NWC) of
-//     every owned tile; its weight loads run DR rounds ahead in a statically
-//     indexed ring;
-//   * loader and compute waves keep separate in-order load queues, so neither
-//     waits on the other's loads; one barrier per round; partial tiles are
-//     added across compute waves through LDS in wave order after a pass.
-// Rows >= M of a slice repeat row M-1 (their outputs are never stored).
-// ---------------------------------------------------------------------------
-template <int BITS, int MT, int RC, int NWC, int NWL, int TM, int DR, typename ST>
-__global__ void __launch_bounds__((NWC + NWL) * 64) persist_kernel(LaunchArgs a) {
-  constexpr int CPW = RC / NWC;           // chunks per compute wave per round
-  constexpr int XROW = RC * kChunkK + 8;  // padded LDS row, bf16 elements
-  constexpr int GR = 2 * RC;              // groups per round
-  constexpr int ROWS = 16 * MT;
-  constexpr int SV = ROWS * RC * 16;      // 16-byte vectors per slice
-  static_assert(SV % (NWL * 64) == 0, "slice must split evenly over loader lanes");
-  constexpr int LV = SV / (NWL * 64);     // vectors per loader lane
-  constexpr size_t XBUF = (size_t)ROWS * XROW;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  uint16_t* xbuf = reinterpret_cast<uint16_t*>(lds);                      // [2][ROWS][XROW]
-  float* xsum = reinterpret_cast<float*>(lds + (size_t)2 * XBUF * 2);     // [2][GR][ROWS]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool loader = wave >= NWC;
-  const int lt = threadIdx.x - NWC * 64;  // loader thread index
-  const int w = wave;                     // compute wave index
-  const int r = lane & 15, kg = lane >> 4;
-  const int G = gridDim.x;
-  const int nT = a.N / kTileN, nC = a.K / kChunkK;
-  const int nR = (nC + RC - 1) / RC;
-  const int M = a.M;
-  const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
-  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-
-  // Loader: slice j -> LDS buffer b, with group sums.  Consecutive loader
-  // lanes hold consecutive 16-byte vectors of a row, so the 8 vectors of a
-  // group sit on 8 aligned lanes.
-  auto copy_slice = [&](int j, int b) {
-    u32x4 xv[LV];
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int idx = lt + i * NWL * 64;
-      const int row = idx / (RC * 16), v = idx - row * (RC * 16);
-      const int col = min(j * RC * kChunkK + 8 * v, a.K - 8);
-      xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)min(row, M - 1) * a.ldx + col);
-    }
-    uint16_t* dst = xbuf + (size_t)b * XBUF;
-    float* sdst = xsum + (size_t)b * GR * ROWS;
-#pragma unroll
-    for (int i = 0; i < LV; ++i) {
-      const int idx = lt + i * NWL * 64;
-      const int row = idx / (RC * 16), v = idx - row * (RC * 16);
-      *reinterpret_cast<u32x4*>(dst + (size_t)row * XROW + 8 * v) = xv[i];
-      float sm = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sm += __uint_as_float(xv[i][e] << 16);
-        sm += __uint_as_float(xv[i][e] & 0xFFFF0000u);
-      }
-      sm += __shfl_xor(sm, 1);
-      sm += __shfl_xor(sm, 2);
-      sm += __shfl_xor(sm, 4);
-      if ((lane & 7) == 0) sdst[(v >> 3) * ROWS + row] = sm;
-    }
-  };
-
-  // Compute waves: weight ring of DR rounds.
-  uint32_t W[DR][CPW][TM][BITS];
-  SBPair<ST> SBv[DR][CPW][TM];
-  f32x4 acc[TM][MT];
-  const uint32_t mask_v = pair_mask_vgpr<BITS>();
-
-  for (int pass_t0 = blockIdx.x; pass_t0 < nT; pass_t0 += G * TM) {
-    int tiles[TM];
-    int ntl = 0;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int t = pass_t0 + i * G;
-      tiles[i] = t < nT ? t : nT - 1;
-      ntl += t < nT ? 1 : 0;
-    }
-    auto load_round = [&](int j, int d) {
-#pragma unroll
-      for (int u = 0; u < CPW; ++u) {
-        const int c = min(j * RC + w + NWC * u, nC - 1);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const uint32_t* p = a.codes + (((long)tiles[i] * nC + c) * 64 + lane) * BITS;
-#pragma unroll
-          for (int q = 0; q < BITS; ++q) W[d][u][i][q] = __builtin_nontemporal_load(p + q);
-          SBv[d][u][i].load(sbp + (((long)tiles[i] * nC + c) * kTileN + r) * 4);
-        }
-      }
-    };
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[i][mt] = zero;
-
-    if (loader) {
-      copy_slice(0, 0);
-    } else {
-#pragma unroll
-      for (int d = 0; d < DR; ++d)
-        if (d < nR) load_round(d, d);
-    }
-    __syncthreads();
-
-    for (int j0 = 0; j0 < nR; j0 += DR) {
-#pragma unroll
-      for (int d = 0; d < DR; ++d) {
-        const int j = j0 + d;
-        if (j < nR) {
-          const int b = j & 1;
-          if (loader) {
-            if (j + 1 < nR) copy_slice(j + 1, b ^ 1);
-          } else {
-            const float* sb_ = xsum + (size_t)b * GR * ROWS;
-#pragma unroll
-            for (int u = 0; u < CPW; ++u) {
-              const int cl = w + NWC * u;  // chunk within the round
-              if (j * RC + cl < nC) {
-                const uint16_t* xb = xbuf + (size_t)b * XBUF + 128 * cl + 16 * kg;
-                if constexpr (MT == 1) {
-                  u32x4 A[4];
-#pragma unroll
-                  for (int t = 0; t < 4; ++t)
-                    A[t] = *reinterpret_cast<const u32x4*>(xb + (size_t)r * XROW + 64 * (t >> 1) +
-                                                           8 * (t & 1));
-                  f32x4 ex[2];
-#pragma unroll
-                  for (int gp = 0; gp < 2; ++gp)
-                    ex[gp] = *reinterpret_cast<const f32x4*>(sb_ + (2 * cl + gp) * ROWS + 4 * kg);
-#pragma unroll
-                  for (int i = 0; i < TM; ++i) {
-                    if (i < ntl) {
-                      uint32_t P[16];
-                      unpack_pairs<BITS>(W[d][u][i], P, mask_v);
-#pragma unroll
-                      for (int gp = 0; gp < 2; ++gp) {
-                        const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
-                        const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
-                        f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0),
-                            zero, 0, 0, 0);
-                        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, A[2 * gp + 1]),
-                            __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
-                        const float sc = SBv[d][u][i].s(gp);
-                        const float bp = SBv[d][u][i].b(gp) - 128.f * sc;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                          acc[i][0][q] = fmaf(sc, dd[q], fmaf(bp, ex[gp][q], acc[i][0][q]));
-                      }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                  }
-                } else {
-                  uint32_t P[TM][16];
-#pragma unroll
-                  for (int i = 0; i < TM; ++i) unpack_pairs<BITS>(W[d][u][i], P[i], mask_v);
-#pragma unroll
-                  for (int mt = 0; mt < MT; ++mt) {
-                    u32x4 A[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                      A[t] = *reinterpret_cast<const u32x4*>(xb + (size_t)(16 * mt + r) * XROW +
-                                                             64 * (t >> 1) + 8 * (t & 1));
-#pragma unroll
-                    for (int gp = 0; gp < 2; ++gp) {
-                      const f32x4 ex = *reinterpret_cast<const f32x4*>(
-                          sb_ + (2 * cl + gp) * ROWS + 16 * mt + 4 * kg);
-#pragma unroll
-                      for (int i = 0; i < TM; ++i) {
-                        if (i < ntl) {
-                          const u32x4 B0 = {P[i][8 * gp + 0], P[i][8 * gp + 1], P[i][8 * gp + 2], P[i][8 * gp + 3]};
-                          const u32x4 B1 = {P[i][8 * gp + 4], P[i][8 * gp + 5], P[i][8 * gp + 6], P[i][8 * gp + 7]};
-                          f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                              __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0),
-                              zero, 0, 0, 0);
-                          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                              __builtin_bit_cast(bf16x8, A[2 * gp + 1]),
-                              __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
-                          const float sc = SBv[d][u][i].s(gp);
-                          const float bp = SBv[d][u][i].b(gp) - 128.f * sc;
-#pragma unroll
-                          for (int q = 0; q < 4; ++q)
-                            acc[i][mt][q] = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[i][mt][q]));
-                        }
-                      }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                  }
-                }
-              }
-            }
-            if (j + DR < nR) load_round(j + DR, d);
-          }
-          __syncthreads();
-        }
-      }
-    }
-
-    // Fold the NWC partial tiles (LDS reused: activations are dead now).
-    f32x4* red = reinterpret_cast<f32x4*>(lds);  // [TM][MT][NWC][64]
-    if (!loader) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) red[((i * MT + mt) * NWC + w) * 64 + lane] = acc[i][mt];
-    }
-    __syncthreads();
-    if (!loader) {
-      for (int job = w; job < TM * MT; job += NWC) {
-        const int i = job / MT, mt = job - i * MT;
-        if (i >= ntl) continue;
-        f32x4 s = red[((i * MT + mt) * NWC + 0) * 64 + lane];
-        for (int v = 1; v < NWC; ++v) s += red[((i * MT + mt) * NWC + v) * 64 + lane];
-        const int n = tiles[i] * kTileN + r;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int m = 16 * mt + 4 * kg + q;
-          if (m < M) store_y<false>(a.y, (long)m * a.ldy + n, s[q]);
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
-size_t persist_lds_bytes(int mt, int rc) {
-  return (size_t)2 * 16 * mt * (rc * kChunkK + 8) * 2 + (size_t)2 * 2 * rc * 16 * mt * 4;
-}
 
 // ---------------------------------------------------------------------------
 // Resident MFMA kernel for blocks of up to 16 activation rows whose whole
@@ -918,7 +718,7 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   const int xm = min(r, M - 1);
   const u32x4* xrow = xs + (long)xm * kv;
   const int sw = xm & 15;
-  const uint32_t mask_v = pair_mask_vgpr<BITS>();
+  const PairMasks mask_v = pair_mask_vgpr<BITS>();
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc = zero;
@@ -944,9 +744,9 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
           __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
       dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
                                                    __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
-      const float s0 = SBv[j].s(gp);
-      const float sc = live ? s0 : 0.f;
-      const float bp = live ? SBv[j].b(gp) - 128.f * s0 : 0.f;
+      const Affine af = group_affine<BITS>(gp, SBv[j].s(gp), SBv[j].b(gp));
+      const float sc = live ? af.sc : 0.f;
+      const float bp = live ? af.bp : 0.f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[q]));
     }
@@ -1083,7 +883,7 @@ __global__ void __launch_bounds__((TM * 4 + 4) * 64) slab_kernel(LaunchArgs a) {
 #pragma unroll
     for (int d = 0; d < DR; ++d)
       if (d < NS) load(d, d);
-    const uint32_t mask_v = pair_mask_vgpr<BITS>();
+    const PairMasks mask_v = pair_mask_vgpr<BITS>();
     const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
     f32x4 acc[MT];
 #pragma unroll
@@ -1099,9 +899,11 @@ __global__ void __launch_bounds__((TM * 4 + 4) * 64) slab_kernel(LaunchArgs a) {
       float sc[2], bp[2];
 #pragma unroll
       for (int gp = 0; gp < 2; ++gp) {
+        // group_affine() spelled out: this form keeps the kernel within 128 VGPRs
         const float s0 = SBv[d].s(gp);
-        sc[gp] = live ? s0 : 0.f;
-        bp[gp] = live ? SBv[d].b(gp) - 128.f * s0 : 0.f;
+        constexpr bool c3 = BITS == 3;
+        sc[gp] = live ? (c3 && gp == 1 ? s0 * 0.125f : s0) : 0.f;
+        bp[gp] = live ? SBv[d].b(gp) - (c3 && gp == 1 ? 16.f : 128.f) * s0 : 0.f;
       }
       // every activation read of the slice is issued before its first MFMA
       constexpr int MA = MT <= 2 ? MT : 2;  // m-tiles whose fragments are read together
@@ -1266,7 +1068,7 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_kernel(LaunchArgs a) {
     for (int m = 0; m < MR; ++m) acc[nt][m] = 0.f;
 
   if (active) {
-    const uint32_t mask_v = pair_mask_vgpr<BITS>();
+    const PairMasks mask_v = pair_mask_vgpr<BITS>();
     auto compute = [&](int j, int d) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
@@ -1275,8 +1077,8 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_kernel(LaunchArgs a) {
         unpack_pairs<BITS>(W[d][nt], P, mask_v);
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          const float sc = SBv[d][nt].s(gp);
-          const float bp = SBv[d][nt].b(gp) - 128.f * sc;
+          const Affine af = group_affine<BITS>(gp, SBv[d][nt].s(gp), SBv[d][nt].b(gp));
+          const float sc = af.sc, bp = af.bp;
           const int kl = kChunkK * j + 64 * gp + 16 * kg;  // lane's 16 columns
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
@@ -1493,32 +1295,6 @@ hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArg
                          size_t lds_bytes, hipStream_t st) {
   if (bits == 3) return sb_f32 ? stream_dispatch<3, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<3, uint16_t>(nw, cpw, a, lds_bytes, st);
   return sb_f32 ? stream_dispatch<4, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<4, uint16_t>(nw, cpw, a, lds_bytes, st);
-}
-
-template <int BITS, typename ST>
-static hipError_t persist_dispatch(int mt, int tm, int nwc, const LaunchArgs& a, int grid,
-                                   size_t lds, hipStream_t st) {
-#define QMM_PERSIST(MTV, RCV, NWCV, TMV, DRV)                                                    \
-  if (mt == MTV && tm == TMV && nwc == NWCV) {                                                   \
-    auto* kfn = &persist_kernel<BITS, MTV, RCV, NWCV, 4, TMV, DRV, ST>;                          \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                       \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);    \
-    if (e != hipSuccess) return e;                                                               \
-    kfn<<<grid, (NWCV + 4) * 64, lds, st>>>(a);                                                  \
-    return hipGetLastError();                                                                    \
-  }
-  QMM_PERSIST(1, 8, 4, 1, 2) QMM_PERSIST(1, 8, 4, 2, 2) QMM_PERSIST(1, 8, 4, 3, 2) QMM_PERSIST(1, 8, 4, 4, 2)
-  QMM_PERSIST(1, 8, 8, 1, 2) QMM_PERSIST(1, 8, 8, 2, 2)
-  QMM_PERSIST(2, 4, 4, 1, 2) QMM_PERSIST(2, 4, 4, 2, 2) QMM_PERSIST(2, 4, 4, 3, 2)
-  QMM_PERSIST(4, 4, 4, 1, 2) QMM_PERSIST(4, 4, 4, 2, 2) QMM_PERSIST(4, 4, 4, 3, 2)
-#undef QMM_PERSIST
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_persist(int bits, bool sb_f32, int mt, int tm, int nwc, const LaunchArgs& a,
-                          int grid, size_t lds_bytes, hipStream_t st) {
-  if (bits == 3) return sb_f32 ? persist_dispatch<3, float>(mt, tm, nwc, a, grid, lds_bytes, st) : persist_dispatch<3, uint16_t>(mt, tm, nwc, a, grid, lds_bytes, st);
-  return sb_f32 ? persist_dispatch<4, float>(mt, tm, nwc, a, grid, lds_bytes, st) : persist_dispatch<4, uint16_t>(mt, tm, nwc, a, grid, lds_bytes, st);
 }
 
 template <int BITS, typename ST, int NW, int TM, int CPW>

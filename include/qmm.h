@@ -65,14 +65,11 @@ typedef enum {
                              per pass; bf16 activations only */
   QMM_VARIANT_STREAM = 3, /* matrix-core kernel for 1..16 rows: one workgroup per 16 rows of W,
                              all of a wave's weight loads issued up front; bf16 activations */
-  QMM_VARIANT_PERSIST = 4, /* matrix-core kernel, 1..64 rows per pass: one workgroup per compute
-                              unit owning several 16-row tiles of W, activations streamed through
-                              LDS by dedicated loader waves; bf16 activations */
-  QMM_VARIANT_RESIDENT = 5, /* matrix-core kernel for 1..16 rows whose activation block fits in
+  QMM_VARIANT_RESIDENT = 4, /* matrix-core kernel for 1..16 rows whose activation block fits in
                                one compute unit's LDS (rows*K*2 <= 160 KB): one workgroup per
                                compute unit, activations staged once, its waves split the K of
                                up to four 16-row tiles of W; bf16 activations */
-  QMM_VARIANT_SLAB = 6      /* matrix-core kernel for 17..64 rows per pass: one workgroup per
+  QMM_VARIANT_SLAB = 5      /* matrix-core kernel for 17..64 rows per pass: one workgroup per
                                compute unit owning three 16-row tiles of W, activations streamed
                                through an LDS ring in slices of 512 columns by loader waves;
                                built for K = 5120 and 8192; bf16 activations */
@@ -97,7 +94,7 @@ typedef struct {
 typedef struct qmm_plan qmm_plan;
 
 typedef struct {
-  uint64_t launches[7];   /* indexed by qmm_variant: kernels run per family */
+  uint64_t launches[6];   /* indexed by qmm_variant: kernels run per family */
   int32_t last_variant;   /* family of the last qmm_run */
   int32_t last_ntw;       /* output tiles (16 rows of W each) per wavefront */
   int32_t last_splitk;    /* K splits folded through the workspace */
@@ -147,7 +144,7 @@ qmm_status qmm_run(const qmm_plan* plan, const void* x, const void* codes, const
 
 /* qmm_run with a forced kernel family and launch shape, for tests and
  * measurement.  ntw: tiles of 16 rows of W per wavefront (1, 2, 4; for the
- * PERSIST family: tiles a workgroup holds at once, 1..4);
+ * RESIDENT family: tiles a workgroup holds at once, 1..4; ignored by SLAB);
  * kwaves: wavefronts of a workgroup that split K between them (1, 2, 4;
  * MFMA family only); splitk: workgroups that split K, folded through the
  * workspace (>= 1).  Each may be 0 for the plan's choice. */

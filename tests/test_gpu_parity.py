@@ -86,7 +86,7 @@ SMALL = [
 def _variants(x_dtype, M, K):
     out = ["gemv"]
     if x_dtype == "bf16":
-        out += ["mfma", "persist"] + (["stream"] if stream_ok(K, M) else []) + (
+        out += ["mfma"] + (["stream"] if stream_ok(K, M) else []) + (
             ["resident"] if resident_ok(K, M) else [])
     return out
 
@@ -97,7 +97,7 @@ def test_small_parity(case):
     p = synth.small(100 + M, bits=bits, K=K, N=N, M=M, x_dtype=xd, sb_dtype=sd)
     r = Runner(p)
     for v in _variants(xd, M, K):
-        shapes = {"stream": [(0, 0, 0)], "persist": [(0, 0, 0), (1, 0, 0), (2, 0, 0), (3, 0, 0)],
+        shapes = {"stream": [(0, 0, 0)],
                   "resident": [(0, 0, 0), (1, 0, 0), (2, 0, 0), (3, 0, 0), (4, 0, 0)]}.get(
             v, [(0, 0, 0), (1, 1, 1), (2, 2, 2), (1, 4, 3), (2, 4, 1), (4, 1, 2)])
         for ntw, kw, s in shapes:
@@ -115,12 +115,12 @@ def test_determinism_and_row_independence():
     p = synth.small(7, bits=3, K=1024, N=320, M=16)
     r = Runner(p)
     for v, ntw, kw, s in (("mfma", 1, 2, 4), ("mfma", 2, 4, 1), ("gemv", 1, 0, 4), ("stream", 0, 0, 0),
-                          ("persist", 0, 0, 0), ("resident", 0, 0, 0)):
+                          ("resident", 0, 0, 0)):
         say("determinism", v)
         a = r.run(variant=v, ntw=ntw, kwaves=kw, splitk=s)
         b2 = r.run(variant=v, ntw=ntw, kwaves=kw, splitk=s)
         assert np.array_equal(a, b2)
-        if v in ("mfma", "stream", "persist", "resident"):
+        if v in ("mfma", "stream", "resident"):
             a9 = r.run(rows=9, variant=v, ntw=ntw, kwaves=kw, splitk=s)
             assert np.array_equal(a9[:9], a[:9])
 
@@ -129,7 +129,7 @@ def test_rows_past_m_and_past_end_untouched():
     import torch
     p = synth.small(8, bits=4, K=512, N=64, M=5)
     r = Runner(p, max_rows=8)
-    for v in ("mfma", "gemv", "stream", "persist", "resident"):
+    for v in ("mfma", "gemv", "stream", "resident"):
         say("canary", v)
         out = torch.full((9, 64), 7.0, dtype=torch.bfloat16, device="cuda")
         r.lin.plan.run(r.x[:5], r.lin.codes, r.lin.sb, out=out[:5], variant=v, splitk=2)
@@ -195,7 +195,7 @@ def test_workload0_full(variant):
     check_against_oracle(p, r.run(variant=variant), label="w0 " + variant)
 
 
-@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma", "stream", "persist", "resident"])
+@pytest.mark.parametrize("variant", ["auto", "gemv", "mfma", "stream", "resident"])
 def test_workload1_full(variant):
     (p,) = synth.workload(1)
     say("workload 1", variant)
@@ -207,7 +207,7 @@ def test_workload1_full(variant):
 def test_workload2_full(rows):
     (p,) = synth.workload(2)
     r = Runner(p, max_rows=64)
-    variants = ["auto", "mfma", "persist", "resident", "slab"] + (["gemv"] if rows <= 9 else []) + (
+    variants = ["auto", "mfma", "resident", "slab"] + (["gemv"] if rows <= 9 else []) + (
         ["stream"] if stream_ok(p.K, rows) else [])
     for v in variants:
         say("workload 2 rows", rows, v)
@@ -218,7 +218,7 @@ def test_workload2_full(rows):
 def test_workload3_full():
     for p in synth.workload(3):
         r = Runner(p)
-        for v in ("auto", "gemv", "mfma", "persist") + (("stream",) if stream_ok(p.K, p.M) else ()) + (
+        for v in ("auto", "gemv", "mfma") + (("stream",) if stream_ok(p.K, p.M) else ()) + (
                 ("resident",) if resident_ok(p.K, p.M) else ()):
             say("workload 3", p.name, v)
             check_against_oracle(p, r.run(variant=v), label="w3 %s %s" % (p.name, v))
@@ -255,17 +255,22 @@ def test_slab_rejects_unbuilt_k():
     assert ei.value.status == b.QMM_ERR_UNSUPPORTED
 
 
-def test_persist_multiple_passes_and_partial_rounds():
-    """More tiles than workgroups (tile passes) and a K that is not a whole
-    number of rounds."""
-    p = synth.small(12, bits=3, K=640, N=4160, M=20)
+def test_resident_and_slab_more_tiles_than_workgroups():
+    """More tiles than one pass of resident workgroups holds (N/16 > 4 x compute
+    units forces the resident kernel's fallback slot count) and ragged slab
+    tile slots at K=8192."""
+    p = synth.small(12, bits=3, K=640, N=16400, M=5)
     r = Runner(p)
-    for tm in (1, 2):
-        say("persist passes tm", tm)
-        check_against_oracle(p, r.run(variant="persist", ntw=tm), label="persist tm=%d" % tm)
+    for tm in (1, 4):
+        say("resident tm", tm)
+        check_against_oracle(p, r.run(variant="resident", ntw=tm), label="resident tm=%d" % tm)
+    q = synth.small(15, bits=4, K=8192, N=16 * 260, M=20)
+    rq = Runner(q)
+    say("slab ragged K=8192")
+    check_against_oracle(q, rq.run(variant="slab"), label="slab ragged")
 
 
-@pytest.mark.parametrize("variant", ["auto", "persist", "slab"])
+@pytest.mark.parametrize("variant", ["auto", "slab", "mfma"])
 def test_workload4_sampled(variant):
     (p,) = synth.workload(4)
     say("workload 4", variant)
