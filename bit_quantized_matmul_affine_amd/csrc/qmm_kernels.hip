@@ -1367,8 +1367,11 @@ int slab_slices(int mt, int nC) {
   return 0;
 }
 
-// LDS ring slots per row-tile count: 128 KB of activations in every case.
-static constexpr int slab_ring(int mt) { return mt == 4 ? 2 : (mt == 2 ? 4 : 8); }
+// LDS ring slots and weight ring depth (slices of loads in flight per
+// compute wave), measured on the 3-bit 5120x10240 workload: deeper weight
+// rings queue the activation slices behind weight loads and run slower.
+static constexpr int slab_ring(int mt) { return mt == 4 ? 2 : 4; }
+static constexpr int slab_depth(int mt) { return mt == 2 ? 2 : 3; }
 size_t slab_lds_bytes(int mt) { return (size_t)slab_ring(mt) * 16 * mt * 1024; }
 
 template <int BITS, typename ST>
@@ -1376,7 +1379,7 @@ static hipError_t slab_dispatch(int mt, int ns, const LaunchArgs& a, int grid, s
                                 hipStream_t st) {
 #define QMM_SLAB(MTV, NSV)                                                                    \
   if (mt == MTV && ns == NSV) {                                                               \
-    auto* kfn = &slab_kernel<BITS, MTV, kSlabTiles, NSV, slab_ring(MTV), MTV == 4 ? 3 : 4, ST>; \
+    auto* kfn = &slab_kernel<BITS, MTV, kSlabTiles, NSV, slab_ring(MTV), slab_depth(MTV), ST>; \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                    \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                            \
