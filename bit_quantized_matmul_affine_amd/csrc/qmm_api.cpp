@@ -127,6 +127,13 @@ bool slab_fits(const qmm_plan* p) {
          qmm::slab_slices(4, p->nC) > 0;
 }
 
+// LDS the streaming kernel may stage activations in: 64 KB keeps two or more
+// of its workgroups per compute unit; when the tiles fit in one pass over the
+// compute units anyway, a workgroup may take a whole unit's LDS.
+size_t stream_max_lds(const qmm_plan* p) {
+  return p->nT <= device_cus() ? qmm::kMaxLdsBytes : (size_t)64 * 1024;
+}
+
 int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
@@ -136,7 +143,8 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   // built for this K; elsewhere the resident kernel while each thread stages
   // at most eight activation vectors (beyond that it spills), else MFMA.
   int nw, cpw;
-  if (rows <= 16 && stream_shape(p, &nw, &cpw) && qmm::stream_fits(nw, rows, (int)p->d.K))
+  if (rows <= 16 && stream_shape(p, &nw, &cpw) &&
+      qmm::stream_fits(nw, rows, (int)p->d.K, stream_max_lds(p)))
     return QMM_VARIANT_STREAM;
   if (slab_fits(p)) return QMM_VARIANT_SLAB;
   if (rows <= 16 && resident_fits(p, rows) &&
@@ -296,7 +304,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
   if (variant_req == QMM_VARIANT_STREAM) {
     int nw, cpw;
-    if (!stream_shape(p, &nw, &cpw) || !qmm::stream_fits(nw, std::min(rows, 16), (int)p->d.K))
+    if (!stream_shape(p, &nw, &cpw) ||
+        !qmm::stream_fits(nw, std::min(rows, 16), (int)p->d.K, stream_max_lds(p)))
       return fail(QMM_ERR_UNSUPPORTED,
                   "the streaming kernel needs K <= 16384 and rows*K*2 bytes of activations "
                   "to fit its LDS budget");

@@ -633,10 +633,9 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
 }
 
 size_t stream_lds_bytes(int nw, int M, int K) { return (size_t)M * K * 2 + (size_t)(nw - 1) * 64 * 16; }
-bool stream_fits(int nw, int M, int K) {
+bool stream_fits(int nw, int M, int K, size_t max_lds) {
   const int xv = M == 1 ? 2 : (M == 2 ? 4 : 8);
-  return M <= 16 && (long)M * K <= (long)nw * 64 * xv * 8 &&
-         stream_lds_bytes(nw, M, K) <= 64 * 1024;
+  return M <= 16 && (long)M * K <= (long)nw * 64 * xv * 8 && stream_lds_bytes(nw, M, K) <= max_lds;
 }
 
 
@@ -1272,10 +1271,16 @@ template <int BITS, typename ST, int MQ>
 static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_t lds,
                                      hipStream_t st) {
   const unsigned grid = (unsigned)(a.N / kTileN);
-#define QMM_STREAM(NWV, CPWV)                                                            \
-  if (nw == NWV && cpw == CPWV) {                                                        \
-    stream_kernel<BITS, NWV, CPWV, MQ, ST><<<grid, NWV * 64, lds, st>>>(a);             \
-    return hipGetLastError();                                                            \
+#define QMM_STREAM(NWV, CPWV)                                                                \
+  if (nw == NWV && cpw == CPWV) {                                                            \
+    auto* kfn = &stream_kernel<BITS, NWV, CPWV, MQ, ST>;                                     \
+    if (lds > 64 * 1024) {                                                                   \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                 \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e != hipSuccess) return e;                                                         \
+    }                                                                                        \
+    kfn<<<grid, NWV * 64, lds, st>>>(a);                                                     \
+    return hipGetLastError();                                                                \
   }
   QMM_STREAM(4, 2) QMM_STREAM(4, 4) QMM_STREAM(8, 4) QMM_STREAM(8, 5) QMM_STREAM(8, 8)
   QMM_STREAM(16, 8)

@@ -13,14 +13,16 @@ def say(*a):
     sys.stdout.flush()
 
 
-def stream_ok(K: int, rows: int) -> bool:
+def stream_ok(K: int, rows: int, N: int = 1 << 30) -> bool:
     """Whether the streaming kernel takes a block of `rows` rows at this K
-    (activation block staged in LDS)."""
+    (activation block staged in LDS: 64 KB, or all 160 KB when the N/16 tiles
+    fit in one pass over the 256 compute units)."""
     rows = min(rows, 16)
     nC = K // 128
     nw = 4 if nC < 16 else (8 if nC <= 64 else 16)
     xv = {1: 2, 2: 4}.get(rows, 8)
-    return nC <= 128 and rows * K <= nw * 64 * xv * 8 and rows * K * 2 + (nw - 1) * 1024 <= 65536
+    lds_cap = 160 * 1024 if N // 16 <= 256 else 65536
+    return nC <= 128 and rows * K <= nw * 64 * xv * 8 and rows * K * 2 + (nw - 1) * 1024 <= lds_cap
 
 
 def resident_ok(K: int, rows: int) -> bool:

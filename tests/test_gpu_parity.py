@@ -83,10 +83,10 @@ SMALL = [
 ]
 
 
-def _variants(x_dtype, M, K):
+def _variants(x_dtype, M, K, N):
     out = ["gemv"]
     if x_dtype == "bf16":
-        out += ["mfma"] + (["stream"] if stream_ok(K, M) else []) + (
+        out += ["mfma"] + (["stream"] if stream_ok(K, M, N) else []) + (
             ["resident"] if resident_ok(K, M) else [])
     return out
 
@@ -96,7 +96,7 @@ def test_small_parity(case):
     bits, K, N, M, xd, sd = case
     p = synth.small(100 + M, bits=bits, K=K, N=N, M=M, x_dtype=xd, sb_dtype=sd)
     r = Runner(p)
-    for v in _variants(xd, M, K):
+    for v in _variants(xd, M, K, N):
         shapes = {"stream": [(0, 0, 0)],
                   "resident": [(0, 0, 0), (1, 0, 0), (2, 0, 0), (3, 0, 0), (4, 0, 0)]}.get(
             v, [(0, 0, 0), (1, 1, 1), (2, 2, 2), (1, 4, 3), (2, 4, 1), (4, 1, 2)])
@@ -208,7 +208,7 @@ def test_workload2_full(rows):
     (p,) = synth.workload(2)
     r = Runner(p, max_rows=64)
     variants = ["auto", "mfma", "resident", "slab"] + (["gemv"] if rows <= 9 else []) + (
-        ["stream"] if stream_ok(p.K, rows) else [])
+        ["stream"] if stream_ok(p.K, rows, p.N) else [])
     for v in variants:
         say("workload 2 rows", rows, v)
         check_against_oracle(p.rows(rows), r.run(rows=rows, variant=v), rows=rows,
@@ -218,7 +218,7 @@ def test_workload2_full(rows):
 def test_workload3_full():
     for p in synth.workload(3):
         r = Runner(p)
-        for v in ("auto", "gemv", "mfma") + (("stream",) if stream_ok(p.K, p.M) else ()) + (
+        for v in ("auto", "gemv", "mfma") + (("stream",) if stream_ok(p.K, p.M, p.N) else ()) + (
                 ("resident",) if resident_ok(p.K, p.M) else ()):
             say("workload 3", p.name, v)
             check_against_oracle(p, r.run(variant=v), label="w3 %s %s" % (p.name, v))
