@@ -97,12 +97,91 @@ def measure_hbm(torch, binding, gib: int = 4, reps: int = 5):
     return best
 
 
+def time_workload(torch, binding, prob, rows, reps=5, cold=True):
+    """Mean us per matmul of `prob` at `rows` rows: a graph of R launches, each
+    on its own weight copy (R copies >= 1 GiB, so reads are cold), replayed
+    `reps` times; with cold=False one copy is reused (cache-resident)."""
+    lin = binding.QuantizedLinear(prob, max_rows=max(rows, 1))
+    wb = prob.weight_bytes
+    ring = max(2, -(-RING_BYTES // wb)) if cold else 1
+    copies = [(lin.codes, lin.sb)] + [(lin.codes.clone(), lin.sb.clone()) for _ in range(ring - 1)]
+    x = binding.to_device(prob.x[:rows])
+    y = torch.empty(rows, prob.N, dtype=torch.bfloat16 if prob.x_dtype == "bf16" else torch.float32,
+                    device="cuda")
+    plan = lin.plan
+    ws = plan.workspace(max(256, plan.workspace_bytes(rows)), x.device)
+    n = max(ring, 16)
+
+    def calls():
+        for i in range(n):
+            c, sbv = copies[i % ring]
+            plan.run(x, c, sbv, out=y, workspace=ws)
+
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    g.replay()
+    torch.cuda.synchronize()
+    d = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        d.append(e0.elapsed_time(e1) * 1e3 / n)
+    variant = plan.stats()["last_variant"]
+    del g, copies, lin
+    torch.cuda.synchronize()
+    return sum(d) / len(d), variant
+
+
+def other_workloads(torch, binding, synth, probe):
+    """The remaining configurations, each cold-read as above."""
+    out = {}
+    (p1,) = synth.workload(1)
+    us, v = time_workload(torch, binding, p1, 1)
+    gb = p1.weight_bytes / (us * 1e-6) / 1e9
+    out["4-bit 5120->10240, 1 row, bf16"] = {
+        "us": round(us, 3), "weight_GBps": round(gb, 1), "variant": v,
+        "frac_of_measured_peak": round(gb / probe, 4) if probe else None}
+    trio = {}
+    total_us, total_bytes = 0.0, 0
+    for p in synth.workload(3):
+        us, v = time_workload(torch, binding, p, p.M)
+        total_us += us
+        total_bytes += p.weight_bytes
+        trio[p.name] = {"us": round(us, 3), "weight_GBps": round(p.weight_bytes / (us * 1e-6) / 1e9, 1),
+                        "variant": v}
+    gb = total_bytes / (total_us * 1e-6) / 1e9
+    out["4-bit MLP trio 3840->15360 x2, 15360->3840, 4 rows, bf16"] = {
+        "per_projection": trio, "trio_us": round(total_us, 3), "weight_GBps": round(gb, 1),
+        "frac_of_measured_peak": round(gb / probe, 4) if probe else None}
+    (p4,) = synth.workload(4)
+    us, v = time_workload(torch, binding, p4, p4.M, reps=3)
+    tf = 2.0 * p4.M * p4.N * p4.K / (us * 1e-6) / 1e12
+    out["4-bit 8192->28672, 128 rows, bf16"] = {
+        "us": round(us, 3), "weight_GBps": round(p4.weight_bytes / (us * 1e-6) / 1e9, 1),
+        "tflops": round(tf, 2), "frac_of_bf16_mfma_peak": round(tf / 2500.0, 4), "variant": v}
+    (p0,) = synth.workload(0)
+    us, v = time_workload(torch, binding, p0, 1)
+    out["4-bit 512->512, 1 row, f32 (launch-bound)"] = {"us": round(us, 3), "variant": v}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--variant", default="auto", choices=["auto", "gemv", "mfma"])
+    ap.add_argument("--variant", default="auto",
+                    choices=["auto", "gemv", "mfma", "stream", "resident", "slab"])
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (4-bit 5120->10240 at 1 row, the MLP trio at "
+                         "4 rows, 4-bit 8192->28672 at 128 rows, 4-bit 512->512 at 1 row) and the "
+                         "cache-resident numbers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read probe")
     ap.add_argument("--probe-only", action="store_true",
@@ -111,8 +190,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: this library has no multi-GPU path",
+              file=sys.stderr)
         return 2
 
     import torch
@@ -219,6 +298,17 @@ def main() -> int:
     achieved = algorithmic_bytes(dominant) / (dom["us_mean"] * 1e-6) / 1e9
     value = len(ROWS) * weight_bytes() / (ms_step * 1e-3) / 1e9
 
+    extra, warm = None, None
+    if not args.no_extra:
+        log("cache-resident numbers")
+        warm = {}
+        for m in ROWS:
+            us, _ = time_workload(torch, binding, prob.rows(m), m, cold=False)
+            warm[str(m)] = {"us": round(us, 3),
+                            "weight_GBps_cache_resident": round(weight_bytes() / (us * 1e-6) / 1e9, 1)}
+        log("other workloads")
+        extra = other_workloads(torch, binding, synth, probe)
+
     cpu = None
     if not args.no_cpu:
         log("oracle CPU baseline")
@@ -249,6 +339,8 @@ def main() -> int:
                      "bytes_per_launch": algorithmic_bytes(dominant),
                      "us_per_launch": dom["us_mean"]},
         "hbm_read_probe_GBps": round(probe, 1) if probe else None,
+        "cache_resident_per_rows": warm,
+        "other_workloads": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
