@@ -143,8 +143,7 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   // built for this K; elsewhere the resident kernel while each thread stages
   // at most eight activation vectors (beyond that it spills), else MFMA.
   int nw, cpw;
-  if (rows <= 16 && stream_shape(p, &nw, &cpw) &&
-      qmm::stream_fits(nw, rows, (int)p->d.K, stream_max_lds(p)))
+  if (stream_shape(p, &nw, &cpw) && qmm::stream_fits(nw, cpw, rows, stream_max_lds(p)))
     return QMM_VARIANT_STREAM;
   if (slab_fits(p)) return QMM_VARIANT_SLAB;
   if (rows <= 16 && resident_fits(p, rows) &&
@@ -194,15 +193,15 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     return c;
   }
   if (variant == QMM_VARIANT_STREAM) {
-    c.rows_per_launch = 16;
+    c.rows_per_launch = qmm::kStreamMaxRows;
     c.tile_rows = 1;
     int nw = 8, cpw = 8;
     stream_shape(p, &nw, &cpw);
     c.wk = nw;
     c.ntw = cpw;  // chunks per wave for this family
     c.nTB = nT;
-    const int r = std::min(rows, 16);
-    c.lds = qmm::stream_lds_bytes(nw, r, (int)p->d.K);
+    const int r = std::min(rows, qmm::kStreamMaxRows);
+    c.lds = qmm::stream_lds_bytes(nw, cpw, r);
     c.S = 1;
     return c;
   }
@@ -305,9 +304,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   if (variant_req == QMM_VARIANT_STREAM) {
     int nw, cpw;
     if (!stream_shape(p, &nw, &cpw) ||
-        !qmm::stream_fits(nw, std::min(rows, 16), (int)p->d.K, stream_max_lds(p)))
+        !qmm::stream_fits(nw, cpw, std::min(rows, qmm::kStreamMaxRows), stream_max_lds(p)))
       return fail(QMM_ERR_UNSUPPORTED,
-                  "the streaming kernel needs K <= 16384 and rows*K*2 bytes of activations "
+                  "the streaming kernel needs K <= 16384 and its activation slices "
                   "to fit its LDS budget");
   }
   if (variant_req == QMM_VARIANT_RESIDENT && !resident_fits(p, std::min(rows, 16)))

@@ -41,10 +41,13 @@ hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const
                        size_t lds_bytes, hipStream_t st);
 hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
                          size_t lds_bytes, hipStream_t st);
-size_t stream_lds_bytes(int nw, int M, int K);
-// Whether rows*K activations fit the streaming kernel's staging (registers
-// and at most max_lds bytes of LDS).
-bool stream_fits(int nw, int M, int K, size_t max_lds);
+// Rows the streaming kernel takes per launch (its waves stage every row of
+// their own chunks' activation slices in registers on the way to LDS).
+constexpr int kStreamMaxRows = 4;
+size_t stream_lds_bytes(int nw, int cpw, int M);
+// Whether M rows fit the streaming kernel (M <= kStreamMaxRows and at most
+// max_lds bytes of LDS for NW waves of at most cpw chunks).
+bool stream_fits(int nw, int cpw, int M, size_t max_lds);
 hipError_t launch_resident(int bits, bool sb_f32, int tm, int cpw, int xv, const LaunchArgs& a,
                            int grid, size_t lds_bytes, hipStream_t st);
 // Chunks per wave of the resident kernel built for `tm` tile slots that

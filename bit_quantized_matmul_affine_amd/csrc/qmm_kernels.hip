@@ -512,54 +512,74 @@ __global__ void __launch_bounds__(kBlockThreads) mfma_kernel(LaunchArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Streaming MFMA kernel for short activation blocks (rows * K <= NW * 4096,
-// at most 16 rows).  One workgroup owns one tile of W (16 rows) and all of K;
-// its NW wavefronts take every NW-th chunk.  Order of work in a wave:
-//   1. its share of the activation block (global -> registers);
-//   2. the loads of ALL its weight chunks (at most CPW), so a compute unit's
-//      whole share of W is in flight at once;
-//   3. activations -> LDS, barrier (the wait covers only step 1: loads retire
-//      in issue order, so step 2 stays in flight);
-//   4. per chunk, in arrival order: unpack, MFMA, per-group scale.
-// MQ = accumulator registers that can hold a live row (1, 2 or 4).  The NW
-// partial tiles are added through LDS in wave order.
+// Streaming MFMA kernel for short activation blocks (at most 4 rows).  One
+// workgroup owns one tile of W (16 rows) and all of K; its NW wavefronts take
+// every NW-th chunk, at most CPW each.  Every wave works on its own data only
+// until the final sum:
+//   1. it loads the activation slices of its chunks (rows x 128 values each,
+//      XL vectors of 16 bytes per lane), then issues the loads of ALL its
+//      weight chunks, so a compute unit's whole share of W is in flight;
+//   2. once the slices arrive (loads retire in issue order, so the weights
+//      stay in flight) it stores them in its own LDS area, together with the
+//      sum of every (row, group) slice (needed for the bias and the offset of
+//      the unpacked codes);
+//   3. per chunk, in arrival order: unpack, MFMA, per-group scale;
+//   4. the NW partial tiles are added through LDS in wave order.
+// No barrier precedes step 3: a wave's compute starts as soon as its own
+// slices arrive, not when the slowest wave of the workgroup has its.
+// LDS per wave: rows x (CPW*256 + 16) bytes of slices (the 16-byte pad puts
+// consecutive rows on different banks) and rows x CPW x 2 group sums.
 // ---------------------------------------------------------------------------
-// Activation vectors (16 bytes) staged per thread: enough for rows*K/8 vectors
-// when the block has at least 512 threads and rows*K <= 4096 * (bucket rows).
-template <int MQ>
-struct StreamXVec { static constexpr int value = MQ == 1 ? 2 : (MQ == 2 ? 4 : 8); };
+constexpr int kStreamRowPad = 16;
+__device__ __forceinline__ float dpp_sum8(float s) {
+  // sum over each aligned group of 8 lanes: swap neighbours, pairs, halves
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, true));
+  return s;
+}
+
+// Vectors of 16 bytes per lane for rows (<= MQ) x CPW slices of 128 values.
+template <int MQ, int CPW>
+struct StreamXL { static constexpr int value = (MQ * CPW * 16 + 63) / 64; };
 
 template <int BITS, int NW, int CPW, int MQ, typename ST>
 __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
-  constexpr int XV = StreamXVec<MQ>::value;
+  constexpr int XL = StreamXL<MQ, CPW>::value;
+  constexpr int ROWB = CPW * 256 + kStreamRowPad;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, kg = lane >> 4;
   const int tile = blockIdx.x;
   const int nC = a.K / kChunkK;
   const int count = nC > w ? (nC - w + NW - 1) / NW : 0;  // chunks w, w+NW, ...
+  const int clast = count > 0 ? w + (count - 1) * NW : 0;  // waves without chunks re-read chunk 0
   const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
   const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
-  uint16_t* xs = reinterpret_cast<uint16_t*>(lds);  // [M][K]
+  unsigned char* xw = lds + (size_t)w * a.M * ROWB;                           // [M][ROWB]
+  float* xsum = reinterpret_cast<float*>(lds + (size_t)NW * a.M * ROWB) +
+                (size_t)w * a.M * CPW * 2;                                     // [M][CPW][2]
 
-  // 1. activation block, 16 bytes per vector; indices past the end repeat
-  //    the last vector (same value stored twice), so no branches
-  const int kv = a.K / 8, vecs = a.M * kv;
-  u32x4 xv[XV];
-  int xidx[XV];
+  // 1. activation slices: vector v = (row m, slot j, part e); slots past
+  //    `count` hold the last chunk's slice again (its results are dropped)
+  const int nv = a.M * CPW * 16;
+  u32x4 xv[XL];
+  int xo[XL];
 #pragma unroll
-  for (int i = 0; i < XV; ++i) {
-    xidx[i] = min((int)threadIdx.x + i * NW * 64, vecs - 1);
-    const int m = xidx[i] / kv, v = xidx[i] - m * kv;
-    xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)m * a.ldx + 8 * v);
+  for (int i = 0; i < XL; ++i) {
+    const int v = min(lane + 64 * i, nv - 1);
+    const int m = v / (CPW * 16), rem = v - m * (CPW * 16);
+    const int j = rem >> 4, e = rem & 15;
+    const int c = min(w + j * NW, clast);
+    xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)m * a.ldx + kChunkK * c + 8 * e);
+    xo[i] = m * ROWB + j * 256 + 16 * e;
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. all weight loads of this wave; slots past `count` re-read the wave's
-  //    last chunk and are discarded below
+  // weight loads of every slot; slots past `count` re-read the last chunk
   const uint32_t* cbase = a.codes + ((long)tile * nC) * 64 * BITS + lane * BITS;
   const ST* sbase = sbp + ((long)tile * nC * kTileN + r) * 4;
-  const int clast = w + (count > 0 ? count - 1 : 0) * NW;
   uint32_t W[CPW][BITS];
   SBPair<ST> SBv[CPW];
 #pragma unroll
@@ -572,34 +592,58 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. activations to LDS
-#pragma unroll
-  for (int i = 0; i < XV; ++i) *reinterpret_cast<u32x4*>(xs + 8 * xidx[i]) = xv[i];
-  __syncthreads();
-
-  // 4. compute in load order; rows past the last one read the last row
-  //    (never stored)
-  const uint16_t* xrow = xs + (long)min(r, a.M - 1) * a.K + 16 * kg;
-  const PairMasks mask_v = pair_mask_vgpr<BITS>();
+  // 2. slices and their group sums to this wave's LDS area.  The 8 lanes
+  //    holding one (row, slot, group) are an aligned group of 8; lanes whose
+  //    vector index is past the end hold a repeated vector and write no sum.
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+  for (int i = 0; i < XL; ++i) {
+    *reinterpret_cast<u32x4*>(xw + xo[i]) = xv[i];
+    // (each element is copied out first: a bit cast of a vector subscript
+    // compiles to element 0 here)
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t xd = xv[i][d], od = ones[d];
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xd),
+                                          __builtin_bit_cast(bf16x2, od), s, false);
+    }
+    s = dpp_sum8(s);
+    const int v = lane + 64 * i;
+    if (v < nv && (lane & 7) == 0) {
+      const int m = v / (CPW * 16), rem = v - m * (CPW * 16);
+      xsum[(m * CPW + (rem >> 4)) * 2 + ((rem >> 3) & 1)] = s;
+    }
+  }
+  // other lanes of this wave read what these lanes wrote: keep the compiler
+  // from moving the reads above the writes (LDS runs a wave's accesses in order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // 3. compute in load order; rows past the last one read the last row
+  //    (never stored)
+  const unsigned char* xrow = xw + min(r, a.M - 1) * ROWB + 32 * kg;
+  const float* srow[MQ];
+#pragma unroll
+  for (int q = 0; q < MQ; ++q) srow[q] = xsum + min(4 * kg + q, a.M - 1) * CPW * 2;
+  const PairMasks mask_v = pair_mask_vgpr<BITS>();
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc = zero;
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
-    const int c = min(w + j * NW, clast);
     const bool live = j < count;
     u32x4 A[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      A[t] = *reinterpret_cast<const u32x4*>(xrow + (long)kChunkK * c + 64 * (t >> 1) + 8 * (t & 1));
+      A[t] = *reinterpret_cast<const u32x4*>(xrow + 256 * j + 128 * (t >> 1) + 16 * (t & 1));
+    float2 ex[MQ];
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) ex[q] = *reinterpret_cast<const float2*>(srow[q] + 2 * j);
     uint32_t P[16];
     unpack_pairs<BITS>(W[j], P, mask_v);
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
-      const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0, 0, 0);
-      const f32x4 ex = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
       const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
       const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
       f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -610,15 +654,15 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
       const float sc = af.sc, bp = af.bp;
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
-        const float v = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[q]));
+        const float v = fmaf(sc, dd[q], fmaf(bp, gp ? ex[q].y : ex[q].x, acc[q]));
         acc[q] = live ? v : acc[q];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // 5. add the NW partial tiles in wave order and store rows < M
-  f32x4* red = reinterpret_cast<f32x4*>(lds + (size_t)a.M * a.K * 2);  // [NW-1][64]
+  // 4. add the NW partial tiles in wave order and store rows < M
+  f32x4* red = reinterpret_cast<f32x4*>(lds + (size_t)NW * a.M * (ROWB + CPW * 8));  // [NW-1][64]
   if (w > 0) red[(w - 1) * 64 + lane] = acc;
   __syncthreads();
   if (w != 0) return;
@@ -632,10 +676,11 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   }
 }
 
-size_t stream_lds_bytes(int nw, int M, int K) { return (size_t)M * K * 2 + (size_t)(nw - 1) * 64 * 16; }
-bool stream_fits(int nw, int M, int K, size_t max_lds) {
-  const int xv = M == 1 ? 2 : (M == 2 ? 4 : 8);
-  return M <= 16 && (long)M * K <= (long)nw * 64 * xv * 8 && stream_lds_bytes(nw, M, K) <= max_lds;
+size_t stream_lds_bytes(int nw, int cpw, int M) {
+  return (size_t)nw * M * (cpw * 256 + kStreamRowPad + cpw * 8) + (size_t)(nw - 1) * 64 * 16;
+}
+bool stream_fits(int nw, int cpw, int M, size_t max_lds) {
+  return M >= 1 && M <= kStreamMaxRows && stream_lds_bytes(nw, cpw, M) <= max_lds;
 }
 
 

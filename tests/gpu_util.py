@@ -13,16 +13,29 @@ def say(*a):
     sys.stdout.flush()
 
 
-def stream_ok(K: int, rows: int, N: int = 1 << 30) -> bool:
-    """Whether the streaming kernel takes a block of `rows` rows at this K
-    (activation block staged in LDS: 64 KB, or all 160 KB when the N/16 tiles
-    fit in one pass over the 256 compute units)."""
-    rows = min(rows, 16)
+def stream_shape(K: int):
+    """(waves, chunks per wave) of the streaming kernel for this K, or None."""
     nC = K // 128
-    nw = 4 if nC < 16 else (8 if nC <= 64 else 16)
-    xv = {1: 2, 2: 4}.get(rows, 8)
+    for nw, cpw in ((4, 2), (4, 4), (8, 4), (8, 5), (8, 8), (16, 8)):
+        if (nC < 16) != (nw == 4):
+            continue
+        if nC <= nw * cpw:
+            return nw, cpw
+    return None
+
+
+def stream_ok(K: int, rows: int, N: int = 1 << 30) -> bool:
+    """Whether the streaming kernel takes blocks of `rows` rows at this K (it
+    runs at most 4 rows per launch; each wave stages its chunks' activation
+    slices and their group sums in LDS: 64 KB per workgroup, or all 160 KB
+    when the N/16 tiles fit in one pass over the 256 compute units)."""
+    shape = stream_shape(K)
+    if shape is None:
+        return False
+    nw, cpw = shape
+    rows = min(rows, 4)
     lds_cap = 160 * 1024 if N // 16 <= 256 else 65536
-    return nC <= 128 and rows * K <= nw * 64 * xv * 8 and rows * K * 2 + (nw - 1) * 1024 <= lds_cap
+    return nw * rows * (cpw * 256 + 16 + cpw * 8) + (nw - 1) * 1024 <= lds_cap
 
 
 def resident_ok(K: int, rows: int) -> bool:

@@ -162,13 +162,22 @@ def test_resident_rejects_blocks_too_long_for_lds():
     check_against_oracle(p, r.run(rows=13, variant="resident"), rows=13, label="13 rows fit")
 
 
-def test_stream_rejects_blocks_too_long_for_lds():
-    p = synth.small(11, bits=3, K=5120, N=32, M=16)
+def test_stream_rejects_shapes_it_does_not_cover():
+    # K past 128 chunks of 128: no wave shape of the streaming kernel covers it
+    p = synth.small(11, bits=3, K=16512, N=32, M=1)
     r = Runner(p)
     with pytest.raises(b.QmmError) as ei:
         r.run(variant="stream")
     assert ei.value.status == b.QMM_ERR_UNSUPPORTED
     check_against_oracle(p, r.run(), label="auto falls back")   # auto picks another family
+    # 260 tiles (more than one pass over the compute units) leave 64 KB of LDS
+    # per workgroup: one row of K=16384 fits the 16 waves' slices, two do not
+    p = synth.small(12, bits=4, K=16384, N=4160, M=2)
+    r = Runner(p)
+    with pytest.raises(b.QmmError) as ei:
+        r.run(variant="stream")
+    assert ei.value.status == b.QMM_ERR_UNSUPPORTED
+    check_against_oracle(p, r.run(rows=1, variant="stream"), rows=1, label="one row fits")
 
 
 def test_stats_report_the_family_that_ran():
