@@ -117,9 +117,8 @@ bool stream_shape(const qmm_plan* p, int* nw, int* cpw) {
 
 // Whether a block of `rows` (<= 16) rows fits the resident kernel's LDS.
 bool resident_fits(const qmm_plan* p, int rows) {
-  return (size_t)rows * p->d.K * 2 <= qmm::kMaxLdsBytes && qmm::resident_cpw(1, p->nC) > 0 &&
-         qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(4)) > 0 &&
-         qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(1)) > 0;
+  int nw, cpw;
+  return (size_t)rows * p->d.K * 2 <= qmm::kMaxLdsBytes && qmm::resident_shape(p->nC, 1, &nw, &cpw);
 }
 
 bool slab_fits(const qmm_plan* p) {
@@ -146,9 +145,7 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (stream_shape(p, &nw, &cpw) && qmm::stream_fits(nw, cpw, rows, stream_max_lds(p)))
     return QMM_VARIANT_STREAM;
   if (slab_fits(p)) return QMM_VARIANT_SLAB;
-  if (rows <= 16 && resident_fits(p, rows) &&
-      qmm::resident_stage_vectors(rows, (int)p->d.K, qmm::resident_waves(1)) <= 8)
-    return QMM_VARIANT_RESIDENT;
+  if (rows <= 16 && resident_fits(p, rows)) return QMM_VARIANT_RESIDENT;
   return QMM_VARIANT_MFMA;
 }
 
@@ -161,22 +158,25 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
   auto pow2_floor = [](int v) { return v >= 4 ? 4 : (v >= 2 ? 2 : 1); };
   int tiles_per_block;
   if (variant == QMM_VARIANT_RESIDENT) {
-    // as few tile slots as fill every compute unit once; fewer where no
-    // built shape covers this K with that many slots
+    // as few tile slots as fill every compute unit once (fewer where no
+    // built shape covers this K with that many); more tiles than slots x
+    // compute units take a second pass
     c.rows_per_launch = 16;
     c.tile_rows = 1;
     const int g = std::min(device_cus(), nT);
-    int tm = std::min(4, (nT + g - 1) / g);
-    if (ntw_req) tm = std::max(1, std::min(ntw_req, 4));
-    while (tm > 1 && qmm::resident_cpw(tm, nC) == 0) --tm;
+    int tm = std::min(qmm::kResidentMaxSlots, (nT + g - 1) / g);
+    if (ntw_req) tm = std::max(1, std::min(ntw_req, qmm::kResidentMaxSlots));
+    int nw = 0, cpw = 0;
+    while (tm > 1 && !qmm::resident_shape(nC, tm, &nw, &cpw)) --tm;
+    qmm::resident_shape(nC, tm, &nw, &cpw);
     c.ntw = tm;
-    c.cpw = qmm::resident_cpw(tm, nC);
-    c.wk = qmm::resident_waves(tm);
+    c.cpw = cpw;
+    c.wk = nw;
     c.grid = (nT + tm - 1) / tm;
     c.nTB = c.grid;
     c.S = 1;
     const int r = std::min(rows, 16);
-    c.lds = std::max((size_t)r * p->d.K * 2, (size_t)c.wk * 64 * 16);
+    c.lds = qmm::resident_lds_bytes(nw, tm, r, (int)p->d.K);
     return c;
   }
   if (variant == QMM_VARIANT_SLAB) {
@@ -311,8 +311,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   }
   if (variant_req == QMM_VARIANT_RESIDENT && !resident_fits(p, std::min(rows, 16)))
     return fail(QMM_ERR_UNSUPPORTED,
-                "the resident kernel needs rows*K*2 bytes of activations (rows capped at 16) "
-                "to fit one compute unit's 160 KB of LDS");
+                "the resident kernel needs K <= 8192 and rows*K*2 bytes of activations (rows "
+                "capped at 16) to fit one compute unit's 160 KB of LDS");
   if (variant_req == QMM_VARIANT_SLAB && !slab_fits(p))
     return fail(QMM_ERR_UNSUPPORTED, "the slab kernel is built for K = 5120 and 8192 (K=%lld)",
                 (long long)p->d.K);
@@ -356,9 +356,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (variant == QMM_VARIANT_SLAB)
       e = qmm::launch_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, a, cb.grid, cb.lds, st);
     else if (variant == QMM_VARIANT_RESIDENT)
-      e = qmm::launch_resident(p->d.bits, sf, cb.ntw, cb.cpw,
-                               qmm::resident_stage_vectors(rb, (int)p->d.K, cb.wk), a, cb.grid,
-                               cb.lds, st);
+      e = qmm::launch_resident(p->d.bits, sf, cb.wk, cb.cpw, cb.ntw, a, cb.grid, cb.lds, st);
     else if (variant == QMM_VARIANT_STREAM)
       e = qmm::launch_stream(p->d.bits, sf, cb.wk, cb.ntw, a, cb.lds, st);
     else if (variant == QMM_VARIANT_MFMA)

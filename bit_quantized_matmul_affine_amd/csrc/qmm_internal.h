@@ -48,12 +48,14 @@ size_t stream_lds_bytes(int nw, int cpw, int M);
 // Whether M rows fit the streaming kernel (M <= kStreamMaxRows and at most
 // max_lds bytes of LDS for NW waves of at most cpw chunks).
 bool stream_fits(int nw, int cpw, int M, size_t max_lds);
-hipError_t launch_resident(int bits, bool sb_f32, int tm, int cpw, int xv, const LaunchArgs& a,
+hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const LaunchArgs& a,
                            int grid, size_t lds_bytes, hipStream_t st);
-// Chunks per wave of the resident kernel built for `tm` tile slots that
-// covers nC chunks of K, or 0 if none does.
-int resident_cpw(int tm, int nC);
-int resident_stage_vectors(int M, int K, int nw);
+// Resident kernel: the built (waves, chunks per wave) for `tm` tile slots
+// that covers nC chunks of K (false if none does), and its dynamic LDS bytes
+// for M rows (the activation block, reused for the partial tiles).
+bool resident_shape(int nC, int tm, int* nw, int* cpw);
+size_t resident_lds_bytes(int nw, int tm, int M, int K);
+constexpr int kResidentMaxSlots = 4;
 // Slab kernel: tile slots per workgroup, slices of K built for `mt` row tiles
 // (0 if none covers nC chunks), dynamic LDS bytes.
 constexpr int kSlabTiles = 3;
@@ -61,7 +63,6 @@ int slab_slices(int mt, int nC);
 size_t slab_lds_bytes(int mt);
 hipError_t launch_slab(int bits, bool sb_f32, int mt, int ns, const LaunchArgs& a, int grid,
                        size_t lds_bytes, hipStream_t st);
-inline int resident_waves(int tm) { return tm == 4 ? 16 : 12; }
 constexpr size_t kMaxLdsBytes = 160 * 1024;
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 

@@ -69,25 +69,38 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(16)));
 // Scales/biases: block b holds 16 rows x {s_g0, s_g1, b_g0, b_g1}.
 // ---------------------------------------------------------------------------
 
-// v_and_or_b32 with the mask in an SGPR and the or-value 0x43004300 in a
-// VGPR.  gfx9 VOP3 instructions take no literal and read at most one scalar,
-// so the compiler splits (x & m) | c with two constants into two
-// instructions; this keeps it to one, and the three masks of the 3-bit layout
-// cost scalar registers only.
+// (x & mask) | or_v as one v_and_or_b32: the masks sit in SGPRs and the
+// or-value 0x43004300 in a VGPR, each produced once by an opaque move (gfx9
+// VOP3 instructions take no literal and read at most one scalar, so with two
+// visible constants the compiler would split the expression in two).  The
+// and-or itself stays ordinary code: its results feed MFMA operands, and the
+// compiler inserts the wait states between a vector write and an MFMA read
+// only for instructions it can see (not for inline assembly).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask_s, uint32_t or_v) {
+  return (x & mask_s) | or_v;
+}
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t v) {
   uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask_s), "v"(or_v));
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
   return r;
 }
 
-// The or-value of unpack_pairs, held in a VGPR.
+// The or-value of unpack_pairs in a VGPR and the field masks in SGPRs.
 struct PairMasks {
   uint32_t orv;
+  uint32_t m4, m0, m3, m5;  // 0x000F000F, 0x00070007, 0x00380038, 0x00200020
 };
 template <int BITS>
 __device__ __forceinline__ PairMasks pair_mask_vgpr() {
   PairMasks k;
   asm volatile("v_mov_b32 %0, %1" : "=v"(k.orv) : "s"(0x43004300u));
+  if constexpr (BITS == 4) {
+    k.m4 = opaque_sgpr(0x000F000Fu);
+  } else {
+    k.m0 = opaque_sgpr(0x00070007u);
+    k.m3 = opaque_sgpr(0x00380038u);
+    k.m5 = opaque_sgpr(0x00200020u);
+  }
   return k;
 }
 
@@ -108,9 +121,9 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* P, con
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) P[4 * j + t] = and_or(w[j] >> (4 * t), 0x000F000Fu, k.orv);
+      for (int t = 0; t < 4; ++t) P[4 * j + t] = and_or(w[j] >> (4 * t), k.m4, k.orv);
   } else {
-    constexpr uint32_t m0 = 0x00070007u, m3 = 0x00380038u;
+    const uint32_t m0 = k.m0, m3 = k.m3;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const uint32_t w6 = w[j] >> 6;
@@ -126,7 +139,7 @@ __device__ __forceinline__ void unpack_pairs(const uint32_t* w, uint32_t* P, con
     // pair 15 (group 1): bit b of each code sits in bit 15 / bit 31 of word b
     const uint32_t b0 = (w[0] >> 12) & 0x00080008u;
     const uint32_t b1 = (w[1] >> 11) & 0x00100010u;
-    const uint32_t b2 = and_or(w[2] >> 10, 0x00200020u, k.orv);
+    const uint32_t b2 = and_or(w[2] >> 10, k.m5, k.orv);
     P[15] = b0 | b1 | b2;
   }
 }
@@ -684,150 +697,7 @@ bool stream_fits(int nw, int cpw, int M, size_t max_lds) {
 }
 
 
-// ---------------------------------------------------------------------------
-// Resident MFMA kernel for blocks of up to 16 activation rows whose whole
-// activation block fits in LDS (rows*K*2 <= 160 KB).  One workgroup per
-// compute unit; workgroup g owns tiles g, g+G, ... (TM slots, one pass).
-//   1. every thread loads its XV vectors of the activation block, then every
-//      wave issues the loads of all (at most CPW) chunks it will use, then
-//      the activations go to LDS; one barrier.  Loads retire in issue order,
-//      so the wait for the activations retires no weight load;
-//   2. wave v works on tile slot v / WPT and on the chunks kpart, kpart+WPT,
-//      ... of K (kpart = v % WPT) with no further barrier or wait on memory
-//      other than its own weights;
-//   3. the WPT partial tiles of each tile are added through LDS (reusing the
-//      activation space) in K-part order.
-// LDS holds row m's 16-byte vector v at position v ^ (m & 15), so the 16 rows
-// an A-fragment read touches fall on distinct banks without padding.
-// ---------------------------------------------------------------------------
-template <int BITS, int NW, int TM, int CPW, int XV, typename ST>
-__global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
-  constexpr int WPT = NW / TM;
-  static_assert(NW % TM == 0, "waves must split evenly over tile slots");
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  u32x4* xs = reinterpret_cast<u32x4*>(lds);  // [M][K/8] swizzled vectors
-  const int lane = threadIdx.x & 63, v = threadIdx.x >> 6;
-  const int r = lane & 15, kg = lane >> 4;
-  const int slot = v / WPT, kpart = v - slot * WPT;
-  const int G = gridDim.x;
-  const int nT = a.N / kTileN, nC = a.K / kChunkK;
-  const int M = a.M;
-  const int kv = a.K / 8;  // vectors per activation row
-  const int tile = blockIdx.x + slot * G;
-  const bool active = tile < nT;
-  const int t = active ? tile : nT - 1;
-  // chunks of this wave (the host guarantees count <= CPW)
-  const int count = nC > kpart ? (nC - kpart + WPT - 1) / WPT : 0;
-  // last chunk this wave reads; a wave with no chunks (nC < WPT) reads chunk 0
-  const int clast = count > 0 ? kpart + (count - 1) * WPT : 0;
-  const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
-  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
-
-  // 1a. activation loads (indices past the end repeat the last vector)
-  const int vecs = M * kv;
-  u32x4 xv[XV];
-  int xi[XV];
-#pragma unroll
-  for (int i = 0; i < XV; ++i) {
-    xi[i] = min((int)threadIdx.x + i * NW * 64, vecs - 1);
-    const int m = xi[i] / kv, c = xi[i] - m * kv;
-    xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)m * a.ldx + 8 * c);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 1b. every weight load of this wave (chunks past the last repeat it)
-  const uint32_t* cbase = a.codes + ((long)t * nC) * 64 * BITS + lane * BITS;
-  const ST* sbase = sbp + ((long)t * nC * kTileN + r) * 4;
-  uint32_t W[CPW][BITS];
-  SBPair<ST> SBv[CPW];
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int c = min(kpart + j * WPT, clast);
-    const uint32_t* p = cbase + (long)c * 64 * BITS;
-#pragma unroll
-    for (int q = 0; q < BITS; ++q) W[j][q] = __builtin_nontemporal_load(p + q);
-    SBv[j].load(sbase + (long)c * kTileN * 4);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 1c. activations to LDS
-#pragma unroll
-  for (int i = 0; i < XV; ++i) {
-    const int m = xi[i] / kv, c = xi[i] - m * kv;
-    xs[(long)m * kv + (c ^ (m & 15))] = xv[i];
-  }
-  __syncthreads();
-
-  // 2. this wave's chunks
-  const int xm = min(r, M - 1);
-  const u32x4* xrow = xs + (long)xm * kv;
-  const int sw = xm & 15;
-  const PairMasks mask_v = pair_mask_vgpr<BITS>();
-  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc = zero;
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const bool live = j < count;
-    const int c = min(kpart + j * WPT, clast);
-    u32x4 A[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)  // vector of (chunk c, group q>>1, quarter kg, half q&1)
-      A[q] = xrow[(16 * c + 8 * (q >> 1) + 2 * kg + (q & 1)) ^ sw];
-    uint32_t P[16];
-    unpack_pairs<BITS>(W[j], P, mask_v);
-#pragma unroll
-    for (int gp = 0; gp < 2; ++gp) {
-      const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0, 0, 0);
-      const f32x4 ex = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
-      const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
-      const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
-      f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
-      dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
-                                                   __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
-      const Affine af = group_affine<BITS>(gp, SBv[j].s(gp), SBv[j].b(gp));
-      const float sc = live ? af.sc : 0.f;
-      const float bp = live ? af.bp : 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(sc, dd[q], fmaf(bp, ex[q], acc[q]));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // 3. fold the WPT partial tiles of each slot in K-part order
-  __syncthreads();  // activations are dead from here on
-  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [NW][64]
-  red[v * 64 + lane] = acc;
-  __syncthreads();
-  if (kpart != 0 || !active) return;
-  for (int i = 1; i < WPT; ++i) acc += red[(v + i) * 64 + lane];
-  const int n = tile * kTileN + r;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int m = 4 * kg + q;
-    if (m < M) store_y<false>(a.y, (long)m * a.ldy + n, acc[q]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Slab kernel for 17..64 activation rows.  One workgroup per compute unit
-// owning TM tiles of W; K is walked in NS slices of four chunks (512 k).
-//   * four loader waves copy activation slices straight from global memory
-//     into a ring of RB LDS slots (LDS-direct loads: no registers), running
-//     up to RB-1 slices ahead; they wait only on their own loads;
-//   * 4*TM compute waves: wave (i, kp) owns tile slot i and chunk kp of every
-//     slice, keeps its weight loads DR slices ahead in a register ring, and
-//     forms the per-group activation sums with an all-ones MFMA;
-//   * one barrier per slice; the slice loop is unrolled, so every wait on
-//     memory is an exact count and no wave waits on another's loads.
-// An LDS slot holds [16*MT rows][64 vectors of 16 bytes]; row m keeps its
-// vector v at v ^ (m & 15) (16 rows reading one column hit distinct banks).
-// Rows >= M repeat row M-1 (their outputs are never stored).  The four
-// partial tiles of each tile are added through LDS in K order at the end.
-// ---------------------------------------------------------------------------
+// Wait and barrier helpers of the resident and slab kernels.
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -857,6 +727,172 @@ __device__ __forceinline__ void wait_slices(int n) {
 // s_waitcnt for every outstanding LDS access (vector-memory counter untouched).
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// ---------------------------------------------------------------------------
+// Resident MFMA kernel for blocks of up to 16 activation rows whose whole
+// activation block fits in LDS (rows*K*2 <= 160 KB).  Workgroup g owns the
+// TM tiles g, g+G, g+2G, ... (G = grid size); its NW wavefronts split K:
+// wave w takes chunks w, w+NW, ... (at most CPW) of every one of those tiles,
+// so each activation fragment it reads, and each group sum it forms, serves
+// TM tiles.  Order of work in a wave:
+//   1. LDS-direct loads (no registers) of the activation slices of its
+//      chunks, then the loads of ALL its weights (CPW chunks x TM tiles), so
+//      a compute unit's whole share of W is in flight at once;
+//   2. a wait for its own activation slices only (loads retire in issue
+//      order, so the weights stay in flight); no barrier;
+//   3. per chunk, in arrival order: the A fragments and the group sums
+//      (all-ones MFMA), then per tile: unpack, MFMA, per-group scale;
+//   4. the NW partial tiles of each tile are added through LDS (reusing the
+//      activation space) in wave order.
+// LDS holds chunk c's slice at c*M*256 bytes, row m's 16-byte vector e at
+// position e ^ (m & 15) of its row, so the 16 rows an A-fragment read
+// touches fall on distinct banks.  Tile slots past the last tile re-read the
+// workgroup's first tile (cache hits; never stored).
+// ---------------------------------------------------------------------------
+template <int BITS, int NW, int CPW, int TM, typename ST>
+__global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, kg = lane >> 4;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int nT = a.N / kTileN, nC = a.K / kChunkK;
+  const int M = a.M;
+  const int count = nC > w ? (nC - w + NW - 1) / NW : 0;  // chunks w, w+NW, ...
+  const int clast = count > 0 ? w + (count - 1) * NW : 0;  // waves without chunks re-read chunk 0
+  const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
+  const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
+
+  // 1a. activation slices: 4 rows x 16 vectors per instruction, lanes of
+  //     rows >= M masked off
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int c = min(w + j * NW, clast);
+    unsigned char* region = lds + (size_t)c * M * 256;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * i < M) {  // wave-uniform
+        const int m = 4 * i + (lane >> 4);
+        const int e = (lane & 15) ^ (m & 15);
+        const uint16_t* src = xg + (long)min(m, M - 1) * a.ldx + kChunkK * c + 8 * e;
+        if (m < M)
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)src,
+              (__attribute__((address_space(3))) void*)(region + i * 1024), 16, 0, 0);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 1b. every weight load, chunk-major
+  int tl[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const int tile = g + t * G;
+    tl[t] = tile < nT ? tile : g;
+  }
+  uint32_t W[CPW][TM][BITS];
+  SBPair<ST> SBv[CPW][TM];
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int c = min(w + j * NW, clast);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const uint32_t* p = a.codes + ((long)tl[t] * nC + c) * 64 * BITS + lane * BITS;
+#pragma unroll
+      for (int q = 0; q < BITS; ++q) W[j][t][q] = __builtin_nontemporal_load(p + q);
+      SBv[j][t].load(sbp + (((long)tl[t] * nC + c) * kTileN + r) * 4);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. this wave's activation slices have landed once at most its weight
+  //    loads (two per chunk and tile) are outstanding
+  wait_vm<CPW * TM * 2>();
+
+  // 3. compute in load order; rows past the last one read the last row
+  //    (never stored)
+  const int xm = min(r, M - 1);
+  const int sw = xm & 15;
+  const PairMasks mask_v = pair_mask_vgpr<BITS>();
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) acc[t] = zero;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const bool live = j < count;
+    const int c = min(w + j * NW, clast);
+    const u32x4* xrow = reinterpret_cast<const u32x4*>(lds + (size_t)c * M * 256) + xm * 16;
+    u32x4 A[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)  // vector of (group q>>1, quarter kg, half q&1)
+      A[q] = xrow[(8 * (q >> 1) + 2 * kg + (q & 1)) ^ sw];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 ex[2];
+#pragma unroll
+    for (int gp = 0; gp < 2; ++gp) {
+      const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0, 0, 0);
+      ex[gp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, A[2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      uint32_t P[16];
+      unpack_pairs<BITS>(W[j][t], P, mask_v);
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
+        const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
+        f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
+                                                     __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
+        const Affine af = group_affine<BITS>(gp, SBv[j][t].s(gp), SBv[j][t].b(gp));
+        const float sc = live ? af.sc : 0.f, bp = live ? af.bp : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, dd[q], fmaf(bp, ex[gp][q], acc[t][q]));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // 4. add the NW partial tiles of each tile in wave order (slices are dead)
+  __syncthreads();
+  f32x4* red = reinterpret_cast<f32x4*>(lds);  // [TM][NW][64]
+#pragma unroll
+  for (int t = 0; t < TM; ++t) red[(t * NW + w) * 64 + lane] = acc[t];
+  __syncthreads();
+  if (w >= TM) return;
+  const int tile = g + w * G;
+  if (tile >= nT) return;
+  f32x4 v = red[(w * NW) * 64 + lane];
+  for (int i = 1; i < NW; ++i) v += red[(w * NW + i) * 64 + lane];
+  const int n = tile * kTileN + r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int m = 4 * kg + q;
+    if (m < M) store_y<false>(a.y, (long)m * a.ldy + n, v[q]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Slab kernel for 17..64 activation rows.  One workgroup per compute unit
+// owning TM tiles of W; K is walked in NS slices of four chunks (512 k).
+//   * four loader waves copy activation slices straight from global memory
+//     into a ring of RB LDS slots (LDS-direct loads: no registers), running
+//     up to RB-1 slices ahead; they wait only on their own loads;
+//   * 4*TM compute waves: wave (i, kp) owns tile slot i and chunk kp of every
+//     slice, keeps its weight loads DR slices ahead in a register ring, and
+//     forms the per-group activation sums with an all-ones MFMA;
+//   * one barrier per slice; the slice loop is unrolled, so every wait on
+//     memory is an exact count and no wave waits on another's loads.
+// An LDS slot holds [16*MT rows][64 vectors of 16 bytes]; row m keeps its
+// vector v at v ^ (m & 15) (16 rows reading one column hit distinct banks).
+// Rows >= M repeat row M-1 (their outputs are never stored).  The four
+// partial tiles of each tile are added through LDS in K order at the end.
+// ---------------------------------------------------------------------------
 template <int BITS, int MT, int TM, int NS, int RB, int DR, typename ST>
 __global__ void __launch_bounds__((TM * 4 + 4) * 64) slab_kernel(LaunchArgs a) {
   constexpr int KP = 4, NWC = TM * KP, NWL = 4;
@@ -1347,63 +1383,55 @@ hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArg
   return sb_f32 ? stream_dispatch<4, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<4, uint16_t>(nw, cpw, a, lds_bytes, st);
 }
 
-template <int BITS, typename ST, int NW, int TM, int CPW>
-static hipError_t resident_launch_xv(int xv, const LaunchArgs& a, int grid, size_t lds,
-                                     hipStream_t st) {
-#define QMM_RES(XVV)                                                                          \
-  if (xv == XVV) {                                                                            \
-    auto* kfn = &resident_kernel<BITS, NW, TM, CPW, XVV, ST>;                                 \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                    \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-    if (e != hipSuccess) return e;                                                            \
-    kfn<<<grid, NW * 64, lds, st>>>(a);                                                       \
-    return hipGetLastError();                                                                 \
+// (waves, chunks per wave, tile slots) shapes of the resident kernel.
+#define QMM_RESIDENT_SHAPES(X)                                                               \
+  X(4, 2, 1) X(4, 2, 2) X(4, 2, 3) X(4, 2, 4) X(4, 4, 1) X(4, 4, 2) X(4, 4, 3) X(4, 4, 4)     \
+  X(8, 4, 1) X(8, 4, 2) X(8, 4, 3) X(8, 4, 4) X(8, 5, 1) X(8, 5, 2) X(8, 5, 3) X(8, 5, 4)     \
+  X(8, 8, 1) X(8, 8, 2)
+
+bool resident_shape(int nC, int tm, int* nw, int* cpw) {
+  // the fewest chunks per wave that cover K: four waves below 16 chunks
+  int best_w = 0, best_c = 0;
+#define QMM_PICK(W, C, T)                                                                  \
+  if (T == tm && (nC < 16) == (W == 4) && W * C >= nC && (best_c == 0 || C < best_c)) { \
+    best_w = W;                                                                           \
+    best_c = C;                                                                           \
   }
-  QMM_RES(2) QMM_RES(4) QMM_RES(8) QMM_RES(14)
-#undef QMM_RES
-  return hipErrorInvalidValue;
-}
-
-// (tile slots, waves, chunks per wave) shapes of the resident kernel.
-#define QMM_RESIDENT_SHAPES(X) X(1, 12, 4) X(1, 12, 8) X(1, 12, 11) X(2, 12, 7) X(2, 12, 11) \
-  X(3, 12, 10) X(4, 16, 10)
-
-int resident_cpw(int tm, int nC) {
-  const int nw = resident_waves(tm), wpt = nw / tm;
-  const int need = (nC + wpt - 1) / wpt;
-  int best = 0;
-#define QMM_PICK(T, W, C) if (T == tm && C >= need && (best == 0 || C < best)) best = C;
   QMM_RESIDENT_SHAPES(QMM_PICK)
 #undef QMM_PICK
-  return best;
+  *nw = best_w;
+  *cpw = best_c;
+  return best_c > 0;
+}
+
+size_t resident_lds_bytes(int nw, int tm, int M, int K) {
+  return std::max((size_t)M * K * 2, (size_t)tm * nw * 64 * 16);
 }
 
 template <int BITS, typename ST>
-static hipError_t resident_dispatch(int tm, int cpw, int xv, const LaunchArgs& a, int grid,
+static hipError_t resident_dispatch(int nw, int cpw, int tm, const LaunchArgs& a, int grid,
                                     size_t lds, hipStream_t st) {
-#define QMM_GO(T, W, C) \
-  if (tm == T && cpw == C) return resident_launch_xv<BITS, ST, W, T, C>(xv, a, grid, lds, st);
+#define QMM_GO(W, C, T)                                                                     \
+  if (nw == W && cpw == C && tm == T) {                                                     \
+    auto* kfn = &resident_kernel<BITS, W, C, T, ST>;                                        \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                  \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (e != hipSuccess) return e;                                                          \
+    kfn<<<grid, W * 64, lds, st>>>(a);                                                      \
+    return hipGetLastError();                                                               \
+  }
   QMM_RESIDENT_SHAPES(QMM_GO)
 #undef QMM_GO
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_resident(int bits, bool sb_f32, int tm, int cpw, int xv, const LaunchArgs& a,
+hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const LaunchArgs& a,
                            int grid, size_t lds_bytes, hipStream_t st) {
   if (bits == 3)
-    return sb_f32 ? resident_dispatch<3, float>(tm, cpw, xv, a, grid, lds_bytes, st)
-                  : resident_dispatch<3, uint16_t>(tm, cpw, xv, a, grid, lds_bytes, st);
-  return sb_f32 ? resident_dispatch<4, float>(tm, cpw, xv, a, grid, lds_bytes, st)
-                : resident_dispatch<4, uint16_t>(tm, cpw, xv, a, grid, lds_bytes, st);
-}
-
-// 16-byte activation vectors each thread stages (2, 4, 8 or 14), or 0 if
-// the block is too large.
-int resident_stage_vectors(int M, int K, int nw) {
-  const long vecs = (long)M * K / 8;
-  for (int xv : {2, 4, 8, 14})
-    if (vecs <= (long)xv * nw * 64) return xv;
-  return 0;
+    return sb_f32 ? resident_dispatch<3, float>(nw, cpw, tm, a, grid, lds_bytes, st)
+                  : resident_dispatch<3, uint16_t>(nw, cpw, tm, a, grid, lds_bytes, st);
+  return sb_f32 ? resident_dispatch<4, float>(nw, cpw, tm, a, grid, lds_bytes, st)
+                : resident_dispatch<4, uint16_t>(nw, cpw, tm, a, grid, lds_bytes, st);
 }
 
 // (row tiles, slices of 512 k) shapes of the slab kernel; three tile slots.

@@ -40,8 +40,9 @@ def stream_ok(K: int, rows: int, N: int = 1 << 30) -> bool:
 
 def resident_ok(K: int, rows: int) -> bool:
     """Whether the resident kernel takes a block of `rows` rows at this K
-    (the whole activation block of up to 16 rows in one compute unit's LDS)."""
-    return min(rows, 16) * K * 2 <= 160 * 1024
+    (the whole activation block of up to 16 rows in one compute unit's LDS,
+    K covered by at most 64 chunks of 128)."""
+    return min(rows, 16) * K * 2 <= 160 * 1024 and K // 128 <= 64
 
 
 def y_to_f64(y_bits: np.ndarray, x_dtype: str) -> np.ndarray:

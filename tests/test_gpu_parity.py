@@ -162,6 +162,19 @@ def test_resident_rejects_blocks_too_long_for_lds():
     check_against_oracle(p, r.run(rows=13, variant="resident"), rows=13, label="13 rows fit")
 
 
+@pytest.mark.parametrize("case", [(3, 640, 208, 3), (4, 1024, 400, 1), (4, 640, 208, 16)],
+                         ids=lambda c: "b%d_K%d_N%d_M%d" % c)
+def test_resident_every_slot_count(case):
+    """Four-wave workgroups (one wave per SIMD) issue the unpack and the MFMAs
+    that read its results back to back; every slot count must match the oracle."""
+    bits, K, N, M = case
+    p = synth.small(100 + M, bits=bits, K=K, N=N, M=M)
+    r = Runner(p)
+    for tm in (1, 2, 3, 4):
+        say(case, "resident tm", tm)
+        check_against_oracle(p, r.run(variant="resident", ntw=tm), label="%s tm=%d" % (case, tm))
+
+
 def test_stream_rejects_shapes_it_does_not_cover():
     # K past 128 chunks of 128: no wave shape of the streaming kernel covers it
     p = synth.small(11, bits=3, K=16512, N=32, M=1)
