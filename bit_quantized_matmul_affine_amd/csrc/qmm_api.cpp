@@ -137,15 +137,18 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
   if (p->force_variant) return p->force_variant;
-  // Measured on the 3-bit 5120->10240 sweep: the streaming kernel while the
-  // activation block fits its LDS budget, then the slab kernel where it is
-  // built for this K; elsewhere the resident kernel while each thread stages
-  // at most eight activation vectors (beyond that it spills), else MFMA.
+  // Measured on the 3-bit 5120->10240 sweep and the 4-bit MLP shapes: the
+  // streaming kernel for one or two rows; the resident kernel up to 16 rows
+  // while the activation block fits one compute unit's LDS; the streaming
+  // kernel up to 4 rows beyond that; then the slab kernel where it is built
+  // for this K; else MFMA.
   int nw, cpw;
-  if (stream_shape(p, &nw, &cpw) && qmm::stream_fits(nw, cpw, rows, stream_max_lds(p)))
-    return QMM_VARIANT_STREAM;
-  if (slab_fits(p)) return QMM_VARIANT_SLAB;
+  const bool stream_ok = stream_shape(p, &nw, &cpw) &&
+                         qmm::stream_fits(nw, cpw, rows, stream_max_lds(p));
+  if (rows <= 2 && stream_ok) return QMM_VARIANT_STREAM;
   if (rows <= 16 && resident_fits(p, rows)) return QMM_VARIANT_RESIDENT;
+  if (stream_ok) return QMM_VARIANT_STREAM;
+  if (slab_fits(p)) return QMM_VARIANT_SLAB;
   return QMM_VARIANT_MFMA;
 }
 
@@ -164,7 +167,12 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.rows_per_launch = 16;
     c.tile_rows = 1;
     const int g = std::min(device_cus(), nT);
+    const int r = std::min(rows, 16);
     int tm = std::min(qmm::kResidentMaxSlots, (nT + g - 1) / g);
+    // four slots per unit: two workgroups of two slots each keep twice the
+    // waves per unit at the same tiles per unit (measured faster) where two
+    // activation blocks fit its LDS
+    if (tm == 4 && 2 * (size_t)r * p->d.K * 2 <= qmm::kMaxLdsBytes) tm = 2;
     if (ntw_req) tm = std::max(1, std::min(ntw_req, qmm::kResidentMaxSlots));
     int nw = 0, cpw = 0;
     while (tm > 1 && !qmm::resident_shape(nC, tm, &nw, &cpw)) --tm;
@@ -175,7 +183,6 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.grid = (nT + tm - 1) / tm;
     c.nTB = c.grid;
     c.S = 1;
-    const int r = std::min(rows, 16);
     c.lds = qmm::resident_lds_bytes(nw, tm, r, (int)p->d.K);
     return c;
   }

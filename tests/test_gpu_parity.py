@@ -202,9 +202,12 @@ def test_stats_report_the_family_that_ran():
     r.run(variant="mfma")
     st = r.lin.plan.stats()
     assert st["last_variant"] == "mfma" and st["launches"]["mfma"] >= 1
-    r.run()  # 4 rows: the streaming kernel serves short blocks by default
+    r.run(rows=2)  # one or two rows: the streaming kernel by default
     st = r.lin.plan.stats()
     assert st["last_variant"] == "stream" and st["launches"]["stream"] >= 1
+    r.run()  # 4 rows whose activations fit one compute unit's LDS: resident
+    st = r.lin.plan.stats()
+    assert st["last_variant"] == "resident" and st["launches"]["resident"] >= 1
 
 
 # ------------------------------------------------------------------ workloads
