@@ -63,12 +63,14 @@ typedef enum {
   QMM_VARIANT_GEMV = 1,   /* vector-ALU kernel, activations staged in LDS; 1..8 rows per pass */
   QMM_VARIANT_MFMA = 2,   /* blocked matrix-core kernel (bf16 in, f32 accumulate), 1..64 rows
                              per pass; bf16 activations only */
-  QMM_VARIANT_STREAM = 3, /* matrix-core kernel for 1..16 rows: one workgroup per 16 rows of W,
-                             all of a wave's weight loads issued up front; bf16 activations */
+  QMM_VARIANT_STREAM = 3, /* matrix-core kernel for 1..4 rows per launch (more rows run as
+                             blocks of 4): one workgroup per 16 rows of W, each wave stages
+                             the activations of its own chunks and issues all its weight
+                             loads up front; K <= 16384; bf16 activations */
   QMM_VARIANT_RESIDENT = 4, /* matrix-core kernel for 1..16 rows whose activation block fits in
-                               one compute unit's LDS (rows*K*2 <= 160 KB): one workgroup per
-                               compute unit, activations staged once, its waves split the K of
-                               up to four 16-row tiles of W; bf16 activations */
+                               one compute unit's LDS (rows*K*2 <= 160 KB, K <= 8192): one
+                               workgroup holds up to four 16-row tiles of W, each wave takes
+                               a share of K for all of them; bf16 activations */
   QMM_VARIANT_SLAB = 5      /* matrix-core kernel for 17..64 rows per pass: one workgroup per
                                compute unit owning three 16-row tiles of W, activations streamed
                                through an LDS ring in slices of 512 columns by loader waves;
