@@ -138,6 +138,44 @@ def time_workload(torch, binding, prob, rows, reps=5, cold=True):
     return sum(d) / len(d), variant
 
 
+def time_gate_up(torch, binding, gate, up, reps=5):
+    """Mean us per fused gate/up call (qmm_run_gate_up) of the MLP's gate and up
+    projections, cold as in time_workload (a ring of weight-pair copies)."""
+    lg = binding.QuantizedLinear(gate, max_rows=gate.M)
+    lu = binding.QuantizedLinear(up, max_rows=up.M)
+    wb = gate.weight_bytes + up.weight_bytes
+    ring = max(2, -(-RING_BYTES // wb))
+    copies = [(lg.codes, lg.sb, lu.codes, lu.sb)] + [
+        (lg.codes.clone(), lg.sb.clone(), lu.codes.clone(), lu.sb.clone()) for _ in range(ring - 1)]
+    x = binding.to_device(gate.x)
+    h = torch.empty(gate.M, gate.N, dtype=torch.bfloat16, device="cuda")
+    n = max(ring, 16)
+
+    def calls():
+        for i in range(n):
+            gc, gs, uc, us_ = copies[i % ring]
+            lg.plan.run_gate_up(x, gc, gs, uc, us_, out=h)
+
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    g.replay()
+    torch.cuda.synchronize()
+    d = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        d.append(e0.elapsed_time(e1) * 1e3 / n)
+    del g, copies, lg, lu
+    torch.cuda.synchronize()
+    return sum(d) / len(d), wb
+
+
 def other_workloads(torch, binding, synth, probe):
     """The remaining configurations, each cold-read as above."""
     out = {}
@@ -156,9 +194,18 @@ def other_workloads(torch, binding, synth, probe):
         trio[p.name] = {"us": round(us, 3), "weight_GBps": round(p.weight_bytes / (us * 1e-6) / 1e9, 1),
                         "variant": v}
     gb = total_bytes / (total_us * 1e-6) / 1e9
+    gate, up, down = synth.workload(3)
+    gu_us, gu_bytes = time_gate_up(torch, binding, gate, up)
+    fused_us = gu_us + trio["c3_down"]["us"]
+    fgb = total_bytes / (fused_us * 1e-6) / 1e9
     out["4-bit MLP trio 3840->15360 x2, 15360->3840, 4 rows, bf16"] = {
         "per_projection": trio, "trio_us": round(total_us, 3), "weight_GBps": round(gb, 1),
-        "frac_of_measured_peak": round(gb / probe, 4) if probe else None}
+        "frac_of_measured_peak": round(gb / probe, 4) if probe else None,
+        "fused_gate_up": {"us": round(gu_us, 3),
+                          "weight_GBps": round(gu_bytes / (gu_us * 1e-6) / 1e9, 1),
+                          "what": "silu(x.Wg^T)*(x.Wu^T) in one kernel (qmm_run_gate_up)"},
+        "trio_fused_us": round(fused_us, 3), "weight_GBps_fused": round(fgb, 1),
+        "frac_of_measured_peak_fused": round(fgb / probe, 4) if probe else None}
     (p4,) = synth.workload(4)
     us, v = time_workload(torch, binding, p4, p4.M, reps=3)
     tf = 2.0 * p4.M * p4.N * p4.K / (us * 1e-6) / 1e12

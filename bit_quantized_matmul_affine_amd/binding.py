@@ -40,6 +40,7 @@ SIGNATURES = {
     "qmm_run": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _P, _c.c_size_t, _P]),
     "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P,
                               _P, _c.c_int32, _P, _c.c_size_t, _P]),
+    "qmm_run_gate_up": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _c.c_int32, _c.c_int32, _P]),
     "qmm_debug_unpack": (_c.c_int, [_P, _P, _P, _P]),
     "qmm_get_stats": (_c.c_int, [_P, _P]),
     "qmm_last_error": (_c.c_char_p, []),
@@ -77,6 +78,13 @@ def lib():
         if _lib is None:
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError("libqmm.so is not built (run __graft_entry__.build()): " + LIB_PATH)
+            # torch owns device memory and streams here: load it (and the HIP
+            # runtime it ships) before the library, so that both resolve to the
+            # one runtime torch brings
+            try:
+                import torch  # noqa: F401
+            except ImportError:
+                pass
             L = ctypes.CDLL(LIB_PATH)
             for name, (res, args) in SIGNATURES.items():
                 f = getattr(L, name)
@@ -198,6 +206,18 @@ class Plan:
         wsb = workspace.numel() if workspace is not None else 0
         _check(lib().qmm_run_ex(self._h, v, ntw, kwaves, splitk, _ptr(x), _ptr(codes), _ptr(sb),
                                 _ptr(out), rows, _ptr(workspace), wsb, _stream(stream)))
+        return out
+
+    def run_gate_up(self, x, gate_codes, gate_sb, up_codes, up_sb, out=None, tile_pairs: int = 0,
+                    stream=None):
+        """h = silu(x . Wg^T) * (x . Wu^T) with bf16 roundings (qmm_run_gate_up)."""
+        import torch
+        rows = x.numel() // self.K
+        if out is None:
+            out = torch.empty(*x.shape[:-1], self.N, dtype=x.dtype, device=x.device)
+        _check(lib().qmm_run_gate_up(self._h, _ptr(x), _ptr(gate_codes), _ptr(gate_sb),
+                                     _ptr(up_codes), _ptr(up_sb), _ptr(out), rows, tile_pairs,
+                                     _stream(stream)))
         return out
 
     def debug_unpack(self, codes, stream=None):

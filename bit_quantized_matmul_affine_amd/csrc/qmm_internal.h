@@ -27,6 +27,8 @@ struct LaunchArgs {
   int S;                  // K splits
   int nTB;                // tile blocks (kWaves * ntw tiles each)
   int ldx, ldy;           // row strides of x and y in elements
+  const uint32_t* codes2; // fused gate/up: the up projection's codes (codes = gate)
+  const void* sb2;        // fused gate/up: the up projection's scales/biases
 };
 
 // All launchers return hipSuccess or the launch error.
@@ -56,6 +58,11 @@ hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const
 bool resident_shape(int nC, int tm, int* nw, int* cpw);
 size_t resident_lds_bytes(int nw, int tm, int M, int K);
 constexpr int kResidentMaxSlots = 4;
+// Fused gate/up through the resident kernel: tile pairs per workgroup (1 or
+// 2) that are built for cq chunks, and the launch.
+bool gate_up_shape(int nC, int pairs, int* nw, int* cpw);
+hipError_t launch_gate_up(int bits, bool sb_f32, int nw, int cpw, int pairs, const LaunchArgs& a,
+                          int grid, size_t lds_bytes, hipStream_t st);
 // Slab kernel: tile slots per workgroup, slices of K built for `mt` row tiles
 // (0 if none covers nC chunks), dynamic LDS bytes.
 constexpr int kSlabTiles = 3;

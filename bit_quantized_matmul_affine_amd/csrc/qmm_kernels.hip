@@ -747,9 +747,25 @@ __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F);
 // position e ^ (m & 15) of its row, so the 16 rows an A-fragment read
 // touches fall on distinct banks.  Tile slots past the last tile re-read the
 // workgroup's first tile (cache hits; never stored).
+// GU (fused gate/up): slots 0..TM/2-1 are gate tiles and slots TM/2..TM-1 the
+// up tiles of the same columns (codes2/sb2); the store applies silu_mul().
 // ---------------------------------------------------------------------------
-template <int BITS, int NW, int CPW, int TM, typename ST>
+// The fused gate/up epilogue ("mlx-bun 0.4.0 -> 1.0.0" page, the shared-M
+// gate/up kernel of trellis-shared-m.ts): gate and up rounded to bf16 first,
+// then the sigmoid of the rounded gate, the SiLU product and the final
+// product, each rounded to bf16 (the unfused chain's roundings).
+__device__ __forceinline__ float bf16_round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+__device__ __forceinline__ float silu_mul(float gate, float up) {
+  const float g = bf16_round(gate), u = bf16_round(up);
+  const float sg = bf16_round(1.f / (1.f + expf(-g)));
+  const float silu = bf16_round(g * sg);
+  return silu * u;  // rounded to bf16 by the store
+}
+
+template <int BITS, int NW, int CPW, int TM, typename ST, bool GU = false>
 __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
+  constexpr int TMH = GU ? TM / 2 : TM;  // distinct tiles per workgroup
+  static_assert(!GU || TM % 2 == 0, "gate/up slots come in pairs");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -787,9 +803,10 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   int tl[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
-    const int tile = g + t * G;
+    const int tile = g + (t % TMH) * G;
     tl[t] = tile < nT ? tile : g;
   }
+  const ST* __restrict__ sbp2 = reinterpret_cast<const ST*>(a.sb2);
   uint32_t W[CPW][TM][BITS];
   SBPair<ST> SBv[CPW][TM];
 #pragma unroll
@@ -797,10 +814,12 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
     const int c = min(w + j * NW, clast);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
-      const uint32_t* p = a.codes + ((long)tl[t] * nC + c) * 64 * BITS + lane * BITS;
+      const bool second = GU && t >= TMH;  // compile-time once unrolled
+      const uint32_t* p = (second ? a.codes2 : a.codes) + ((long)tl[t] * nC + c) * 64 * BITS +
+                          lane * BITS;
 #pragma unroll
       for (int q = 0; q < BITS; ++q) W[j][t][q] = __builtin_nontemporal_load(p + q);
-      SBv[j][t].load(sbp + (((long)tl[t] * nC + c) * kTileN + r) * 4);
+      SBv[j][t].load((second ? sbp2 : sbp) + (((long)tl[t] * nC + c) * kTileN + r) * 4);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -864,12 +883,18 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
 #pragma unroll
   for (int t = 0; t < TM; ++t) red[(t * NW + w) * 64 + lane] = acc[t];
   __syncthreads();
-  if (w >= TM) return;
+  if (w >= TMH) return;
   const int tile = g + w * G;
   if (tile >= nT) return;
   f32x4 v = red[(w * NW) * 64 + lane];
   for (int i = 1; i < NW; ++i) v += red[(w * NW + i) * 64 + lane];
   const int n = tile * kTileN + r;
+  if constexpr (GU) {
+    f32x4 u = red[((w + TMH) * NW) * 64 + lane];
+    for (int i = 1; i < NW; ++i) u += red[((w + TMH) * NW + i) * 64 + lane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = silu_mul(v[q], u[q]);
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int m = 4 * kg + q;
@@ -1432,6 +1457,50 @@ hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const
                   : resident_dispatch<3, uint16_t>(nw, cpw, tm, a, grid, lds_bytes, st);
   return sb_f32 ? resident_dispatch<4, float>(nw, cpw, tm, a, grid, lds_bytes, st)
                 : resident_dispatch<4, uint16_t>(nw, cpw, tm, a, grid, lds_bytes, st);
+}
+
+// (waves, chunks per wave, tile pairs) shapes of the fused gate/up kernel.
+#define QMM_GATE_UP_SHAPES(X) X(4, 2, 1) X(4, 2, 2) X(4, 4, 1) X(4, 4, 2) X(8, 4, 1) X(8, 4, 2) \
+  X(8, 5, 1) X(8, 5, 2) X(8, 8, 1)
+
+bool gate_up_shape(int nC, int pairs, int* nw, int* cpw) {
+  int best_w = 0, best_c = 0;
+#define QMM_PICK(W, C, P)                                                                  \
+  if (P == pairs && (nC < 16) == (W == 4) && W * C >= nC && (best_c == 0 || C < best_c)) { \
+    best_w = W;                                                                           \
+    best_c = C;                                                                           \
+  }
+  QMM_GATE_UP_SHAPES(QMM_PICK)
+#undef QMM_PICK
+  *nw = best_w;
+  *cpw = best_c;
+  return best_c > 0;
+}
+
+template <int BITS, typename ST>
+static hipError_t gate_up_dispatch(int nw, int cpw, int pairs, const LaunchArgs& a, int grid,
+                                   size_t lds, hipStream_t st) {
+#define QMM_GO(W, C, P)                                                                     \
+  if (nw == W && cpw == C && pairs == P) {                                                  \
+    auto* kfn = &resident_kernel<BITS, W, C, 2 * P, ST, true>;                              \
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                  \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (e != hipSuccess) return e;                                                          \
+    kfn<<<grid, W * 64, lds, st>>>(a);                                                      \
+    return hipGetLastError();                                                               \
+  }
+  QMM_GATE_UP_SHAPES(QMM_GO)
+#undef QMM_GO
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gate_up(int bits, bool sb_f32, int nw, int cpw, int pairs, const LaunchArgs& a,
+                          int grid, size_t lds_bytes, hipStream_t st) {
+  if (bits == 3)
+    return sb_f32 ? gate_up_dispatch<3, float>(nw, cpw, pairs, a, grid, lds_bytes, st)
+                  : gate_up_dispatch<3, uint16_t>(nw, cpw, pairs, a, grid, lds_bytes, st);
+  return sb_f32 ? gate_up_dispatch<4, float>(nw, cpw, pairs, a, grid, lds_bytes, st)
+                : gate_up_dispatch<4, uint16_t>(nw, cpw, pairs, a, grid, lds_bytes, st);
 }
 
 // (row tiles, slices of 512 k) shapes of the slab kernel; three tile slots.

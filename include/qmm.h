@@ -155,6 +155,27 @@ qmm_status qmm_run_ex(const qmm_plan* plan, int32_t variant, int32_t ntw, int32_
                       void* y, int32_t rows, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Fused gate/up projections of a gated MLP with a SiLU-times-up epilogue
+ * ("mlx-bun 0.4.0 -> 1.0.0" page, trellis-shared-m.ts, its gate/up kernel:
+ * both projections of one activation row block, then sigmoid, SiLU and
+ * product; applied here to affine weights):
+ *   gate = x . Wg^T, up = x . Wu^T (f32 sums, as qmm_run), then
+ *   h = bf16( bf16( bf16(gate) * bf16(sigmoid(bf16(gate))) ) * bf16(up) )
+ * element by element, every intermediate rounded to bf16 round-to-nearest-
+ * even as the unfused chain of bf16 operations would.  Wg and Wu share the
+ * plan's shape (bits, K, N, group size 64) and are both in the native layout
+ * of qmm_prepack.  x and h: bf16 [rows, K] and [rows, N], row-contiguous.
+ * Every activation row block of up to 16 rows is read once for both
+ * projections.  tile_pairs: 16-column tiles of each projection per
+ * workgroup (1 or 2; 0 = the plan's choice, 1).  No workspace.
+ * Errors: QMM_ERR_UNSUPPORTED for f32 activations, or when 16 rows x K bf16
+ * activations (fewer if rows < 16) exceed 160 KB or K > 8192;
+ * QMM_ERR_INVALID_ARG for NULL or misaligned pointers and rows outside
+ * 1..max_rows; QMM_ERR_HIP for launch failures. */
+qmm_status qmm_run_gate_up(const qmm_plan* plan, const void* x, const void* gate_codes,
+                           const void* gate_sb, const void* up_codes, const void* up_sb,
+                           void* h, int32_t rows, int32_t tile_pairs, void* stream);
+
 /* Workspace needed by qmm_run_ex with the same variant/ntw/kwaves/splitk. */
 size_t qmm_workspace_bytes_ex(const qmm_plan* plan, int32_t variant, int32_t ntw,
                               int32_t kwaves, int32_t splitk, int32_t rows);

@@ -15,4 +15,8 @@ from .oracle import (  # noqa: F401
     build,
     load_library,
     tolerance_coefficient,
+    round_bf16,
+    silu_mul_bf16,
+    gate_up,
+    gate_up_tolerance,
 )

@@ -161,3 +161,59 @@ def tolerance(bits: int, K: int, x, w, scales, biases, x_dtype: str,
     """Element-wise acceptance bound [M, N]."""
     sx, mw = bound_terms(bits, K, x, w, scales, biases, group_size)
     return tolerance_coefficient(x_dtype) * np.outer(sx, mw) + 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Fused gate/up epilogue ("mlx-bun 0.4.0 -> 1.0.0" page, trellis-shared-m.ts,
+# its shared-M gate/up kernel of the trellis path: gate and up are rounded to
+# the activation type, then the sigmoid of the rounded gate, the SiLU product
+# and the final product are each rounded to that type).  Applied here to the
+# affine projections.
+
+def round_bf16(v) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (8 significant bits,
+    ties to even), returned as float64.  Values below 2^-126 use the subnormal
+    spacing 2^-133; magnitudes from (2 - 2^-8) * 2^127 up overflow to inf."""
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)  # v = m * 2^e, 0.5 <= |m| < 1
+    r = np.ldexp(np.round(m * 256.0), e - 8)  # numpy rounds halves to even
+    small = np.abs(v) < 2.0 ** -126
+    r = np.where(small, np.round(v * 2.0 ** 133) * 2.0 ** -133, r)
+    big = np.abs(v) >= (2.0 - 2.0 ** -8) * 2.0 ** 127
+    return np.where(big, np.copysign(np.inf, v), r)
+
+
+def silu_mul_bf16(gate, up) -> np.ndarray:
+    """h = R(R(R(g) * R(sigmoid(R(g)))) * R(u)) with R = round_bf16 and
+    sigmoid(z) = 1 / (1 + e^-z), on float64 gate and up values."""
+    g = round_bf16(gate)
+    u = round_bf16(up)
+    with np.errstate(over="ignore"):
+        sig = round_bf16(1.0 / (1.0 + np.exp(-g)))
+    silu = round_bf16(g * sig)
+    return round_bf16(silu * u)
+
+
+def gate_up(bits: int, K: int, x, wg, sg, bg, wu, su, bu, group_size: int = 64,
+            threads: int = 1, lib=None) -> np.ndarray:
+    """The fused gate/up output for every row and column: both projections by
+    matmul(), then silu_mul_bf16()."""
+    g = matmul(bits, K, x, wg, sg, bg, group_size, threads, lib)
+    u = matmul(bits, K, x, wu, su, bu, group_size, threads, lib)
+    return silu_mul_bf16(g, u)
+
+
+def gate_up_tolerance(gate, up, tol_gate, tol_up) -> np.ndarray:
+    """Element-wise acceptance bound for the fused gate/up output, from the
+    exact gate/up values and the matmul bounds of the two projections: the
+    gate error (the matmul bound plus one bf16 step where the two sides round
+    it differently) times the largest slope of SiLU (1.1) times |up|, the up
+    error likewise times |silu(gate)|, and four bf16 steps of the result for
+    the chain's roundings."""
+    gate = np.asarray(gate, dtype=np.float64)
+    up = np.asarray(up, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        silu = gate / (1.0 + np.exp(-gate))
+    return (1.1 * np.abs(up) * (tol_gate + 2.0 ** -8 * np.abs(gate))
+            + np.abs(silu) * (tol_up + 2.0 ** -8 * np.abs(up))
+            + 2.0 ** -6 * np.abs(silu * up) + 1e-6)
