@@ -176,6 +176,42 @@ def time_gate_up(torch, binding, gate, up, reps=5):
     return sum(d) / len(d), wb
 
 
+def time_norm(torch, binding, synth, rows, D, reps=5):
+    """Mean us per residual add + RMS norm call (qmm_residual_rms_norm) over
+    bf16 [rows, D]; algorithmic bytes: x, update read, residual, normalized
+    written (2 bytes each) plus the weight vector."""
+    xr, ur, wr = synth.norm_inputs(7, rows, D, "bf16")
+    x, u, w = binding.to_device(xr), binding.to_device(ur), binding.to_device(wr)
+    res, norm = torch.empty_like(x), torch.empty_like(x)
+    n = 32 if rows * D < (1 << 24) else 4
+
+    def calls():
+        for _ in range(n):
+            binding.residual_rms_norm(x, u, w, 1e-5, residual=res, normalized=norm)
+
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    g.replay()
+    torch.cuda.synchronize()
+    d = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        d.append(e0.elapsed_time(e1) * 1e3 / n)
+    del g, x, u, res, norm
+    torch.cuda.synchronize()
+    us = sum(d) / len(d)
+    nbytes = 4 * rows * D * 2 + D * 2
+    return {"us": round(us, 3), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_8TBps": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+
 def other_workloads(torch, binding, synth, probe):
     """The remaining configurations, each cold-read as above."""
     out = {}
@@ -212,6 +248,9 @@ def other_workloads(torch, binding, synth, probe):
     out["4-bit 8192->28672, 128 rows, bf16"] = {
         "us": round(us, 3), "weight_GBps": round(p4.weight_bytes / (us * 1e-6) / 1e9, 1),
         "tflops": round(tf, 2), "frac_of_bf16_mfma_peak": round(tf / 2500.0, 4), "variant": v}
+    out["residual add + RMS norm, bf16"] = {
+        "4x3840 (decode)": time_norm(torch, binding, synth, 4, 3840),
+        "16384x5120 (HBM-bound)": time_norm(torch, binding, synth, 16384, 5120)}
     (p0,) = synth.workload(0)
     us, v = time_workload(torch, binding, p0, 1)
     out["4-bit 512->512, 1 row, f32 (launch-bound)"] = {"us": round(us, 3), "variant": v}

@@ -41,6 +41,8 @@ SIGNATURES = {
     "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P,
                               _P, _c.c_int32, _P, _c.c_size_t, _P]),
     "qmm_run_gate_up": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _c.c_int32, _c.c_int32, _P]),
+    "qmm_residual_rms_norm": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _c.c_int64, _c.c_float,
+                                         _c.c_int32, _P]),
     "qmm_debug_unpack": (_c.c_int, [_P, _P, _P, _P]),
     "qmm_get_stats": (_c.c_int, [_P, _P]),
     "qmm_last_error": (_c.c_char_p, []),
@@ -232,6 +234,30 @@ class Plan:
         return {"launches": {VARIANT_NAMES[i]: s.launches[i] for i in (1, 2, 3, 4, 5)},
                 "last_variant": VARIANT_NAMES.get(s.last_variant, "none"),
                 "last_ntw": s.last_ntw, "last_splitk": s.last_splitk, "last_grid": s.last_grid}
+
+
+def residual_rms_norm(x, update, weight, eps: float, residual=None, normalized=None,
+                      stream=None):
+    """(residual, normalized) of qmm_residual_rms_norm for [..., D] tensors."""
+    import torch
+    D = x.shape[-1]
+    rows = x.numel() // D
+    if update.shape != x.shape or weight.numel() != D:
+        raise ValueError("update must have x's shape and weight D=%d values" % D)
+    if update.dtype != x.dtype or weight.dtype != x.dtype:
+        raise ValueError("x, update and weight must share one dtype")
+    for t in (x, update, weight):
+        if not t.is_contiguous():
+            raise ValueError("x, update and weight must be contiguous")
+    if residual is None:
+        residual = torch.empty_like(x)
+    if normalized is None:
+        normalized = torch.empty_like(x)
+    dt = {torch.bfloat16: QMM_BF16, torch.float32: QMM_F32}.get(x.dtype, -1)
+    _check(lib().qmm_residual_rms_norm(_ptr(x), _ptr(update), _ptr(weight), _ptr(residual),
+                                       _ptr(normalized), rows, D, float(eps), dt,
+                                       _stream(stream)))
+    return residual, normalized
 
 
 def hbm_probe(buf, grid: int = 0, stream=None):

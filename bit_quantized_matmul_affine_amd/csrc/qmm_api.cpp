@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -550,6 +551,29 @@ qmm_status qmm_run_gate_up(const qmm_plan* p, const void* x, const void* gate_co
     p->last_splitk = 1;
     p->last_grid = grid;
   }
+  return QMM_OK;
+}
+
+qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* weight,
+                                 void* residual, void* normalized, int32_t rows, int64_t D,
+                                 float eps, int32_t dtype, void* stream) {
+  if (!x || !update || !weight || !residual || !normalized)
+    return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
+  if (!aligned(x, 16) || !aligned(update, 16) || !aligned(weight, 16) || !aligned(residual, 16) ||
+      !aligned(normalized, 16))
+    return fail(QMM_ERR_INVALID_ARG, "every buffer must be 16-byte aligned");
+  if (rows < 1) return fail(QMM_ERR_INVALID_ARG, "rows=%d must be >= 1", rows);
+  if (dtype != QMM_BF16 && dtype != QMM_F32)
+    return fail(QMM_ERR_INVALID_ARG, "dtype must be QMM_BF16 or QMM_F32");
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(QMM_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (!qmm::residual_rms_norm_supported(D))
+    return fail(QMM_ERR_UNSUPPORTED, "D=%lld: a multiple of 8 from 8 to 16384 is supported",
+                (long long)D);
+  if (hipError_t e = qmm::launch_residual_rms_norm(dtype == QMM_BF16, x, update, weight, residual,
+                                                   normalized, rows, (int)D, eps,
+                                                   reinterpret_cast<hipStream_t>(stream)))
+    return hip_fail(e, "kernel launch");
   return QMM_OK;
 }
 

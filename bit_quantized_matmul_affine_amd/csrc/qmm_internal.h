@@ -58,6 +58,12 @@ hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const
 bool resident_shape(int nC, int tm, int* nw, int* cpw);
 size_t resident_lds_bytes(int nw, int tm, int M, int K);
 constexpr int kResidentMaxSlots = 4;
+// Residual add + RMS normalization (qmm_norm.hip): D a multiple of 8, at most
+// 16384.
+bool residual_rms_norm_supported(long D);
+hipError_t launch_residual_rms_norm(bool bf16, const void* x, const void* update,
+                                    const void* weight, void* residual, void* normalized,
+                                    int rows, int D, float eps, hipStream_t st);
 // Fused gate/up through the resident kernel: tile pairs per workgroup (1 or
 // 2) that are built for cq chunks, and the launch.
 bool gate_up_shape(int nC, int pairs, int* nw, int* cpw);

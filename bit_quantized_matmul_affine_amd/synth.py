@@ -158,3 +158,14 @@ def small(seed: int, *, bits: int, K: int, N: int, M: int, x_dtype: str = "bf16"
     return draw(rng, name="small", bits=bits, K=K, N=N, M=M, x_dtype=x_dtype,
                 sb_dtype=sb_dtype or x_dtype, scale_lo=lo, scale_hi=hi, bias_c=c,
                 bias_sigma=sig)
+
+
+def norm_inputs(seed: int, rows: int, D: int, dtype: str = "bf16"):
+    """Seeded inputs of a residual add + RMS normalization, as stored arrays
+    (uint16 bf16 patterns or float32): hidden state x ~ N(0, 1) [rows, D],
+    block output update ~ N(0, 0.5^2) [rows, D], weight ~ 1 + N(0, 0.1^2) [D]."""
+    rng = np.random.default_rng(seed)
+    x = _store(rng.standard_normal((rows, D)), dtype)
+    update = _store(0.5 * rng.standard_normal((rows, D)), dtype)
+    weight = _store(1.0 + 0.1 * rng.standard_normal(D), dtype)
+    return x, update, weight

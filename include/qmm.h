@@ -176,6 +176,21 @@ qmm_status qmm_run_gate_up(const qmm_plan* plan, const void* x, const void* gate
                            const void* gate_sb, const void* up_codes, const void* up_sb,
                            void* h, int32_t rows, int32_t tile_pairs, void* stream);
 
+/* Residual add + RMS normalization producing the activations a projection
+ * consumes ("@mlx-bun/inference 0.0.0-stage -> 1.0.0" page, residual-rms-
+ * norm.ts).  Per row of D values, T = dtype (QMM_BF16 or QMM_F32), R = round
+ * to T (nearest, ties to even):
+ *   residual[i]   = R(x[i] + update[i])
+ *   normalized[i] = R(weight[i] * R(residual[i] / sqrt(mean_i residual^2 + eps)))
+ * with the sum of squares and the scaling in f32.  x, update, residual and
+ * normalized: T [rows, D] row-contiguous; weight: T [D]; all 16-byte aligned;
+ * residual and normalized must not overlap the inputs.  D: a multiple of 8,
+ * 8..16384 (else QMM_ERR_UNSUPPORTED); rows >= 1, eps finite and >= 0 (else
+ * QMM_ERR_INVALID_ARG).  Enqueued on `stream`; no plan, no workspace. */
+qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* weight,
+                                 void* residual, void* normalized, int32_t rows, int64_t D,
+                                 float eps, int32_t dtype, void* stream);
+
 /* Workspace needed by qmm_run_ex with the same variant/ntw/kwaves/splitk. */
 size_t qmm_workspace_bytes_ex(const qmm_plan* plan, int32_t variant, int32_t ntw,
                               int32_t kwaves, int32_t splitk, int32_t rows);

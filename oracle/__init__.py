@@ -19,4 +19,7 @@ from .oracle import (  # noqa: F401
     silu_mul_bf16,
     gate_up,
     gate_up_tolerance,
+    round_f32,
+    residual_rms_norm,
+    residual_rms_norm_tolerance,
 )

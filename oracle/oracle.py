@@ -217,3 +217,40 @@ def gate_up_tolerance(gate, up, tol_gate, tol_up) -> np.ndarray:
     return (1.1 * np.abs(up) * (tol_gate + 2.0 ** -8 * np.abs(gate))
             + np.abs(silu) * (tol_up + 2.0 ** -8 * np.abs(up))
             + 2.0 ** -6 * np.abs(silu * up) + 1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Residual add + RMS normalization ("@mlx-bun/inference 0.0.0-stage ->
+# 1.0.0" page, residual-rms-norm.ts): the residual sum is rounded to the
+# storage type before it is squared, the normalized value is rounded before
+# the weight multiplies it, and the product is stored in that type.
+
+def round_f32(v) -> np.ndarray:
+    """Round float64 values to the nearest float32 (ties to even), as float64."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def residual_rms_norm(x, update, weight, eps: float, dtype: str):
+    """(residual, normalized) in float64 for decoded inputs x, update [rows, D]
+    and weight [D]; dtype 'bf16' or 'f32' names the storage type T:
+        residual   = R(x + update)
+        normalized = R(weight * R(residual / sqrt(mean(residual^2) + eps)))
+    with R the rounding to T and everything else exact (float64)."""
+    R = round_bf16 if dtype == "bf16" else round_f32
+    x = np.asarray(x, dtype=np.float64)
+    update = np.asarray(update, dtype=np.float64)
+    weight = np.asarray(weight, dtype=np.float64)
+    res = R(x + update)
+    ms = np.mean(res * res, axis=-1, keepdims=True)
+    inv = 1.0 / np.sqrt(ms + float(np.float32(eps)))
+    return res, R(weight * R(res * inv))
+
+
+def residual_rms_norm_tolerance(normalized_ref, D: int, dtype: str) -> np.ndarray:
+    """Bound on |normalized - reference| for an implementation that sums the
+    squares in f32 in any order: that sum and the f32 square root are off by
+    at most about (D + 2) * 2^-24 relative, which can move R(residual * inv)
+    across one rounding step of T and the weighted product across another:
+    two steps of T (2^-7 relative for bf16) plus the f32 error itself."""
+    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    return np.abs(normalized_ref) * (2 * ulp + (D + 2) * 2.0 ** -24) + 1e-30
