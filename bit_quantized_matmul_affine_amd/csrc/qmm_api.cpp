@@ -49,7 +49,8 @@ struct Cfg {
   int nTB;        // tile blocks
   size_t lds;     // dynamic LDS bytes (GEMV, STREAM, RESIDENT, SLAB)
   int grid;       // RESIDENT, SLAB: workgroups
-  int cpw;        // RESIDENT: chunks of K per wave
+  int cpw;        // RESIDENT: chunks of K per wave; SLAB: slices per workgroup
+  bool split;     // SLAB: the split slab kernel (ntw = tiles per wave, wk = tile slots)
 };
 
 }  // namespace
@@ -191,6 +192,25 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.rows_per_launch = qmm::kMaxMfmaRows;
     const int r = std::min(rows, qmm::kMaxMfmaRows);
     c.tile_rows = r <= 16 ? 1 : (r <= 32 ? 2 : 4);
+    // the split slab kernel (ntw = 2 W tiles per compute wave, splitk = 2 K
+    // parts) by default for 33..64 rows, where the slab kernel's compute units
+    // each take in the whole activation block (measured 19.8 against 23 us at
+    // 64 rows of the 3-bit 5120x10240 workload; at 32 rows the slab kernel is
+    // faster, 12.5 against 13.6 us); ntw = 1 forces the slab kernel
+    const int tw = ntw_req ? ntw_req : (c.tile_rows == 4 ? 2 : 1);
+    const int S = s_req ? s_req : 2;
+    int ns = 0, nslot = 0;
+    if (c.tile_rows >= 2 && tw >= 2 && qmm::split_slab_shape(c.tile_rows, tw, nC, S, &ns, &nslot)) {
+      c.split = true;
+      c.ntw = tw;
+      c.wk = nslot;
+      c.cpw = ns;
+      c.S = S;
+      c.nTB = (nT + tw * nslot - 1) / (tw * nslot);
+      c.grid = c.nTB * S;
+      c.lds = qmm::split_slab_lds_bytes(c.tile_rows);
+      return c;
+    }
     c.cpw = qmm::slab_slices(c.tile_rows, nC);
     c.ntw = qmm::kSlabTiles;
     c.wk = 4;
@@ -264,6 +284,8 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
 
 size_t cfg_workspace(const qmm_plan* p, const Cfg& c, int rows) {
   if (c.S <= 1) return 0;
+  if (c.split)
+    return ticket_bytes(p) + qmm::split_slab_part_bytes(c.tile_rows, c.ntw, c.wk, c.nTB, c.S);
   const int r = std::min(rows, c.rows_per_launch);
   return ticket_bytes(p) + (size_t)c.S * r * p->d.N * sizeof(float);
 }
@@ -361,7 +383,10 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (variant == QMM_VARIANT_SLAB)
+    if (variant == QMM_VARIANT_SLAB && cb.split)
+      e = qmm::launch_split_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, cb.ntw, a, cb.grid, cb.lds,
+                                 st);
+    else if (variant == QMM_VARIANT_SLAB)
       e = qmm::launch_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, a, cb.grid, cb.lds, st);
     else if (variant == QMM_VARIANT_RESIDENT)
       e = qmm::launch_resident(p->d.bits, sf, cb.wk, cb.cpw, cb.ntw, a, cb.grid, cb.lds, st);

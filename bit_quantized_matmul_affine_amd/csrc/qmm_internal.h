@@ -74,6 +74,14 @@ hipError_t launch_gate_up(int bits, bool sb_f32, int nw, int cpw, int pairs, con
 constexpr int kSlabTiles = 3;
 int slab_slices(int mt, int nC);
 size_t slab_lds_bytes(int mt);
+// Split slab kernel: K cut into S (1 or 2) parts across workgroups, TW (2 or
+// 3) W tiles per compute wave, NSLOT tile slots; partial tiles of S = 2 go
+// through the workspace (tickets, then the part area).
+bool split_slab_shape(int mt, int tw, int nC, int S, int* ns, int* nslot);
+size_t split_slab_lds_bytes(int mt);
+size_t split_slab_part_bytes(int mt, int tw, int nslot, int groups, int S);
+hipError_t launch_split_slab(int bits, bool sb_f32, int mt, int ns, int tw, const LaunchArgs& a,
+                             int grid, size_t lds_bytes, hipStream_t st);
 hipError_t launch_slab(int bits, bool sb_f32, int mt, int ns, const LaunchArgs& a, int grid,
                        size_t lds_bytes, hipStream_t st);
 constexpr size_t kMaxLdsBytes = 160 * 1024;

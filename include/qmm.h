@@ -74,6 +74,10 @@ typedef enum {
   QMM_VARIANT_SLAB = 5      /* matrix-core kernel for 17..64 rows per pass: one workgroup per
                                compute unit owning three 16-row tiles of W, activations streamed
                                through an LDS ring in slices of 512 columns by loader waves;
+                               for 33..64 rows its split form: six tiles per workgroup, K cut
+                               in two across workgroups, partial tiles added through the
+                               workspace (ntw = 1 forces the unsplit form, ntw = 2 with
+                               splitk = 2 the split one at 17..32 rows too);
                                built for K = 5120 and 8192; bf16 activations */
 } qmm_variant;
 
@@ -146,10 +150,12 @@ qmm_status qmm_run(const qmm_plan* plan, const void* x, const void* codes, const
 
 /* qmm_run with a forced kernel family and launch shape, for tests and
  * measurement.  ntw: tiles of 16 rows of W per wavefront (1, 2, 4; for the
- * RESIDENT family: tiles a workgroup holds at once, 1..4; ignored by SLAB);
- * kwaves: wavefronts of a workgroup that split K between them (1, 2, 4;
- * MFMA family only); splitk: workgroups that split K, folded through the
- * workspace (>= 1).  Each may be 0 for the plan's choice. */
+ * RESIDENT family: tiles a workgroup holds at once, 1..4; for SLAB: 1 = the
+ * unsplit form, 2 = the split form where it is built for this K and splitk,
+ * else the unsplit form); kwaves: wavefronts of a workgroup that split K
+ * between them (1, 2, 4; MFMA family only); splitk: workgroups that split K,
+ * folded through the workspace (>= 1; SLAB's split form: 2).  Each may be 0
+ * for the plan's choice. */
 qmm_status qmm_run_ex(const qmm_plan* plan, int32_t variant, int32_t ntw, int32_t kwaves,
                       int32_t splitk, const void* x, const void* codes, const void* sb,
                       void* y, int32_t rows, void* workspace, size_t workspace_bytes,

@@ -272,6 +272,26 @@ def test_slab_parity(case):
     check_against_oracle(p, r.run(variant="slab"), label="slab %s" % (case,))
 
 
+@pytest.mark.parametrize("case", [(3, 5120, 208, 17, "bf16"), (4, 5120, 176, 32, "f32"),
+                                  (3, 5120, 96, 64, "bf16"), (4, 8192, 112, 40, "bf16"),
+                                  (3, 8192, 64, 29, "bf16")],
+                         ids=lambda c: "b%d_K%d_N%d_M%d_%s" % c)
+def test_slab_split_and_unsplit_forms(case):
+    """Both slab forms on one problem: the split form (six W tiles per
+    workgroup, K in two parts added through the workspace; ragged tile groups
+    where N/16 is not a multiple of 6) and the unsplit form, twice in a row so
+    the workspace's tickets are reused."""
+    bits, K, N, M, sd = case
+    p = synth.small(700 + M, bits=bits, K=K, N=N, M=M, sb_dtype=sd)
+    r = Runner(p)
+    for ntw, sk in ((2, 2), (1, 0), (2, 2)):
+        say("slab form ntw", ntw, "splitk", sk, case)
+        y = r.run(variant="slab", ntw=ntw, splitk=sk)
+        st = r.lin.plan.stats()
+        assert st["last_splitk"] == (2 if ntw == 2 else 1)
+        check_against_oracle(p, y, label="slab ntw=%d %s" % (ntw, case))
+
+
 def test_slab_rejects_unbuilt_k():
     p = synth.small(14, bits=4, K=1024, N=32, M=20)
     r = Runner(p)
