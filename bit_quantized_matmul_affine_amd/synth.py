@@ -169,3 +169,34 @@ def norm_inputs(seed: int, rows: int, D: int, dtype: str = "bf16"):
     update = _store(0.5 * rng.standard_normal((rows, D)), dtype)
     weight = _store(1.0 + 0.1 * rng.standard_normal(D), dtype)
     return x, update, weight
+
+
+def pack_lsb(codes: np.ndarray, bits: int) -> np.ndarray:
+    """uint32 words [..., D*bits/32] holding codes [..., D] (values < 2^bits),
+    32/bits per word, the first in the least significant bits."""
+    per = 32 // bits
+    c = codes.astype(np.uint64).reshape(codes.shape[:-1] + (codes.shape[-1] // per, per))
+    shifts = np.arange(per, dtype=np.uint64) * np.uint64(bits)
+    return np.bitwise_or.reduce(c << shifts, axis=-1).astype(np.uint32)
+
+
+def attention_inputs(seed: int, *, H: int, KV: int, N: int, D: int, bits: int,
+                     group_size: int):
+    """Seeded decode-attention inputs as stored arrays (bf16 as uint16):
+    q [H, D] ~ N(0, 1.4^2 / D) (scores of a few units); for keys and values,
+    per group of a row a range [lo, hi] with -lo, hi ~ 2 + 0.5|N(0, 1)|,
+    scale = (hi - lo) / (2^bits - 1), bias = lo (both bf16), codes uniform.
+    Returns q, (k_words, k_scales, k_biases), (v_words, v_scales, v_biases)."""
+    rng = np.random.default_rng(seed)
+    q = _store(rng.standard_normal((H, D)) * 1.4 / np.sqrt(D), "bf16")
+
+    def cache():
+        G = D // group_size
+        lo = -(2.0 + 0.5 * np.abs(rng.standard_normal((KV, N, G))))
+        hi = 2.0 + 0.5 * np.abs(rng.standard_normal((KV, N, G)))
+        scales = _store((hi - lo) / (2 ** bits - 1), "bf16")
+        biases = _store(lo, "bf16")
+        codes = rng.integers(0, 2 ** bits, size=(KV, N, D), dtype=np.int64)
+        return pack_lsb(codes, bits), scales, biases
+
+    return q, cache(), cache()

@@ -22,4 +22,8 @@ from .oracle import (  # noqa: F401
     round_f32,
     residual_rms_norm,
     residual_rms_norm_tolerance,
+    unpack_lsb,
+    dequant_rows,
+    decode_attention,
+    decode_attention_tolerance,
 )

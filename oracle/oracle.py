@@ -254,3 +254,91 @@ def residual_rms_norm_tolerance(normalized_ref, D: int, dtype: str) -> np.ndarra
     two steps of T (2^-7 relative for bf16) plus the f32 error itself."""
     ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
     return np.abs(normalized_ref) * (2 * ulp + (D + 2) * 2.0 ** -24) + 1e-30
+
+
+# ---------------------------------------------------------------------------
+# Decode attention over an affine-quantized KV cache ("mlx-bun 0.0.4" page,
+# fused-decode-kernel.ts): one query row per head attends to all N cached
+# rows of its KV head (head h reads KV head h // (H / KV)); keys and values
+# are stored like the weights (codes packed along D, least significant bits
+# first, one scale and bias per group of `group_size` values of a row).
+#   score[h, n] = R(sum_d q[h, d] * k[kv, n, d])      (rounded to bf16)
+#   out[h, :]   = R(sum_n e^score[h, n] * v[kv, n, :] / sum_n e^score[h, n])
+# with k = s*code + b and v likewise, R the rounding to bf16 and everything
+# else exact in float64.  No extra score scale: the query arrives scaled.
+
+def unpack_lsb(words, bits: int, D: int) -> np.ndarray:
+    """Codes [..., D] from uint32 words [..., D*bits/32], each word holding
+    32/bits codes with the first in its least significant bits."""
+    w = np.asarray(words, dtype=np.uint64)
+    per = 32 // bits
+    shifts = (np.arange(per, dtype=np.uint64) * np.uint64(bits))
+    codes = (w[..., :, None] >> shifts) & np.uint64((1 << bits) - 1)
+    return codes.reshape(w.shape[:-1] + (w.shape[-1] * per,))[..., :D].astype(np.int64)
+
+
+def dequant_rows(words, scales, biases, bits: int, D: int, group_size: int) -> np.ndarray:
+    """float64 values s*code + b of rows stored as words [..., D*bits/32] with
+    scales/biases [..., D/group_size] (decoded float64)."""
+    codes = unpack_lsb(words, bits, D).astype(np.float64)
+    s = np.repeat(np.asarray(scales, dtype=np.float64), group_size, axis=-1)
+    b = np.repeat(np.asarray(biases, dtype=np.float64), group_size, axis=-1)
+    return s * codes + b
+
+
+def decode_attention(q, k_words, k_scales, k_biases, v_words, v_scales, v_biases,
+                     bits: int, group_size: int, return_scores: bool = False):
+    """out [H, D] (float64 values of bf16 results) for decoded q [H, D] and a
+    cache of KV heads: words [KV, N, D*bits/32], scales/biases [KV, N, D/gs]."""
+    q = np.asarray(q, dtype=np.float64)
+    H, D = q.shape
+    KV = k_words.shape[0]
+    rep = H // KV
+    k = dequant_rows(k_words, k_scales, k_biases, bits, D, group_size)  # [KV, N, D]
+    v = dequant_rows(v_words, v_scales, v_biases, bits, D, group_size)
+    out = np.empty((H, D))
+    scores = np.empty((H, k.shape[1]))
+    for h in range(H):
+        kv = h // rep
+        s = round_bf16(k[kv] @ q[h])
+        e = np.exp(s - s.max())
+        out[h] = round_bf16((e @ v[kv]) / e.sum())
+        scores[h] = s
+    return (out, scores) if return_scores else out
+
+
+def decode_attention_tolerance(out_ref, q, k_words, k_scales, k_biases, v_words, v_scales,
+                               v_biases, bits: int, group_size: int) -> np.ndarray:
+    """Bound on |out - out_ref| for an implementation that sums the scores and
+    the weighted values in f32 in any order.  Score n's f32 sum is off by at
+    most eps_n = (D + 8) 2^-24 sum_d |q_d k_nd|, which moves its bf16 rounding
+    by at most delta_n = eps_n + 2^-7 (|score_n| + eps_n).  With softmax
+    weights w_n, shifting score n by at most delta_n scales w_n by at most
+    e^(delta_n + delta_w), delta_w = log sum_m w_m e^(delta_m) (the change of
+    the normaliser), so the unrounded output moves by at most
+    sum_n w_n (e^(delta_n + delta_w) - 1) |v_n - out|; the f32 sums of the
+    weights and weighted values add (N + 8) 2^-24 max|v|; the final bf16
+    rounding of either side adds one bf16 step, 2^-7 |out|."""
+    q = np.asarray(q, dtype=np.float64)
+    H, D = q.shape
+    KV = k_words.shape[0]
+    rep = H // KV
+    k = dequant_rows(k_words, k_scales, k_biases, bits, D, group_size)
+    v = dequant_rows(v_words, v_scales, v_biases, bits, D, group_size)
+    N = k.shape[1]
+    tol = np.empty((H, D))
+    for h in range(H):
+        kv = h // rep
+        sig = k[kv] @ q[h]
+        eps = (D + 8) * 2.0 ** -24 * (np.abs(k[kv]) @ np.abs(q[h]))
+        delta = eps + 2.0 ** -7 * (np.abs(sig) + eps)
+        s = round_bf16(sig)
+        w = np.exp(s - s.max())
+        w /= w.sum()
+        dw = np.log(np.sum(w * np.exp(delta)))
+        growth = w * np.expm1(delta + dw)                       # [N]
+        unrounded = (w @ v[kv])
+        move = growth @ np.abs(v[kv] - unrounded[None, :])      # [D]
+        vmax = np.max(np.abs(v[kv]), axis=0)
+        tol[h] = (2.0 ** -7 * np.abs(out_ref[h]) + move + (N + 8) * 2.0 ** -24 * vmax + 1e-6)
+    return tol

@@ -1,0 +1,145 @@
+"""Pins for the oracle's decode attention over an affine-quantized KV cache
+("mlx-bun 0.0.4" page, fused-decode-kernel.ts): closed forms (one cached row,
+equal scores, one dominant score), shift invariance of the softmax on inputs
+whose scores are exact, the head -> KV head mapping of grouped queries, the
+least-significant-first code order, and the score rounding."""
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_matmul_affine_amd import synth
+
+
+def _dec(raw):
+    return oracle.decode_bf16(raw)
+
+
+def _run(q, k, v, bits, gs, **kw):
+    return oracle.decode_attention(_dec(q), k[0], _dec(k[1]), _dec(k[2]), v[0], _dec(v[1]),
+                                   _dec(v[2]), bits, gs, **kw)
+
+
+def test_code_order_lsb_first():
+    # 8-bit: word 0x04030201 holds codes 1, 2, 3, 4; 4-bit: 0x87654321 holds 1..8
+    assert oracle.unpack_lsb(np.array([0x04030201], dtype=np.uint32), 8, 4).tolist() == [1, 2, 3, 4]
+    assert oracle.unpack_lsb(np.array([0x87654321], dtype=np.uint32), 4, 8).tolist() == list(range(1, 9))
+    codes = np.random.default_rng(0).integers(0, 16, (3, 64))
+    assert np.array_equal(oracle.unpack_lsb(synth.pack_lsb(codes, 4), 4, 64), codes)
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 64), (8, 32), (4, 128)])
+def test_one_row_returns_its_value(bits, gs):
+    # softmax over one row is 1: out = R(v_0) = R(s*code + b) for any query
+    q, k, v = synth.attention_inputs(1, H=4, KV=2, N=1, D=128, bits=bits, group_size=gs)
+    out = _run(q, k, v, bits, gs)
+    vals = oracle.dequant_rows(v[0], _dec(v[1]), _dec(v[2]), bits, 128, gs)  # [KV, 1, D]
+    for h in range(4):
+        assert np.array_equal(out[h], oracle.round_bf16(vals[h // 2, 0]))
+    # and by hand for one element: code of (kv 0, row 0, d 0) is the low bits of word 0
+    c0 = int(v[0][0, 0, 0]) & ((1 << bits) - 1)
+    s0, b0 = _dec(v[1])[0, 0, 0], _dec(v[2])[0, 0, 0]
+    assert out[0, 0] == oracle.round_bf16(s0 * c0 + b0)
+
+
+def test_equal_scores_average_the_values():
+    # a zero query gives every row score 0: out = R(mean_n v_n)
+    q, k, v = synth.attention_inputs(2, H=2, KV=1, N=37, D=64, bits=4, group_size=32)
+    q = np.zeros_like(q)
+    out = _run(q, k, v, 4, 32)
+    vals = oracle.dequant_rows(v[0], _dec(v[1]), _dec(v[2]), 4, 64, 32)
+    assert np.array_equal(out[0], oracle.round_bf16(vals[0].mean(axis=0)))
+    assert np.array_equal(out[1], out[0])
+
+
+def test_dominant_score_selects_its_row():
+    # keys equal to a constant c in every row but row 5, whose keys are c + 64:
+    # with q = 1 in every dim the score gap is 64 * D = 8192 (exp underflows)
+    D, N = 128, 9
+    kw = np.zeros((1, N, D // 8), dtype=np.uint32)
+    kw[0, 5] = synth.pack_lsb(np.full((1, D), 1), 4)[0]
+    ks = np.full((1, N, 2), synth.f32_to_bf16_bits(np.float32(64.0)), dtype=np.uint16)
+    kb = np.full((1, N, 2), synth.f32_to_bf16_bits(np.float32(0.5)), dtype=np.uint16)
+    q = np.full((1, D), synth.f32_to_bf16_bits(np.float32(1.0)), dtype=np.uint16)
+    _, _, v = synth.attention_inputs(3, H=1, KV=1, N=N, D=D, bits=4, group_size=64)
+    out, scores = _run(q, (kw, ks, kb), v, 4, 64, return_scores=True)
+    assert scores[0, 5] - scores[0, 0] == 64 * D
+    vals = oracle.dequant_rows(v[0], _dec(v[1]), _dec(v[2]), 4, D, 64)
+    assert np.array_equal(out[0], oracle.round_bf16(vals[0, 5]))
+
+
+def _exact_score_inputs(seed, shift_codes=0):
+    """Small integer queries and codes with unit scales: every score is a
+    small integer (exact in bf16), so the softmax sees exact scores."""
+    rng = np.random.default_rng(seed)
+    D, N = 64, 20
+    qv = rng.integers(-2, 3, (2, D)).astype(np.float32)
+    q = synth.f32_to_bf16_bits(qv)
+    codes = rng.integers(0, 4, (1, N, D))
+    ks = np.full((1, N, 1), synth.f32_to_bf16_bits(np.float32(0.25)), dtype=np.uint16)
+    kb = np.full((1, N, 1), synth.f32_to_bf16_bits(np.float32(shift_codes)), dtype=np.uint16)
+    _, _, v = synth.attention_inputs(seed, H=2, KV=1, N=N, D=D, bits=4, group_size=64)
+    return q, (synth.pack_lsb(codes, 4), ks, kb), v, qv
+
+
+def test_softmax_shift_invariance_on_exact_scores():
+    # raising every key by b adds b * sum_d q_d to every score of a head
+    q, k0, v, qv = _exact_score_inputs(4, 0)
+    _, k1, _, _ = _exact_score_inputs(4, 2)
+    out0, s0 = _run(q, k0, v, 4, 64, return_scores=True)
+    out1, s1 = _run(q, k1, v, 4, 64, return_scores=True)
+    shift = 2 * qv.sum(axis=1, dtype=np.float64)
+    assert np.array_equal(s1 - s0, np.repeat(shift[:, None], s0.shape[1], axis=1))
+    assert np.array_equal(out0, out1)
+
+
+def test_grouped_query_heads_map_to_kv_head_h_div_rep():
+    # 4 query heads over 2 KV heads, one query for all: heads 0, 1 read KV
+    # head 0 and heads 2, 3 read KV head 1 (h % KV would pair 0 with 2)
+    q, k, v = synth.attention_inputs(5, H=4, KV=2, N=16, D=64, bits=8, group_size=64)
+    q[:] = q[0]
+    out = _run(q, k, v, 8, 64)
+    assert np.array_equal(out[1], out[0])
+    assert np.array_equal(out[3], out[2])
+    assert not np.array_equal(out[2], out[0])
+
+
+def test_scores_are_rounded_to_bf16():
+    q, k, v = synth.attention_inputs(6, H=2, KV=1, N=50, D=128, bits=4, group_size=64)
+    _, scores = _run(q, k, v, 4, 64, return_scores=True)
+    assert np.array_equal(scores, oracle.round_bf16(scores))
+    kf = oracle.dequant_rows(k[0], _dec(k[1]), _dec(k[2]), 4, 128, 64)
+    exact = kf[0] @ _dec(q)[0]
+    assert np.array_equal(scores[0], oracle.round_bf16(exact))
+    assert not np.array_equal(scores[0], exact)  # the rounding is not a no-op here
+
+
+def test_tolerance_is_small_for_typical_inputs():
+    q, k, v = synth.attention_inputs(7, H=2, KV=1, N=256, D=256, bits=4, group_size=64)
+    args = (_dec(q), k[0], _dec(k[1]), _dec(k[2]), v[0], _dec(v[1]), _dec(v[2]), 4, 64)
+    out = oracle.decode_attention(*args)
+    tol = oracle.decode_attention_tolerance(out, *args)
+    assert np.all(tol > 0) and np.median(tol) < 0.2
+
+
+def test_tolerance_covers_every_score_rounding_flip():
+    """Brute force on a tiny case: move every score by -1, 0 or +1 bf16 step
+    (all 3^6 combinations) and recompute the unrounded output exactly; the
+    change must stay inside the bound less its final-rounding term."""
+    import itertools
+    q, k, v = synth.attention_inputs(8, H=1, KV=1, N=6, D=32, bits=4, group_size=32)
+    args = (_dec(q), k[0], _dec(k[1]), _dec(k[2]), v[0], _dec(v[1]), _dec(v[2]), 4, 32)
+    out, scores = oracle.decode_attention(*args, return_scores=True)
+    tol = oracle.decode_attention_tolerance(out, *args)[0] - 2.0 ** -7 * np.abs(out[0])
+    vals = oracle.dequant_rows(v[0], _dec(v[1]), _dec(v[2]), 4, 32, 32)[0]
+    s = scores[0]
+    step = 2.0 ** (np.floor(np.log2(np.abs(s))) - 7)  # one bf16 step at each score
+    def unrounded(sc):
+        e = np.exp(sc - sc.max())
+        return (e @ vals) / e.sum()
+    base = unrounded(s)
+    worst = 0.0
+    for signs in itertools.product((-1, 0, 1), repeat=6):
+        moved = unrounded(s + np.array(signs) * step)
+        worst = max(worst, float(np.max(np.abs(moved - base) / tol)))
+    assert worst <= 1.0
+    assert worst > 0.05  # the bound is not vacuous: a flip uses a visible part of it
