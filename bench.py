@@ -212,6 +212,46 @@ def time_norm(torch, binding, synth, rows, D, reps=5):
             "frac_of_8TBps": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
+def time_attention(torch, binding, synth, H, KV, N, D, bits, gs, reps=5):
+    """Mean us per decode-attention call (qmm_decode_attention, both kernels)
+    over a cache of KV heads x N rows; algorithmic bytes: the key and value
+    codes, scales and biases once, plus q and the output."""
+    q, k, v = synth.attention_inputs(13, H=H, KV=KV, N=N, D=D, bits=bits, group_size=gs)
+    qd = binding.to_device(q)
+    kd = tuple(binding.to_device(x) for x in k)
+    vd = tuple(binding.to_device(x) for x in v)
+    out = torch.empty_like(qd)
+    need = binding.lib().qmm_attention_workspace_bytes(H, N, D)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    n = 32
+
+    def calls():
+        for _ in range(n):
+            binding.decode_attention(qd, kd, vd, bits, gs, out=out, workspace=ws)
+
+    calls()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    g.replay()
+    torch.cuda.synchronize()
+    d = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        d.append(e0.elapsed_time(e1) * 1e3 / n)
+    del g
+    us = sum(d) / len(d)
+    nbytes = sum(x.nbytes for x in k) + sum(x.nbytes for x in v) + 2 * q.nbytes
+    return {"us": round(us, 3), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_8TBps": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": "cache %.1f MB stays in the 256 MB last-level cache across calls" % (nbytes / 1e6)}
+
+
 def other_workloads(torch, binding, synth, probe):
     """The remaining configurations, each cold-read as above."""
     out = {}
@@ -251,6 +291,11 @@ def other_workloads(torch, binding, synth, probe):
     out["residual add + RMS norm, bf16"] = {
         "4x3840 (decode)": time_norm(torch, binding, synth, 4, 3840),
         "16384x5120 (HBM-bound)": time_norm(torch, binding, synth, 16384, 5120)}
+    out["decode attention over a 4-bit group-64 KV cache, bf16"] = {
+        "16 heads / 8 KV heads, D=256, N=8192": time_attention(torch, binding, synth, 16, 8, 8192,
+                                                               256, 4, 64),
+        "16 heads / 8 KV heads, D=256, N=32768": time_attention(torch, binding, synth, 16, 8,
+                                                                32768, 256, 4, 64)}
     (p0,) = synth.workload(0)
     us, v = time_workload(torch, binding, p0, 1)
     out["4-bit 512->512, 1 row, f32 (launch-bound)"] = {"us": round(us, 3), "variant": v}

@@ -37,6 +37,10 @@ SIGNATURES = {
     "qmm_workspace_bytes": (_c.c_size_t, [_P, _c.c_int32]),
     "qmm_workspace_bytes_ex": (_c.c_size_t, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32,
                                               _c.c_int32]),
+    "qmm_attention_workspace_bytes": (_c.c_size_t, [_c.c_int32, _c.c_int64, _c.c_int32]),
+    "qmm_decode_attention": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _c.c_int32, _c.c_int32,
+                                        _c.c_int64, _c.c_int32, _c.c_int32, _c.c_int32, _P,
+                                        _c.c_size_t, _P]),
     "qmm_run": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _P, _c.c_size_t, _P]),
     "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P,
                               _P, _c.c_int32, _P, _c.c_size_t, _P]),
@@ -258,6 +262,32 @@ def residual_rms_norm(x, update, weight, eps: float, residual=None, normalized=N
                                        _ptr(normalized), rows, D, float(eps), dt,
                                        _stream(stream)))
     return residual, normalized
+
+
+def decode_attention(q, k_cache, v_cache, bits: int, group_size: int, out=None,
+                     workspace=None, stream=None):
+    """out [H, D] of qmm_decode_attention; q bf16 [H, D]; k_cache and v_cache
+    are (words int32 [KV, N, D*bits/32], scales bf16 [KV, N, D/gs], biases)."""
+    import torch
+    H, D = q.shape
+    kw, ks, kb = k_cache
+    vw, vs, vb = v_cache
+    KV, N = kw.shape[0], kw.shape[1]
+    for t in (q, kw, ks, kb, vw, vs, vb):
+        if not t.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+    if q.dtype != torch.bfloat16 or ks.dtype != torch.bfloat16 or vs.dtype != torch.bfloat16:
+        raise ValueError("q, scales and biases must be bfloat16")
+    if out is None:
+        out = torch.empty_like(q)
+    need = lib().qmm_attention_workspace_bytes(H, N, D)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().qmm_decode_attention(_ptr(q), _ptr(kw), _ptr(ks), _ptr(kb), _ptr(vw), _ptr(vs),
+                                      _ptr(vb), _ptr(out), H, KV, N, D, bits, group_size,
+                                      _ptr(workspace), wsb, _stream(stream)))
+    return out
 
 
 def hbm_probe(buf, grid: int = 0, stream=None):

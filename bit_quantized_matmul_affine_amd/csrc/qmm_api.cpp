@@ -602,6 +602,68 @@ qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* 
   return QMM_OK;
 }
 
+size_t qmm_attention_workspace_bytes(int32_t H, int64_t N, int32_t D) {
+  if (H < 1 || N < 1 || D < 1) return 0;
+  const int64_t G = (N + qmm::kAttnBlock - 1) / qmm::kAttnBlock;
+  if (G <= 1) return 0;
+  return (size_t)H * G * (D + 2) * sizeof(float);
+}
+
+qmm_status qmm_decode_attention(const void* q, const uint32_t* k_words, const void* k_scales,
+                                const void* k_biases, const uint32_t* v_words,
+                                const void* v_scales, const void* v_biases, void* out, int32_t H,
+                                int32_t KV, int64_t N, int32_t D, int32_t bits,
+                                int32_t group_size, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!q || !k_words || !k_scales || !k_biases || !v_words || !v_scales || !v_biases || !out)
+    return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
+  if (!aligned(k_words, 16) || !aligned(v_words, 16) || !aligned(q, 4) || !aligned(out, 4) ||
+      !aligned(k_scales, 2) || !aligned(k_biases, 2) || !aligned(v_scales, 2) ||
+      !aligned(v_biases, 2))
+    return fail(QMM_ERR_INVALID_ARG, "code words must be 16-byte aligned, q and out 4-byte aligned");
+  if (H < 1 || KV < 1 || H % KV != 0)
+    return fail(QMM_ERR_INVALID_ARG, "H=%d must be a positive multiple of KV=%d", H, KV);
+  if (N < 1) return fail(QMM_ERR_INVALID_ARG, "N=%lld: the cache must hold a row", (long long)N);
+  if (bits != 4 && bits != 8) return fail(QMM_ERR_UNSUPPORTED, "bits=%d: 4 and 8 are supported", bits);
+  if (group_size != 32 && group_size != 64 && group_size != 128)
+    return fail(QMM_ERR_UNSUPPORTED, "group_size=%d: 32, 64 and 128 are supported", group_size);
+  const int rep = H / KV;
+  if (!qmm::attention_supported(D, rep))
+    return fail(QMM_ERR_UNSUPPORTED,
+                "D=%d with %d query heads per KV head: D in {128, 256, 512}, heads per KV head "
+                "in {1, 2, 4, 8}, their product <= 1024", D, rep);
+  if (N > (int64_t)qmm::kAttnMaxBlocks * qmm::kAttnBlock || (int64_t)KV * N > (1LL << 31))
+    return fail(QMM_ERR_UNSUPPORTED, "N=%lld: at most %d cached rows per head are supported",
+                (long long)N, qmm::kAttnMaxBlocks * qmm::kAttnBlock);
+  const int64_t G = (N + qmm::kAttnBlock - 1) / qmm::kAttnBlock;
+  const size_t need = qmm_attention_workspace_bytes(H, N, D);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16)) return fail(QMM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  qmm::AttnArgs a{};
+  a.q = q;
+  a.kw = k_words;
+  a.ks = k_scales;
+  a.kb = k_biases;
+  a.vw = v_words;
+  a.vs = v_scales;
+  a.vb = v_biases;
+  a.out = out;
+  a.opart = need ? static_cast<float*>(workspace) : nullptr;
+  a.stats = need ? static_cast<float*>(workspace) + (size_t)H * G * D : nullptr;
+  a.H = H;
+  a.KV = KV;
+  a.N = (int)N;
+  a.GS = group_size;
+  a.G = (int)G;
+  if (hipError_t e = qmm::launch_attention(bits, D, rep, a, reinterpret_cast<hipStream_t>(stream)))
+    return hip_fail(e, "attention launch");
+  return QMM_OK;
+}
+
 qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, void* stream) {
   if (qmm_status st = check_plan(p)) return st;
   if (!codes || !out) return fail(QMM_ERR_INVALID_ARG, "NULL pointer");

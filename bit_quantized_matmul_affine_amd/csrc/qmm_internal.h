@@ -60,6 +60,28 @@ size_t resident_lds_bytes(int nw, int tm, int M, int K);
 constexpr int kResidentMaxSlots = 4;
 // Residual add + RMS normalization (qmm_norm.hip): D a multiple of 8, at most
 // 16384.
+// Decode attention over an affine-quantized KV cache: kAttnBlock cached rows
+// per workgroup of the block kernel; partial outputs [H, G, D] and
+// (max, sum) pairs [H, G, 2] of G = ceil(N / kAttnBlock) blocks in the
+// workspace when G > 1.
+constexpr int kAttnBlock = 128;
+constexpr int kAttnMaxBlocks = 8192;  // merge weights in LDS: 32 KB
+struct AttnArgs {
+  const void* q;         // bf16 [H, D]
+  const uint32_t* kw;    // [KV, N, D*bits/32]
+  const void* ks;        // bf16 [KV, N, D/GS]
+  const void* kb;
+  const uint32_t* vw;
+  const void* vs;
+  const void* vb;
+  void* out;             // bf16 [H, D]
+  float* opart;          // [H, G, D]
+  float* stats;          // [H, G, 2]
+  int H, KV, N, GS, G;
+};
+bool attention_supported(int D, int rep);
+hipError_t launch_attention(int bits, int D, int rep, const AttnArgs& a, hipStream_t st);
+
 bool residual_rms_norm_supported(long D);
 hipError_t launch_residual_rms_norm(bool bf16, const void* x, const void* update,
                                     const void* weight, void* residual, void* normalized,

@@ -197,6 +197,34 @@ qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* 
                                  void* residual, void* normalized, int32_t rows, int64_t D,
                                  float eps, int32_t dtype, void* stream);
 
+/* Decode attention over an affine-quantized KV cache ("mlx-bun 0.0.4" page,
+ * fused-decode-kernel.ts): one query row per head, head h attending to all N
+ * cached rows of KV head h / (H / KV).  Keys and values are stored like MLX
+ * affine weights: k_words/v_words uint32 [KV, N, D*bits/32], codes packed
+ * along D least significant bits first; k_scales, k_biases, v_scales,
+ * v_biases bf16 [KV, N, D/group_size]; value = scale * code + bias.
+ *   score[h, n] = bf16(q[h] . k[kv, n])      (no extra scale: q arrives scaled)
+ *   out[h]      = bf16(sum_n e^score[h, n] v[kv, n] / sum_n e^score[h, n])
+ * with every sum in f32.  q, out: bf16 [H, D]; all buffers device memory,
+ * row-contiguous, borrowed until the enqueued work completes; code words
+ * 16-byte aligned.  The cache is split into blocks of 128 rows whose partial
+ * results are merged in block order (bitwise reproducible).  workspace: >=
+ * qmm_attention_workspace_bytes(H, N, D) bytes (none when N <= 128; no
+ * zero-fill needed).  Errors: QMM_ERR_INVALID_ARG for NULL or misaligned
+ * pointers, N < 1 or H not a multiple of KV; QMM_ERR_UNSUPPORTED for bits
+ * other than 4 and 8, group sizes other than 32, 64, 128, D outside
+ * {128, 256, 512} or H/KV outside {1, 2, 4, 8} or D * H/KV > 1024, or N
+ * above 2^20 rows;
+ * QMM_ERR_WORKSPACE for a missing or short workspace; QMM_ERR_HIP for launch
+ * failures.  Enqueued on `stream`. */
+size_t qmm_attention_workspace_bytes(int32_t H, int64_t N, int32_t D);
+qmm_status qmm_decode_attention(const void* q, const uint32_t* k_words, const void* k_scales,
+                                const void* k_biases, const uint32_t* v_words,
+                                const void* v_scales, const void* v_biases, void* out, int32_t H,
+                                int32_t KV, int64_t N, int32_t D, int32_t bits,
+                                int32_t group_size, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
 /* Workspace needed by qmm_run_ex with the same variant/ntw/kwaves/splitk. */
 size_t qmm_workspace_bytes_ex(const qmm_plan* plan, int32_t variant, int32_t ntw,
                               int32_t kwaves, int32_t splitk, int32_t rows);

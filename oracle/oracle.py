@@ -309,10 +309,15 @@ def decode_attention(q, k_words, k_scales, k_biases, v_words, v_scales, v_biases
 
 def decode_attention_tolerance(out_ref, q, k_words, k_scales, k_biases, v_words, v_scales,
                                v_biases, bits: int, group_size: int) -> np.ndarray:
-    """Bound on |out - out_ref| for an implementation that sums the scores and
-    the weighted values in f32 in any order.  Score n's f32 sum is off by at
-    most eps_n = (D + 8) 2^-24 sum_d |q_d k_nd|, which moves its bf16 rounding
-    by at most delta_n = eps_n + 2^-7 (|score_n| + eps_n).  With softmax
+    """Bound on |out - out_ref| for an implementation whose score sums chain at
+    most D/16 + 8 f32 roundings per term (sums over slices of D/16 values,
+    then a tree over the slices and the affine step), in the factored form
+    that offsets each code by up to 2176 (an 8-bit code as two nibbles
+    offset by 128, the high one against 16 q, before the slice's offset is
+    removed with its sum of q): terms are at most |q_d| (|k_nd| + 2560
+    |scale_nd|), so score n's sum is off by at most
+    eps_n = (D/16 + 8) 2^-24 sum_d |q_d| (|k_nd| + 2560 |scale_nd|), which
+    moves its bf16 rounding by at most delta_n = eps_n + 2^-7 (|score_n| + eps_n).  With softmax
     weights w_n, shifting score n by at most delta_n scales w_n by at most
     e^(delta_n + delta_w), delta_w = log sum_m w_m e^(delta_m) (the change of
     the normaliser), so the unrounded output moves by at most
@@ -330,7 +335,8 @@ def decode_attention_tolerance(out_ref, q, k_words, k_scales, k_biases, v_words,
     for h in range(H):
         kv = h // rep
         sig = k[kv] @ q[h]
-        eps = (D + 8) * 2.0 ** -24 * (np.abs(k[kv]) @ np.abs(q[h]))
+        ksc = np.repeat(np.abs(np.asarray(k_scales, dtype=np.float64)[kv]), group_size, axis=-1)
+        eps = (D / 16 + 8) * 2.0 ** -24 * ((np.abs(k[kv]) + 2560.0 * ksc) @ np.abs(q[h]))
         delta = eps + 2.0 ** -7 * (np.abs(sig) + eps)
         s = round_bf16(sig)
         w = np.exp(s - s.max())
