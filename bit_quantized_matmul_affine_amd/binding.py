@@ -19,10 +19,11 @@ LIB_PATH = os.path.join(_PKG, "libqmm.so")
 QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED = 0, -1, -2
 QMM_ERR_HIP, QMM_ERR_WORKSPACE, QMM_ERR_NO_DEVICE = -3, -4, -5
 QMM_F32, QMM_BF16 = 0, 1
-VARIANT_AUTO, VARIANT_GEMV, VARIANT_MFMA, VARIANT_STREAM, VARIANT_RESIDENT, VARIANT_SLAB = (
-    0, 1, 2, 3, 4, 5)
+(VARIANT_AUTO, VARIANT_GEMV, VARIANT_MFMA, VARIANT_STREAM, VARIANT_RESIDENT, VARIANT_SLAB,
+ VARIANT_GENERIC) = (0, 1, 2, 3, 4, 5, 6)
 VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "mfma": VARIANT_MFMA,
-            "stream": VARIANT_STREAM, "resident": VARIANT_RESIDENT, "slab": VARIANT_SLAB}
+            "stream": VARIANT_STREAM, "resident": VARIANT_RESIDENT, "slab": VARIANT_SLAB,
+            "generic": VARIANT_GENERIC}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 _DTYPES = {"f32": QMM_F32, "bf16": QMM_BF16}
 
@@ -62,7 +63,7 @@ class QmmDesc(ctypes.Structure):
 
 
 class QmmStats(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_uint64 * 6), ("last_variant", ctypes.c_int32),
+    _fields_ = [("launches", ctypes.c_uint64 * 8), ("last_variant", ctypes.c_int32),
                 ("last_ntw", ctypes.c_int32), ("last_splitk", ctypes.c_int32),
                 ("last_grid", ctypes.c_int32)]
 
@@ -235,7 +236,7 @@ class Plan:
     def stats(self) -> dict:
         s = QmmStats()
         _check(lib().qmm_get_stats(self._h, ctypes.byref(s)))
-        return {"launches": {VARIANT_NAMES[i]: s.launches[i] for i in (1, 2, 3, 4, 5)},
+        return {"launches": {VARIANT_NAMES[i]: s.launches[i] for i in (1, 2, 3, 4, 5, 6)},
                 "last_variant": VARIANT_NAMES.get(s.last_variant, "none"),
                 "last_ntw": s.last_ntw, "last_splitk": s.last_splitk, "last_grid": s.last_grid}
 
@@ -306,7 +307,8 @@ class QuantizedLinear:
     def __init__(self, problem_or_shape, w=None, scales=None, biases=None, max_rows=None,
                  device="cuda"):
         p = problem_or_shape
-        self.plan = Plan(p.bits, p.K, p.N, max_rows or max(p.M, 1), p.x_dtype, p.sb_dtype)
+        self.plan = Plan(p.bits, p.K, p.N, max_rows or max(p.M, 1), p.x_dtype, p.sb_dtype,
+                         group_size=getattr(p, "group_size", 64))
         wd = to_device(p.w if w is None else w, device)
         sd = to_device(p.scales if scales is None else scales, device)
         bd = to_device(p.biases if biases is None else biases, device)

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmm.so")
-SOURCES = ["qmm_kernels.hip", "qmm_norm.hip", "qmm_attention.hip", "qmm_api.cpp"]
+SOURCES = ["qmm_kernels.hip", "qmm_norm.hip", "qmm_attention.hip", "qmm_generic.hip", "qmm_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -60,7 +60,8 @@ struct qmm_plan {
   int nT, nC;
   int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
   int env_ntw, env_splitk, env_kwaves;
-  mutable std::atomic<uint64_t> launches[6];
+  mutable std::atomic<uint64_t> launches[8];
+  bool generic;  // not 3/4-bit group 64: MLX's own layout and the generic kernel
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
 };
 
@@ -136,6 +137,7 @@ size_t stream_max_lds(const qmm_plan* p) {
 }
 
 int pick_variant(const qmm_plan* p, int rows, int forced) {
+  if (p->generic) return QMM_VARIANT_GENERIC;
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
   if (p->force_variant) return p->force_variant;
@@ -186,6 +188,16 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.nTB = c.grid;
     c.S = 1;
     c.lds = qmm::resident_lds_bytes(nw, tm, r, (int)p->d.K);
+    return c;
+  }
+  if (variant == QMM_VARIANT_GENERIC) {
+    c.rows_per_launch = qmm::kGenericMaxRows;
+    c.tile_rows = std::min(rows, qmm::kGenericMaxRows);
+    c.ntw = 1;
+    c.wk = 1;
+    c.S = 1;
+    c.nTB = nT;
+    c.grid = nT;
     return c;
   }
   if (variant == QMM_VARIANT_SLAB) {
@@ -324,8 +336,15 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   if (!x || !codes || !sb || !y) return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(sb, 16) || !aligned(y, 4))
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
-  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_SLAB)
+  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_GENERIC)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
+  if (p->generic && variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GENERIC)
+    return fail(QMM_ERR_UNSUPPORTED,
+                "bits=%d group_size=%d run only on the generic kernel (QMM_VARIANT_GENERIC)",
+                p->d.bits, p->d.group_size);
+  if (!p->generic && variant_req == QMM_VARIANT_GENERIC)
+    return fail(QMM_ERR_UNSUPPORTED,
+                "3- and 4-bit group-64 plans use the native layout, not the generic kernel");
   if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM ||
        variant_req == QMM_VARIANT_RESIDENT ||
        variant_req == QMM_VARIANT_SLAB) &&
@@ -383,7 +402,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (variant == QMM_VARIANT_SLAB && cb.split)
+    if (variant == QMM_VARIANT_GENERIC)
+      e = qmm::launch_generic(p->d.bits, p->d.group_size, xf, sf, rb, a, st);
+    else if (variant == QMM_VARIANT_SLAB && cb.split)
       e = qmm::launch_split_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, cb.ntw, a, cb.grid, cb.lds,
                                  st);
     else if (variant == QMM_VARIANT_SLAB)
@@ -431,9 +452,8 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
       (d->sb_dtype != QMM_F32 && d->sb_dtype != QMM_BF16))
     return fail(QMM_ERR_INVALID_ARG, "unknown dtype");
   if (d->flags != 0) return fail(QMM_ERR_INVALID_ARG, "flags must be 0");
-  if (b != 3 && b != 4) return fail(QMM_ERR_UNSUPPORTED, "bits=%d: only 3 and 4 are implemented", b);
-  if (d->group_size != 64)
-    return fail(QMM_ERR_UNSUPPORTED, "group_size=%d: only 64 is implemented", d->group_size);
+  if (b != 2 && b != 3 && b != 4 && b != 8)
+    return fail(QMM_ERR_UNSUPPORTED, "bits=%d: 2, 3, 4 and 8 are implemented", b);
   if (d->K % qmm::kChunkK != 0)
     return fail(QMM_ERR_UNSUPPORTED, "K=%lld: must be a multiple of %d", (long long)d->K, qmm::kChunkK);
   if (d->N % qmm::kTileN != 0)
@@ -444,6 +464,7 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
   qmm_plan* p = new (std::nothrow) qmm_plan();
   if (!p) return fail(QMM_ERR_INVALID_ARG, "out of host memory");
   p->d = *d;
+  p->generic = !((b == 3 || b == 4) && d->group_size == 64);
   p->nT = (int)(d->N / qmm::kTileN);
   p->nC = (int)(d->K / qmm::kChunkK);
   p->force_variant = 0;
@@ -472,7 +493,7 @@ qmm_status qmm_packed_bytes(const qmm_plan* p, size_t* codes_bytes, size_t* sb_b
   if (qmm_status st = check_plan(p)) return st;
   if (!codes_bytes || !sb_bytes) return fail(QMM_ERR_INVALID_ARG, "NULL output pointer");
   *codes_bytes = (size_t)p->d.N * p->d.K * p->d.bits / 8;
-  *sb_bytes = (size_t)2 * p->d.N * (p->d.K / 64) * (p->d.sb_dtype == QMM_F32 ? 4 : 2);
+  *sb_bytes = (size_t)2 * p->d.N * (p->d.K / p->d.group_size) * (p->d.sb_dtype == QMM_F32 ? 4 : 2);
   return QMM_OK;
 }
 
@@ -485,6 +506,18 @@ qmm_status qmm_prepack(const qmm_plan* p, const uint32_t* w, const void* scales,
       !aligned(scales, p->d.sb_dtype == QMM_F32 ? 4 : 2) ||
       !aligned(biases, p->d.sb_dtype == QMM_F32 ? 4 : 2))
     return fail(QMM_ERR_INVALID_ARG, "misaligned pointer");
+  if (p->generic) {
+    // MLX's layout as it is: the codes, then the scales and biases as planes
+    const size_t cb = (size_t)p->d.N * p->d.K * p->d.bits / 8;
+    const size_t pb = (size_t)p->d.N * (p->d.K / p->d.group_size) * (p->d.sb_dtype == QMM_F32 ? 4 : 2);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(codes_out, w, cb, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(sb_out, scales, pb, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(static_cast<char*>(sb_out) + pb, biases, pb, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "prepack copy");
+    return QMM_OK;
+  }
   hipError_t e = qmm::launch_repack(p->d.bits, p->d.sb_dtype == QMM_F32, w, scales, biases,
                                     static_cast<uint32_t*>(codes_out), sb_out, (int)p->d.N,
                                     (int)p->d.K, reinterpret_cast<hipStream_t>(stream));
@@ -534,6 +567,8 @@ qmm_status qmm_run_gate_up(const qmm_plan* p, const void* x, const void* gate_co
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, h 4-byte aligned");
   if (p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up kernel takes bf16 activations");
+  if (p->generic)
+    return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up kernel takes 3- and 4-bit group-64 weights");
   if (tile_pairs < 0 || tile_pairs > 2)
     return fail(QMM_ERR_INVALID_ARG, "tile_pairs must be 0 (plan's choice), 1 or 2");
   const int nT = p->nT, nC = p->nC;
@@ -666,6 +701,8 @@ qmm_status qmm_decode_attention(const void* q, const uint32_t* k_words, const vo
 
 qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, void* stream) {
   if (qmm_status st = check_plan(p)) return st;
+  if (p->generic)
+    return fail(QMM_ERR_UNSUPPORTED, "the generic kernel keeps MLX's layout: nothing to unpack");
   if (!codes || !out) return fail(QMM_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(codes, 4)) return fail(QMM_ERR_INVALID_ARG, "misaligned codes");
   hipError_t e = qmm::launch_debug_unpack(p->d.bits, static_cast<const uint32_t*>(codes), out,
@@ -678,7 +715,7 @@ qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, 
 qmm_status qmm_get_stats(const qmm_plan* p, qmm_stats* out) {
   if (qmm_status st = check_plan(p)) return st;
   if (!out) return fail(QMM_ERR_INVALID_ARG, "out is NULL");
-  for (int i = 0; i < 6; ++i) out->launches[i] = p->launches[i].load();
+  for (int i = 0; i < 8; ++i) out->launches[i] = p->launches[i].load();
   out->last_variant = p->last_variant;
   out->last_ntw = p->last_ntw;
   out->last_splitk = p->last_splitk;

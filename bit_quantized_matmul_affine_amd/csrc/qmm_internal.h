@@ -60,6 +60,13 @@ size_t resident_lds_bytes(int nw, int tm, int M, int K);
 constexpr int kResidentMaxSlots = 4;
 // Residual add + RMS normalization (qmm_norm.hip): D a multiple of 8, at most
 // 16384.
+// Format variants (bits 2, 3, 4, 8; groups of 32, 64, 128) on MLX's own
+// layout: codes as given, scales then biases as two [N, K/gs] planes; up to
+// kGenericMaxRows activation rows per launch; N a multiple of 16.
+constexpr int kGenericMaxRows = 2;
+hipError_t launch_generic(int bits, int group_size, bool x_f32, bool sb_f32, int rows,
+                          const LaunchArgs& a, hipStream_t st);
+
 // Decode attention over an affine-quantized KV cache: kAttnBlock cached rows
 // per workgroup of the block kernel; partial outputs [H, G, D] and
 // (max, sum) pairs [H, G, 2] of G = ceil(N / kAttnBlock) blocks in the

@@ -64,26 +64,28 @@ class Problem:
     biases: np.ndarray    # same dtype as scales
     x: np.ndarray         # f32 values or bf16 bits, [M, K]
     meta: dict = field(default_factory=dict)
+    group_size: int = GROUP
 
     def rows(self, m: int) -> "Problem":
         """The same weights with the first m activation rows."""
         return Problem(self.name, self.bits, self.K, self.N, m, self.x_dtype,
                        self.sb_dtype, self.w, self.scales, self.biases,
-                       self.x[:m], dict(self.meta))
+                       self.x[:m], dict(self.meta), self.group_size)
 
     @property
     def weight_bytes(self) -> int:
         sb = 2 if self.sb_dtype == "bf16" else 4
-        return self.N * self.K * self.bits // 8 + 2 * self.N * (self.K // GROUP) * sb
+        return self.N * self.K * self.bits // 8 + 2 * self.N * (self.K // self.group_size) * sb
 
 
 def draw(rng: np.random.Generator, *, name: str, bits: int, K: int, N: int, M: int,
          x_dtype: str, sb_dtype: str, scale_lo: float, scale_hi: float,
          bias_c: float, bias_sigma: float, outlier_frac: float = 0.0,
-         outlier_factor: float = 1.0, x_override: np.ndarray | None = None) -> Problem:
+         outlier_factor: float = 1.0, x_override: np.ndarray | None = None,
+         group_size: int = GROUP) -> Problem:
     """Draw one projection in the recipe's order."""
-    assert K % GROUP == 0 and (K * bits) % 32 == 0
-    G = K // GROUP
+    assert K % group_size == 0 and (K * bits) % 32 == 0
+    G = K // group_size
     w = rng.integers(0, 2**32, size=(N, K * bits // 32), dtype=np.uint64).astype(np.uint32)
     scale = rng.uniform(scale_lo, scale_hi, size=(N, G))
     bias = -bias_c * scale
@@ -98,7 +100,7 @@ def draw(rng: np.random.Generator, *, name: str, bits: int, K: int, N: int, M: i
     else:
         xs = x_override
     return Problem(name, bits, K, N, M, x_dtype, sb_dtype, w, _store(scale, sb_dtype),
-                   _store(bias, sb_dtype), xs)
+                   _store(bias, sb_dtype), xs, {}, group_size)
 
 
 # The five workloads.  Index = seed.
@@ -146,18 +148,22 @@ def workload(idx: int, M: int | None = None) -> list[Problem]:
 
 
 def small(seed: int, *, bits: int, K: int, N: int, M: int, x_dtype: str = "bf16",
-          sb_dtype: str | None = None) -> Problem:
+          sb_dtype: str | None = None, group_size: int = GROUP) -> Problem:
     """A small seeded problem with the distributions of the matching workload
     (3-bit: scale U[0.01,0.04], bias -4s+N(0,.002); 4-bit: U[0.005,0.02],
-    -8s+N(0,.001))."""
+    -8s+N(0,.001)); other widths: a weight range of about 0.16 split into
+    2^bits steps, bias -2^(bits-1) s + N(0, .001)."""
     rng = np.random.default_rng(seed)
     if bits == 3:
         lo, hi, c, sig = 0.01, 0.04, 4.0, 0.002
+    elif bits == 4:
+        lo, hi, c, sig = 0.005, 0.02, 8.0, 0.001
     else:
-        lo, hi, c, sig = 0.005, 0.02, float(2 ** (bits - 1)), 0.001
+        step = 0.16 / 2 ** bits
+        lo, hi, c, sig = 0.5 * step, 2.0 * step, float(2 ** (bits - 1)), 0.001
     return draw(rng, name="small", bits=bits, K=K, N=N, M=M, x_dtype=x_dtype,
                 sb_dtype=sb_dtype or x_dtype, scale_lo=lo, scale_hi=hi, bias_c=c,
-                bias_sigma=sig)
+                bias_sigma=sig, group_size=group_size)
 
 
 def norm_inputs(seed: int, rows: int, D: int, dtype: str = "bf16"):

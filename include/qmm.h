@@ -78,11 +78,17 @@ typedef enum {
                                in two across workgroups, partial tiles added through the
                                workspace (ntw = 1 forces the unsplit form, ntw = 2 with
                                splitk = 2 the split one at 17..32 rows too);
-                               built for K = 5120 and 8192; bf16 activations */
+                               built for K = 5120 and 8192; bf16 activations */,
+  QMM_VARIANT_GENERIC = 6   /* vector-ALU kernel for the other formats (bits 2 and 8, and 3 or
+                               4 with groups of 32 or 128) on MLX's own layout; 1..2 rows per
+                               pass; the only family such plans run on */
 } qmm_variant;
 
-/* Shape and format of one projection.  bits: 3 or 4 (other MLX widths are
- * UNSUPPORTED).  group_size: 64.  K: multiple of 128.  N: multiple of 16.
+/* Shape and format of one projection.  bits: 2, 3, 4 or 8 (5 and 6 are
+ * UNSUPPORTED).  group_size: 32, 64 or 128.  3- and 4-bit group-64 weights
+ * run on the matrix-core families in the native layout; every other format
+ * runs on QMM_VARIANT_GENERIC in MLX's layout.  K: multiple of 128.  N:
+ * multiple of 16.
  * max_rows: the largest row count qmm_run will be given (>= 1).
  * x_dtype: dtype of x and y.  sb_dtype: dtype of scales and biases.
  * flags: must be 0. */
@@ -100,7 +106,7 @@ typedef struct {
 typedef struct qmm_plan qmm_plan;
 
 typedef struct {
-  uint64_t launches[6];   /* indexed by qmm_variant: kernels run per family */
+  uint64_t launches[8];   /* indexed by qmm_variant: kernels run per family */
   int32_t last_variant;   /* family of the last qmm_run */
   int32_t last_ntw;       /* output tiles (16 rows of W each) per wavefront */
   int32_t last_splitk;    /* K splits folded through the workspace */
@@ -116,18 +122,20 @@ void qmm_destroy(qmm_plan* plan);
 
 /* Bytes of the two buffers of the kernel-native weight layout written by
  * qmm_prepack: packed codes (exactly N*K*bits/8, the MLX byte count) and
- * packed scales+biases (exactly 2*N*(K/64) elements of sb_dtype). */
+ * packed scales+biases (exactly 2*N*(K/group_size) elements of sb_dtype). */
 qmm_status qmm_packed_bytes(const qmm_plan* plan, size_t* codes_bytes, size_t* sb_bytes);
 
 /* One-time weight loader: MLX layout -> kernel-native layout.
  *   w       uint32 [N, K*bits/32]  (MLX packed words, row-major)
- *   scales  sb_dtype [N, K/64]
- *   biases  sb_dtype [N, K/64]
+ *   scales  sb_dtype [N, K/group_size]
+ *   biases  sb_dtype [N, K/group_size]
  *   codes_out, sb_out: buffers of qmm_packed_bytes().
- * In the native layout the 16 rows x 128 columns of W that one wavefront
- * multiplies are contiguous, and each lane's codes are ordered so that the
- * unpack to bf16 pairs is a shift and one and-or per pair.  Enqueued on
- * `stream`; the inputs may be freed once it completes. */
+ * In the native layout (3- and 4-bit group 64) the 16 rows x 128 columns of
+ * W that one wavefront multiplies are contiguous, and each lane's codes are
+ * ordered so that the unpack to bf16 pairs is a shift and one and-or per
+ * pair.  Other formats keep MLX's layout: the codes are copied as they are
+ * and sb_out holds the scales, then the biases.  Enqueued on `stream`; the
+ * inputs may be freed once it completes. */
 qmm_status qmm_prepack(const qmm_plan* plan, const uint32_t* w, const void* scales,
                        const void* biases, void* codes_out, void* sb_out, void* stream);
 

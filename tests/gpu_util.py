@@ -75,10 +75,12 @@ def check_against_oracle(p, y_bits, rows=None, sample=None, threads=8, label="")
     rows = rows or p.M
     y = y_to_f64(y_bits, p.x_dtype)[:rows]
     x = p.x[:rows]
-    sx, mw = oracle.bound_terms(p.bits, p.K, x, p.w, p.scales, p.biases)
+    gs = getattr(p, "group_size", 64)
+    sx, mw = oracle.bound_terms(p.bits, p.K, x, p.w, p.scales, p.biases, group_size=gs)
     c = oracle.tolerance_coefficient(p.x_dtype)
     if sample is None:
-        ref = oracle.matmul(p.bits, p.K, x, p.w, p.scales, p.biases, threads=threads)
+        ref = oracle.matmul(p.bits, p.K, x, p.w, p.scales, p.biases, group_size=gs,
+                            threads=threads)
         tol = c * np.outer(sx, mw) + 1e-6
         err = np.abs(y - ref)
         assert np.all(np.isfinite(y)), label + ": non-finite output"
@@ -91,7 +93,7 @@ def check_against_oracle(p, y_bits, rows=None, sample=None, threads=8, label="")
     rng = np.random.default_rng(seed)
     ms = rng.integers(0, rows, count)
     ns = rng.integers(0, p.N, count)
-    ref = oracle.matmul_at(p.bits, p.K, x, p.w, p.scales, p.biases, ms, ns)
+    ref = oracle.matmul_at(p.bits, p.K, x, p.w, p.scales, p.biases, ms, ns, group_size=gs)
     tol = c * sx[ms] * mw[ns] + 1e-6
     got = y[ms, ns]
     err = np.abs(got - ref)

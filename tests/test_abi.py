@@ -33,10 +33,9 @@ def test_library_exports_every_declared_symbol():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(bits=7), b.QMM_ERR_INVALID_ARG),          # not an MLX width
-    (dict(bits=2), b.QMM_ERR_UNSUPPORTED),          # MLX width, no kernel here
-    (dict(bits=8), b.QMM_ERR_UNSUPPORTED),
+    (dict(bits=5), b.QMM_ERR_UNSUPPORTED),          # MLX width, no kernel here
+    (dict(bits=6), b.QMM_ERR_UNSUPPORTED),
     (dict(group_size=48), b.QMM_ERR_INVALID_ARG),
-    (dict(group_size=128), b.QMM_ERR_UNSUPPORTED),
     (dict(K=500), b.QMM_ERR_INVALID_ARG),           # not a multiple of the group
     (dict(K=192), b.QMM_ERR_UNSUPPORTED),           # group-aligned, not 128-aligned
     (dict(N=24), b.QMM_ERR_UNSUPPORTED),
@@ -97,3 +96,15 @@ def test_workspace_sizes_are_bounded():
         ws = p.workspace_bytes(rows)
         assert ws <= 16 * rows * 10240 * 4 + 65536
         assert ws < 10240 * 5120 * 2 // 8
+
+
+@pytest.mark.parametrize("bits,gs", [(2, 32), (2, 64), (2, 128), (3, 32), (3, 128), (4, 32),
+                                     (4, 128), (8, 32), (8, 64), (8, 128)])
+def test_format_variants_plan_on_the_generic_kernel(bits, gs):
+    """Every other MLX format builds a plan whose packed buffers are MLX's own
+    byte counts (codes; scales then biases) and that needs no workspace."""
+    p = b.Plan(bits, 512, 64, 4, "bf16", group_size=gs)
+    cb, sbb = p.packed_bytes()
+    assert cb == 64 * 512 * bits // 8
+    assert sbb == 2 * 64 * (512 // gs) * 2
+    assert p.workspace_bytes(4) == 0
