@@ -197,7 +197,7 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.wk = 1;
     c.S = 1;
     c.nTB = nT;
-    c.grid = nT;
+    c.grid = (int)(p->d.N / 8);  // eight W rows per workgroup
     return c;
   }
   if (variant == QMM_VARIANT_SLAB) {

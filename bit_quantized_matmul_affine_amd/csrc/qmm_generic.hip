@@ -9,7 +9,7 @@
 // words); scales and biases are two planes [N, K/gs] (scales, then biases).
 //
 // gfx950 design (a vector-ALU kernel for the decode regime): a workgroup of
-// four waves owns 16 rows of W, each wave 4 of them; lane l takes the
+// four waves owns 8 rows of W, each wave 2 of them; lane l takes the
 // 32-value slices k0 = 32 l, 32 l + 2048, ... of K (a slice lies in one
 // group because every group size is a multiple of 32, and is `bits` whole
 // words).  Per slice a lane loads its activation slices of up to MR rows
@@ -17,7 +17,12 @@
 // slice's words, scale and bias, converts the 32 codes to floats (one
 // v_cvt_f32_ubyteN per code for 2-, 4- and 8-bit codes, on byte planes of
 // the word) and accumulates s * sum q x + b * sum x.  Lanes are added by a
-// fixed butterfly: the result is bitwise reproducible.
+// fixed butterfly: the result is bitwise reproducible.  Measured at 1 row of
+// 5120 -> 10240: two W rows per wave (eight per workgroup) beat four (more
+// waves hide the load latency of each slice pass); the offset-128 bf16 pair
+// form of 2- and 4-bit codes with v_dot2_f32_bf16 was slower here than the
+// byte-plane conversion, the kernel being bound by load latency, not by its
+// vector instructions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -28,7 +33,7 @@ namespace qmm {
 namespace {
 
 constexpr int kGenThreads = 256;
-constexpr int kGenRowsPerWave = 4;
+constexpr int kGenRowsPerWave = 2;
 constexpr int kGenSlice = 32;  // values per lane slice
 
 // f32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
