@@ -12,14 +12,20 @@
  *     fields of MLX's LSB-first bit stream of uint32 words, a 3-bit field may
  *     straddle two words, a 4-bit field never does.
  *   - affine3-mma.ts / affine4-mma.ts kernel bodies: row n of w starts at byte
- *     n*K*bits/8; scale and bias of (row n, group g) sit at n*(K/64)+g; the
- *     weight is scale*q + bias.
+ *     n*K*bits/8; scale and bias of (row n, group g) sit at n*(K/gs)+g; the
+ *     weight is scale*q + bias.  The hot path is the pages' 3- and 4-bit,
+ *     group-64 format; the other MLX widths 2 and 8 and group sizes 32 and
+ *     128 (those the pages name for their affine KV cache, "mlx-bun 0.0.4"
+ *     page, fused-decode-kernel.ts) run on a generic kernel.
  *   - affine-split-mma.ts, affineSplitMma(): x [..., K] times W^T gives
  *     [..., N] in x's dtype; it borrows its inputs and throws when there are
  *     no rows.  affineSplitMmaEligible(): a separate yes/no predicate (affine,
  *     group 64, bits 3 or 4, shape rules) under which the caller falls back.
- * So for rows m < M and outputs n < N:
- *     y[m][n] = sum_k x[m][k] * (scale[n][k/64] * q(n,k) + bias[n][k/64]).
+ * So for rows m < M and outputs n < N, with gs the group size:
+ *     y[m][n] = sum_k x[m][k] * (scale[n][k/gs] * q(n,k) + bias[n][k/gs]).
+ * Beside it: the fused gate/up projection pair (qmm_run_gate_up), residual
+ * add + RMS normalization (qmm_residual_rms_norm) and decode attention over
+ * an affine-quantized KV cache (qmm_decode_attention).
  * Summation order is the kernels' own (not bit-identical to any other
  * implementation); each kernel is deterministic run to run.
  *
