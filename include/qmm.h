@@ -14,9 +14,9 @@
  *   - affine3-mma.ts / affine4-mma.ts kernel bodies: row n of w starts at byte
  *     n*K*bits/8; scale and bias of (row n, group g) sit at n*(K/gs)+g; the
  *     weight is scale*q + bias.  The hot path is the pages' 3- and 4-bit,
- *     group-64 format; the other MLX widths 2 and 8 and group sizes 32 and
- *     128 (those the pages name for their affine KV cache, "mlx-bun 0.0.4"
- *     page, fused-decode-kernel.ts) run on a generic kernel.
+ *     group-64 format; width 8 and group sizes 32 and 128 (which the pages
+ *     name for their affine KV cache, "mlx-bun 0.0.4" page,
+ *     fused-decode-kernel.ts) and MLX's width 2 run on a generic kernel.
  *   - affine-split-mma.ts, affineSplitMma(): x [..., K] times W^T gives
  *     [..., N] in x's dtype; it borrows its inputs and throws when there are
  *     no rows.  affineSplitMmaEligible(): a separate yes/no predicate (affine,
