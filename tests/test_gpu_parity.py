@@ -10,7 +10,7 @@ import pytest
 import oracle
 from bit_quantized_matmul_affine_amd import binding as b
 from bit_quantized_matmul_affine_amd import synth
-from tests.gpu_util import Runner, check_against_oracle, resident_ok, say, stream_ok
+from tests.gpu_util import Runner, check_against_oracle, resident_ok, say, stream_ok, y_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -325,3 +325,39 @@ def test_workload4_sampled(variant):
     # every output row and column is finite and rows are distinct results
     yf = oracle.decode_bf16(y)
     assert np.all(np.isfinite(yf))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_degenerate_weights_every_family(bits):
+    """Zero scales and biases give exact zeros; a zero activation block gives
+    exact zeros; all-maximum codes (every word all ones) match the oracle; in
+    every kernel family that takes the shape."""
+    import dataclasses
+    base = synth.small(60 + bits, bits=bits, K=5120, N=48, M=3)
+    zero_sb = dataclasses.replace(base, scales=np.zeros_like(base.scales),
+                                  biases=np.zeros_like(base.biases))
+    zero_x = dataclasses.replace(base, x=np.zeros_like(base.x))
+    max_codes = dataclasses.replace(base, w=np.full_like(base.w, 0xFFFFFFFF))
+    variants = ["auto", "gemv", "mfma", "stream", "resident", "slab"]
+    for label, p in (("zero scales and biases", zero_sb), ("zero activations", zero_x)):
+        r = Runner(p)
+        for v in variants:
+            say("degenerate", bits, label, v)
+            y = y_to_f64(r.run(variant=v), p.x_dtype)
+            assert np.all(y == 0.0), "%s %s: %s" % (label, v, y[y != 0][:4])
+    r = Runner(max_codes)
+    for v in variants:
+        say("degenerate", bits, "all-maximum codes", v)
+        check_against_oracle(max_codes, r.run(variant=v), label="max codes %s" % v)
+
+
+def test_degenerate_weights_generic_formats():
+    import dataclasses
+    for bits, gs in ((2, 32), (8, 128)):
+        base = synth.small(70 + bits, bits=bits, K=1024, N=32, M=2, group_size=gs)
+        zero_sb = dataclasses.replace(base, scales=np.zeros_like(base.scales),
+                                      biases=np.zeros_like(base.biases))
+        y = y_to_f64(Runner(zero_sb).run(), base.x_dtype)
+        assert np.all(y == 0.0)
+        max_codes = dataclasses.replace(base, w=np.full_like(base.w, 0xFFFFFFFF))
+        check_against_oracle(max_codes, Runner(max_codes).run(), label="max codes b%d" % bits)
