@@ -12,10 +12,11 @@
 // with M the largest score, v = s_v * code_v + b_v, all sums in f32.
 //
 // gfx950 design:
-//   * kernel 1, one 256-thread workgroup per (block of 128 cached rows, KV
+//   * kernel 1, one 512-thread workgroup per (block of 256 cached rows, KV
 //     head) serving all REP query heads of that KV head, so every key and
-//     value byte is read once per head group; 512 workgroups at 8 KV heads
-//     and 8192 rows;
+//     value byte is read once per head group; 256 workgroups at 8 KV heads
+//     and 8192 rows (measured against 256 threads and 128 rows: 11.8 against
+//     12.0 us for the block kernel, and half as many blocks to merge);
 //   * 16 lanes per cached row (a wave covers 4 rows at once, the 16 lanes
 //     reading one row's words as one contiguous run); lane j owns values
 //     j*D/16 .. (j+1)*D/16 - 1 of a row for the score and of the output;
@@ -43,7 +44,7 @@ namespace qmm {
 
 namespace {
 
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 512;
 constexpr int kAttnLanesPerRow = 16;
 constexpr int kAttnGroups = kAttnThreads / kAttnLanesPerRow;  // lane groups per workgroup
 constexpr int kAttnRowsPerGroup = kAttnBlock / kAttnGroups;    // rows per lane group

@@ -71,7 +71,7 @@ hipError_t launch_generic(int bits, int group_size, bool x_f32, bool sb_f32, int
 // per workgroup of the block kernel; partial outputs [H, G, D] and
 // (max, sum) pairs [H, G, 2] of G = ceil(N / kAttnBlock) blocks in the
 // workspace when G > 1.
-constexpr int kAttnBlock = 128;
+constexpr int kAttnBlock = 256;
 constexpr int kAttnMaxBlocks = 8192;  // merge weights in LDS: 32 KB
 struct AttnArgs {
   const void* q;         // bf16 [H, D]

@@ -221,14 +221,14 @@ qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* 
  *   out[h]      = bf16(sum_n e^score[h, n] v[kv, n] / sum_n e^score[h, n])
  * with every sum in f32.  q, out: bf16 [H, D]; all buffers device memory,
  * row-contiguous, borrowed until the enqueued work completes; code words
- * 16-byte aligned.  The cache is split into blocks of 128 rows whose partial
+ * 16-byte aligned.  The cache is split into blocks of 256 rows whose partial
  * results are merged in block order (bitwise reproducible).  workspace: >=
- * qmm_attention_workspace_bytes(H, N, D) bytes (none when N <= 128; no
+ * qmm_attention_workspace_bytes(H, N, D) bytes (none when N <= 256; no
  * zero-fill needed).  Errors: QMM_ERR_INVALID_ARG for NULL or misaligned
  * pointers, N < 1 or H not a multiple of KV; QMM_ERR_UNSUPPORTED for bits
  * other than 4 and 8, group sizes other than 32, 64, 128, D outside
  * {128, 256, 512} or H/KV outside {1, 2, 4, 8} or D * H/KV > 1024, or N
- * above 2^20 rows;
+ * above 2^21 rows;
  * QMM_ERR_WORKSPACE for a missing or short workspace; QMM_ERR_HIP for launch
  * failures.  Enqueued on `stream`. */
 size_t qmm_attention_workspace_bytes(int32_t H, int64_t N, int32_t D);

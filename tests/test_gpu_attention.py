@@ -49,7 +49,7 @@ CASES = [
     # every head-group width, both code widths, every group size
     (4, 4, 1, 128, 4, 64),
     (2, 1, 127, 256, 8, 32),
-    (8, 2, 129, 128, 4, 128),
+    (8, 2, 257, 128, 4, 128),
     (2, 2, 300, 512, 8, 128),
     (8, 1, 1000, 128, 8, 32),
     (4, 2, 2048, 512, 4, 32),
