@@ -20,10 +20,10 @@ QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED = 0, -1, -2
 QMM_ERR_HIP, QMM_ERR_WORKSPACE, QMM_ERR_NO_DEVICE = -3, -4, -5
 QMM_F32, QMM_BF16 = 0, 1
 (VARIANT_AUTO, VARIANT_GEMV, VARIANT_MFMA, VARIANT_STREAM, VARIANT_RESIDENT, VARIANT_SLAB,
- VARIANT_GENERIC) = (0, 1, 2, 3, 4, 5, 6)
+ VARIANT_GENERIC, VARIANT_WIDE) = (0, 1, 2, 3, 4, 5, 6, 7)
 VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "mfma": VARIANT_MFMA,
             "stream": VARIANT_STREAM, "resident": VARIANT_RESIDENT, "slab": VARIANT_SLAB,
-            "generic": VARIANT_GENERIC}
+            "generic": VARIANT_GENERIC, "wide": VARIANT_WIDE}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 _DTYPES = {"f32": QMM_F32, "bf16": QMM_BF16}
 
@@ -236,7 +236,7 @@ class Plan:
     def stats(self) -> dict:
         s = QmmStats()
         _check(lib().qmm_get_stats(self._h, ctypes.byref(s)))
-        return {"launches": {VARIANT_NAMES[i]: s.launches[i] for i in (1, 2, 3, 4, 5, 6)},
+        return {"launches": {VARIANT_NAMES[i]: s.launches[i] for i in (1, 2, 3, 4, 5, 6, 7)},
                 "last_variant": VARIANT_NAMES.get(s.last_variant, "none"),
                 "last_ntw": s.last_ntw, "last_splitk": s.last_splitk, "last_grid": s.last_grid}
 

@@ -152,6 +152,8 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (rows <= 2 && stream_ok) return QMM_VARIANT_STREAM;
   if (rows <= 16 && resident_fits(p, rows)) return QMM_VARIANT_RESIDENT;
   if (stream_ok) return QMM_VARIANT_STREAM;
+  // more than 64 rows: the wide kernel (bf16 weights, no per-group epilogue)
+  if (rows > qmm::kMaxMfmaRows && qmm::wide_fits(p->nC)) return QMM_VARIANT_WIDE;
   if (slab_fits(p)) return QMM_VARIANT_SLAB;
   return QMM_VARIANT_MFMA;
 }
@@ -188,6 +190,17 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.nTB = c.grid;
     c.S = 1;
     c.lds = qmm::resident_lds_bytes(nw, tm, r, (int)p->d.K);
+    return c;
+  }
+  if (variant == QMM_VARIANT_WIDE) {
+    c.rows_per_launch = 16 * qmm::kWideRowTiles;
+    c.tile_rows = qmm::kWideRowTiles;
+    c.ntw = qmm::kWideTiles;
+    c.wk = 1;
+    c.S = 1;
+    c.nTB = (nT + qmm::kWideTiles - 1) / qmm::kWideTiles;
+    c.grid = c.nTB;
+    c.lds = qmm::wide_lds_bytes();
     return c;
   }
   if (variant == QMM_VARIANT_GENERIC) {
@@ -336,7 +349,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   if (!x || !codes || !sb || !y) return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(sb, 16) || !aligned(y, 4))
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
-  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_GENERIC)
+  if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_WIDE)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
   if (p->generic && variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GENERIC)
     return fail(QMM_ERR_UNSUPPORTED,
@@ -346,8 +359,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     return fail(QMM_ERR_UNSUPPORTED,
                 "3- and 4-bit group-64 plans use the native layout, not the generic kernel");
   if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM ||
-       variant_req == QMM_VARIANT_RESIDENT ||
-       variant_req == QMM_VARIANT_SLAB) &&
+       variant_req == QMM_VARIANT_RESIDENT || variant_req == QMM_VARIANT_SLAB ||
+       variant_req == QMM_VARIANT_WIDE) &&
       p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
   if (variant_req == QMM_VARIANT_STREAM) {
@@ -362,6 +375,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     return fail(QMM_ERR_UNSUPPORTED,
                 "the resident kernel needs K <= 8192 and rows*K*2 bytes of activations (rows "
                 "capped at 16) to fit one compute unit's 160 KB of LDS");
+  if (variant_req == QMM_VARIANT_WIDE && !qmm::wide_fits(p->nC))
+    return fail(QMM_ERR_UNSUPPORTED, "the wide kernel needs K to be a multiple of 256 (K=%lld)",
+                (long long)p->d.K);
   if (variant_req == QMM_VARIANT_SLAB && !slab_fits(p))
     return fail(QMM_ERR_UNSUPPORTED, "the slab kernel is built for K = 5120 and 8192 (K=%lld)",
                 (long long)p->d.K);
@@ -404,6 +420,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     hipError_t e;
     if (variant == QMM_VARIANT_GENERIC)
       e = qmm::launch_generic(p->d.bits, p->d.group_size, xf, sf, rb, a, st);
+    else if (variant == QMM_VARIANT_WIDE)
+      e = qmm::launch_wide(p->d.bits, sf, a, cb.grid, cb.lds, st);
     else if (variant == QMM_VARIANT_SLAB && cb.split)
       e = qmm::launch_split_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, cb.ntw, a, cb.grid, cb.lds,
                                  st);

@@ -87,7 +87,12 @@ typedef enum {
                                built for K = 5120 and 8192; bf16 activations */,
   QMM_VARIANT_GENERIC = 6   /* vector-ALU kernel for the other formats (bits 2 and 8, and 3 or
                                4 with groups of 32 or 128) on MLX's own layout; 1..2 rows per
-                               pass; the only family such plans run on */
+                               pass; the only family such plans run on */,
+  QMM_VARIANT_WIDE = 7      /* matrix-core kernel for 65..128 rows per pass (the default above
+                               64 rows): eight 16-row tiles of W per workgroup, each weight
+                               dequantized once to bf16 in registers (rounded to nearest
+                               even) and the matrix cores accumulating over all of K;
+                               K a multiple of 256; bf16 activations */
 } qmm_variant;
 
 /* Shape and format of one projection.  bits: 2, 3, 4 or 8 (5 and 6 are

@@ -315,7 +315,7 @@ def test_resident_and_slab_more_tiles_than_workgroups():
     check_against_oracle(q, rq.run(variant="slab"), label="slab ragged")
 
 
-@pytest.mark.parametrize("variant", ["auto", "slab", "mfma"])
+@pytest.mark.parametrize("variant", ["auto", "wide", "slab", "mfma"])
 def test_workload4_sampled(variant):
     (p,) = synth.workload(4)
     say("workload 4", variant)
@@ -361,3 +361,38 @@ def test_degenerate_weights_generic_formats():
         assert np.all(y == 0.0)
         max_codes = dataclasses.replace(base, w=np.full_like(base.w, 0xFFFFFFFF))
         check_against_oracle(max_codes, Runner(max_codes).run(), label="max codes b%d" % bits)
+
+
+WIDE = [
+    # bits, K, N, M, sb_dtype: one and many slices, ragged tile groups (N/16 not a
+    # multiple of 8), a second row block, f32 scales
+    (3, 5120, 208, 65, "bf16"),
+    (4, 8192, 112, 128, "bf16"),
+    (4, 5120, 48, 100, "f32"),
+    (3, 256, 16, 130, "bf16"),
+    (4, 2048, 400, 97, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=lambda c: "b%d_K%d_N%d_M%d_%s" % c)
+def test_wide_parity(case):
+    """The wide kernel (65..128 rows per launch, weights dequantized to bf16)
+    is the default above 64 rows."""
+    bits, K, N, M, sd = case
+    p = synth.small(800 + M, bits=bits, K=K, N=N, M=M, sb_dtype=sd)
+    r = Runner(p)
+    say("wide", case)
+    y = r.run()
+    assert r.lin.plan.stats()["last_variant"] == "wide"
+    check_against_oracle(p, y, label="wide %s" % (case,))
+    # the same rows through the slab or MFMA families agree within the bound too
+    check_against_oracle(p, r.run(variant="mfma"), label="mfma %s" % (case,))
+
+
+def test_wide_rejects_k_not_multiple_of_256():
+    p = synth.small(16, bits=4, K=640, N=32, M=70)
+    r = Runner(p)
+    with pytest.raises(b.QmmError) as ei:
+        r.run(variant="wide")
+    assert ei.value.status == b.QMM_ERR_UNSUPPORTED
+    check_against_oracle(p, r.run(), label="K=640 above 64 rows")
