@@ -1319,6 +1319,10 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
 //     LDS ring by LDS-direct loads; each A fragment read from LDS serves the
 //     wave's 2 tiles; one barrier per slice; the slice loop is a run-time
 //     loop (with a 2-slot ring every wait is the same count);
+//   * within a slice the work goes k-step by k-step (32 k): dequantize the
+//     step's B fragments of both tiles, then its 16 MFMAs (8 row tiles x 2
+//     tiles), with no scheduling barriers, so the next step's dequant and
+//     fragment reads overlap the MFMAs;
 //   * the next slice's weight words are loaded as soon as the current ones
 //     are unpacked; the 2 chunk positions' partial tiles are added through
 //     LDS in K order at the end.
@@ -1405,44 +1409,49 @@ __global__ void __launch_bounds__(12 * 64) wide_kernel(LaunchArgs a) {
     wg_barrier();
     for (int j = 0; j < NS; ++j) {
       const u32x4* slot = xs + (j & 1) * SLOT;
-      // dequantized bf16 B fragments of both tiles, group by group
-      uint32_t BD[TW][16];
+      // k-step by k-step (32 k): step q's B fragments of both tiles are
+      // dequantized, then its MFMAs run for every row tile.  No scheduling
+      // barriers here: the compiler overlaps the next step's dequant and
+      // A-fragment reads with this step's MFMAs (16 independent accumulators)
 #pragma unroll
-      for (int i = 0; i < TW; ++i) {
-        uint32_t P[16];
-        unpack_pairs<BITS>(W[i], P, mask_v);
+      for (int gp = 0; gp < 2; ++gp) {
+        uint32_t P[TW][16];
+        Affine f[TW];
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          const Affine f = group_affine<BITS>(gp, SBv[i].s(gp), SBv[i].b(gp));
-#pragma unroll
-          for (int pp = 0; pp < 8; ++pp) {
-            const uint32_t v = P[8 * gp + pp];
-            const float lo = fmaf(f.sc, __uint_as_float(v << 16), f.bp);
-            const float hi = fmaf(f.sc, __uint_as_float(v & 0xFFFF0000u), f.bp);
-            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-            const bf16x2_t pk = {(__bf16)lo, (__bf16)hi};
-            BD[i][8 * gp + pp] = __builtin_bit_cast(uint32_t, pk);
-          }
+        for (int i = 0; i < TW; ++i) {
+          unpack_pairs<BITS>(W[i], P[i], mask_v);
+          f[i] = group_affine<BITS>(gp, SBv[i].s(gp), SBv[i].b(gp));
         }
-      }
-      if (j + 1 < NS) load(j + 1);  // the raw words are free once dequantized
+        if (gp == 1 && j + 1 < NS) load(j + 1);  // the raw words are unpacked
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x4* xrow = slot + (16 * mt + r) * VPR;
-        u32x4 A[4];
+        for (int h = 0; h < 2; ++h) {
+          const int q = 2 * gp + h;
+          u32x4 B[TW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)  // vector of (chunk kp, group q>>1, quarter kg, half q&1)
-          A[q] = xrow[(16 * kp + 8 * (q >> 1) + 2 * kg + (q & 1)) ^ r];
-        __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < TW; ++i) {
+            uint32_t bd[4];
 #pragma unroll
-        for (int i = 0; i < TW; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 B = {BD[i][4 * q], BD[i][4 * q + 1], BD[i][4 * q + 2], BD[i][4 * q + 3]};
-            acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, A[q]), __builtin_bit_cast(bf16x8, B), acc[i][mt], 0, 0, 0);
+            for (int pp = 0; pp < 4; ++pp) {
+              const uint32_t v = P[i][8 * gp + 4 * h + pp];
+              const float lo = fmaf(f[i].sc, __uint_as_float(v << 16), f[i].bp);
+              const float hi = fmaf(f[i].sc, __uint_as_float(v & 0xFFFF0000u), f[i].bp);
+              typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+              const bf16x2_t pk = {(__bf16)lo, (__bf16)hi};
+              bd[pp] = __builtin_bit_cast(uint32_t, pk);
+            }
+            B[i] = u32x4{bd[0], bd[1], bd[2], bd[3]};
           }
-        __builtin_amdgcn_sched_barrier(0);
+          u32x4 A[MT];  // vector (chunk kp, group gp, quarter kg, half h) of each row tile
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            A[mt] = slot[(16 * mt + r) * VPR + ((16 * kp + 8 * gp + 2 * kg + h) ^ r)];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < TW; ++i)
+              acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8, A[mt]), __builtin_bit_cast(bf16x8, B[i]), acc[i][mt], 0, 0, 0);
+        }
       }
       wait_lds();
       wg_barrier();
