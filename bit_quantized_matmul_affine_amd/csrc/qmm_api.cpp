@@ -373,7 +373,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   }
   if (variant_req == QMM_VARIANT_RESIDENT && !resident_fits(p, std::min(rows, 16)))
     return fail(QMM_ERR_UNSUPPORTED,
-                "the resident kernel needs K <= 8192 and rows*K*2 bytes of activations (rows "
+                "the resident kernel needs K <= 16384 and rows*K*2 bytes of activations (rows "
                 "capped at 16) to fit one compute unit's 160 KB of LDS");
   if (variant_req == QMM_VARIANT_WIDE && !qmm::wide_fits(p->nC))
     return fail(QMM_ERR_UNSUPPORTED, "the wide kernel needs K to be a multiple of 256 (K=%lld)",

@@ -1820,11 +1820,14 @@ hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArg
   return sb_f32 ? stream_dispatch<4, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<4, uint16_t>(nw, cpw, a, lds_bytes, st);
 }
 
-// (waves, chunks per wave, tile slots) shapes of the resident kernel.
+// (waves, chunks per wave, tile slots) shapes of the resident kernel.  The
+// 16-wave shapes cover 65..128 chunks (K up to 16384, a few rows): 10.3 us
+// against 10.7 us for the streaming kernel on the 4-bit 15360 -> 3840
+// projection at 4 rows (eight waves of 15 chunks: 11.6 us).
 #define QMM_RESIDENT_SHAPES(X)                                                               \
   X(4, 2, 1) X(4, 2, 2) X(4, 2, 3) X(4, 2, 4) X(4, 4, 1) X(4, 4, 2) X(4, 4, 3) X(4, 4, 4)     \
   X(8, 4, 1) X(8, 4, 2) X(8, 4, 3) X(8, 4, 4) X(8, 5, 1) X(8, 5, 2) X(8, 5, 3) X(8, 5, 4)     \
-  X(8, 8, 1) X(8, 8, 2)
+  X(8, 8, 1) X(8, 8, 2) X(16, 8, 1) X(16, 8, 2)
 
 bool resident_shape(int nC, int tm, int* nw, int* cpw) {
   // the fewest chunks per wave that cover K: four waves below 16 chunks

@@ -74,7 +74,7 @@ typedef enum {
                              the activations of its own chunks and issues all its weight
                              loads up front; K <= 16384; bf16 activations */
   QMM_VARIANT_RESIDENT = 4, /* matrix-core kernel for 1..16 rows whose activation block fits in
-                               one compute unit's LDS (rows*K*2 <= 160 KB, K <= 8192): one
+                               one compute unit's LDS (rows*K*2 <= 160 KB, K <= 16384): one
                                workgroup holds up to four 16-row tiles of W, each wave takes
                                a share of K for all of them; bf16 activations */
   QMM_VARIANT_SLAB = 5      /* matrix-core kernel for 17..64 rows per pass: one workgroup per

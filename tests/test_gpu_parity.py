@@ -162,11 +162,14 @@ def test_resident_rejects_blocks_too_long_for_lds():
     check_against_oracle(p, r.run(rows=13, variant="resident"), rows=13, label="13 rows fit")
 
 
-@pytest.mark.parametrize("case", [(3, 640, 208, 3), (4, 1024, 400, 1), (4, 640, 208, 16)],
+@pytest.mark.parametrize("case", [(3, 640, 208, 3), (4, 1024, 400, 1), (4, 640, 208, 16),
+                                  (4, 15360, 48, 4), (3, 10240, 80, 7)],
                          ids=lambda c: "b%d_K%d_N%d_M%d" % c)
 def test_resident_every_slot_count(case):
     """Four-wave workgroups (one wave per SIMD) issue the unpack and the MFMAs
-    that read its results back to back; every slot count must match the oracle."""
+    that read its results back to back; every slot count must match the oracle.
+    The long-K cases run the sixteen-wave shapes (up to 128 chunks, some
+    waves with fewer chunks than others)."""
     bits, K, N, M = case
     p = synth.small(100 + M, bits=bits, K=K, N=N, M=M)
     r = Runner(p)
