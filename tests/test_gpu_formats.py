@@ -35,6 +35,20 @@ def test_full_shape_sampled(bits, gs):
     check_against_oracle(p, r.run(), sample=(3000, bits), label="b%d g%d full" % (bits, gs))
 
 
+@pytest.mark.parametrize("K", [2048, 4096, 6144, 8192, 8320])
+def test_slice_passes(K):
+    """One to five slice passes per lane (2048 values per pass of a wave),
+    with a ragged last pass at 6144 and 8320."""
+    for bits, gs, x_dtype, sb_dtype, M in ((2, 32, "bf16", "bf16", 2), (8, 128, "f32", "bf16", 1),
+                                          (3, 128, "bf16", "f32", 1)):
+        p = synth.small(500 + K // 128 + bits, bits=bits, K=K, N=32, M=M, x_dtype=x_dtype,
+                        sb_dtype=sb_dtype, group_size=gs)
+        say("format K", K, bits, gs, x_dtype, sb_dtype, M)
+        r = Runner(p)
+        check_against_oracle(p, r.run(), label="K=%d b%d g%d %s/%s M=%d" % (K, bits, gs, x_dtype,
+                                                                         sb_dtype, M))
+
+
 def test_variant_rules():
     p = synth.small(3, bits=2, K=256, N=16, M=1, group_size=64)
     r = Runner(p)
