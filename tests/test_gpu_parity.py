@@ -153,6 +153,42 @@ def test_non_default_stream_and_workspace_reuse():
             check_against_oracle(p.rows(rows), b.to_numpy_bits(y), label="rows %d" % rows)
 
 
+def test_concurrent_streams_with_their_own_workspaces():
+    """Two streams run the split-K 64-row kernel on different inputs at the
+    same time, each with its own workspace (the ticket words live in the
+    workspace, nothing in the library is shared between calls); each result
+    must equal the same call run alone, bit for bit, over several rounds."""
+    import torch
+    probs = [synth.small(31 + i, bits=3, K=5120, N=416, M=64) for i in range(2)]
+    lins = [b.QuantizedLinear(p, max_rows=64) for p in probs]
+    xs = [b.to_device(p.x) for p in probs]
+    need = lins[0].plan.workspace_bytes(64)
+    assert need > 0
+    wss = [torch.zeros(need, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    alone = []
+    for lin, x, ws in zip(lins, xs, wss):
+        alone.append(lin(x, workspace=ws))
+        torch.cuda.synchronize()
+        assert lin.plan.stats()["last_splitk"] == 2
+    for p, y in zip(probs, alone):
+        check_against_oracle(p, b.to_numpy_bits(y), label="alone")
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [torch.empty_like(y) for y in alone]
+    for rnd in range(4):
+        say("concurrent round", rnd)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for lin, x, ws, s, o in zip(lins, xs, wss, streams, outs):
+            with torch.cuda.stream(s):
+                for _ in range(3):  # several launches in flight on each stream
+                    lin(x, out=o, workspace=ws, stream=s)
+        torch.cuda.synchronize()
+        for i, (o, y) in enumerate(zip(outs, alone)):
+            assert torch.equal(o.view(torch.int16), y.view(torch.int16)), \
+                "stream %d, round %d differs from the call run alone" % (i, rnd)
+
+
 def test_resident_rejects_blocks_too_long_for_lds():
     p = synth.small(13, bits=4, K=6144, N=32, M=16)   # 16*6144*2 bytes > 160 KB
     r = Runner(p)
