@@ -225,6 +225,10 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     const int tw = ntw_req ? ntw_req : (c.tile_rows == 4 ? 2 : 1);
     const int S = s_req ? s_req : 2;
     int ns = 0, nslot = 0;
+    // 33..48 rows: the split form in three row tiles (48 rows) where it is
+    // built, instead of four with a fourth computed for nothing
+    if (c.tile_rows == 4 && r <= 48 && tw >= 2 && qmm::split_slab_shape(3, tw, nC, S, &ns, &nslot))
+      c.tile_rows = 3;
     if (c.tile_rows >= 2 && tw >= 2 && qmm::split_slab_shape(c.tile_rows, tw, nC, S, &ns, &nslot)) {
       c.split = true;
       c.ntw = tw;

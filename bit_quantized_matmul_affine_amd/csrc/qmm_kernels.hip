@@ -1932,7 +1932,9 @@ int slab_slices(int mt, int nC) {
 // LDS ring slots and weight ring depth (slices of loads in flight per
 // compute wave), measured on the 3-bit 5120x10240 workload: deeper weight
 // rings queue the activation slices behind weight loads and run slower.
-static constexpr int slab_ring(int mt) { return mt == 4 ? 2 : 4; }
+// LDS ring slots per row-tile count (128 KB at one, two and four row tiles,
+// 144 KB at three; three row tiles run in the split form only)
+static constexpr int slab_ring(int mt) { return mt == 4 ? 2 : (mt == 3 ? 3 : 4); }
 static constexpr int slab_depth(int mt) { return mt == 2 ? 2 : 3; }
 size_t slab_lds_bytes(int mt) { return (size_t)slab_ring(mt) * 16 * mt * 1024; }
 
@@ -1967,7 +1969,7 @@ hipError_t launch_slab(int bits, bool sb_f32, int mt, int ns, const LaunchArgs& 
 // (5 or 8 slices each), two W tiles per wave in three slots (three tiles per
 // wave in two slots spills registers at four row tiles and measured no
 // faster; one K part leaves half the compute units idle).
-#define QMM_SPLIT_SLAB_SHAPES(X) X(2, 5) X(4, 5) X(2, 8) X(4, 8)
+#define QMM_SPLIT_SLAB_SHAPES(X) X(2, 5) X(3, 5) X(4, 5) X(2, 8) X(3, 8) X(4, 8)
 #define QMM_SPLIT_SLAB_WAVES(X) X(2, 3)
 
 bool split_slab_shape(int mt, int tw, int nC, int S, int* ns, int* nslot) {

@@ -313,13 +313,15 @@ def test_slab_parity(case):
 
 @pytest.mark.parametrize("case", [(3, 5120, 208, 17, "bf16"), (4, 5120, 176, 32, "f32"),
                                   (3, 5120, 96, 64, "bf16"), (4, 8192, 112, 40, "bf16"),
-                                  (3, 8192, 64, 29, "bf16")],
+                                  (3, 8192, 64, 29, "bf16"), (3, 5120, 208, 33, "bf16"),
+                                  (4, 5120, 96, 48, "f32"), (3, 8192, 160, 49, "bf16")],
                          ids=lambda c: "b%d_K%d_N%d_M%d_%s" % c)
 def test_slab_split_and_unsplit_forms(case):
     """Both slab forms on one problem: the split form (six W tiles per
     workgroup, K in two parts added through the workspace; ragged tile groups
-    where N/16 is not a multiple of 6) and the unsplit form, twice in a row so
-    the workspace's tickets are reused."""
+    where N/16 is not a multiple of 6; three row tiles at 33..48 rows, four
+    above) and the unsplit form, twice in a row so the workspace's tickets
+    are reused."""
     bits, K, N, M, sd = case
     p = synth.small(700 + M, bits=bits, K=K, N=N, M=M, sb_dtype=sd)
     r = Runner(p)
