@@ -82,7 +82,8 @@ typedef enum {
                                through an LDS ring in slices of 512 columns by loader waves;
                                for 33..64 rows its split form: six tiles per workgroup, K cut
                                in two across workgroups, partial tiles added through the
-                               workspace (ntw = 1 forces the unsplit form, ntw = 2 with
+                               workspace, 48-row blocks at 33..48 rows and 64-row blocks
+                               above (ntw = 1 forces the unsplit form, ntw = 2 with
                                splitk = 2 the split one at 17..32 rows too);
                                built for K = 5120 and 8192; bf16 activations */,
   QMM_VARIANT_GENERIC = 6   /* vector-ALU kernel for the other formats (bits 2 and 8, and 3 or
