@@ -153,7 +153,14 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   if (rows <= 16 && resident_fits(p, rows)) return QMM_VARIANT_RESIDENT;
   if (stream_ok) return QMM_VARIANT_STREAM;
   // more than 64 rows: the wide kernel (bf16 weights, no per-group epilogue)
-  if (rows > qmm::kMaxMfmaRows && qmm::wide_fits(p->nC)) return QMM_VARIANT_WIDE;
+  // where its grid (eight W tiles per workgroup) fills at least half the
+  // compute units; else 64-row blocks on the slab or MFMA kernels (3-bit
+  // 5120->10240 at 128 rows, 80 workgroups: 41.6 us wide against about 36 us
+  // as two 64-row split slab launches; 4-bit 8192->28672, 224 workgroups:
+  // 85 against 155 us)
+  if (rows > qmm::kMaxMfmaRows && qmm::wide_fits(p->nC) &&
+      2 * ((p->nT + qmm::kWideTiles - 1) / qmm::kWideTiles) >= device_cus())
+    return QMM_VARIANT_WIDE;
   if (slab_fits(p)) return QMM_VARIANT_SLAB;
   return QMM_VARIANT_MFMA;
 }
@@ -194,13 +201,15 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
   }
   if (variant == QMM_VARIANT_WIDE) {
     c.rows_per_launch = 16 * qmm::kWideRowTiles;
-    c.tile_rows = qmm::kWideRowTiles;
+    // 65..96 rows in six row tiles: no MFMAs or A-fragment reads for a
+    // seventh and eighth tile of padding rows
+    c.tile_rows = std::min(rows, c.rows_per_launch) <= 96 ? 6 : qmm::kWideRowTiles;
     c.ntw = qmm::kWideTiles;
     c.wk = 1;
     c.S = 1;
     c.nTB = (nT + qmm::kWideTiles - 1) / qmm::kWideTiles;
     c.grid = c.nTB;
-    c.lds = qmm::wide_lds_bytes();
+    c.lds = qmm::wide_lds_bytes(c.tile_rows);
     return c;
   }
   if (variant == QMM_VARIANT_GENERIC) {
@@ -425,7 +434,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (variant == QMM_VARIANT_GENERIC)
       e = qmm::launch_generic(p->d.bits, p->d.group_size, xf, sf, rb, a, st);
     else if (variant == QMM_VARIANT_WIDE)
-      e = qmm::launch_wide(p->d.bits, sf, a, cb.grid, cb.lds, st);
+      e = qmm::launch_wide(p->d.bits, sf, cb.tile_rows, a, cb.grid, cb.lds, st);
     else if (variant == QMM_VARIANT_SLAB && cb.split)
       e = qmm::launch_split_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, cb.ntw, a, cb.grid, cb.lds,
                                  st);

@@ -103,15 +103,16 @@ hipError_t launch_gate_up(int bits, bool sb_f32, int nw, int cpw, int pairs, con
 constexpr int kSlabTiles = 3;
 int slab_slices(int mt, int nC);
 size_t slab_lds_bytes(int mt);
-// Wide kernel: 65..128 activation rows per launch (kWideRowTiles tiles of
-// 16), weights dequantized to bf16 in registers, 8 W tiles per workgroup,
-// K in slices of 256 (K a multiple of 256).
+// Wide kernel: 65..128 activation rows per launch (up to kWideRowTiles tiles
+// of 16 rows; 6 tiles for up to 96 rows, else 8), weights dequantized to bf16
+// in registers, 8 W tiles per workgroup, K in slices of 256 (K a multiple of
+// 256).
 constexpr int kWideRowTiles = 8;
 constexpr int kWideTiles = 8;
-size_t wide_lds_bytes();
+size_t wide_lds_bytes(int mt);
 bool wide_fits(int nC);
-hipError_t launch_wide(int bits, bool sb_f32, const LaunchArgs& a, int grid, size_t lds_bytes,
-                       hipStream_t st);
+hipError_t launch_wide(int bits, bool sb_f32, int mt, const LaunchArgs& a, int grid,
+                       size_t lds_bytes, hipStream_t st);
 // Split slab kernel: K cut into S (1 or 2) parts across workgroups, TW (2 or
 // 3) W tiles per compute wave, NSLOT tile slots; partial tiles of S = 2 go
 // through the workspace (tickets, then the part area).

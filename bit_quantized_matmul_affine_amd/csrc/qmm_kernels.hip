@@ -1327,9 +1327,10 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
 //     are unpacked; the 2 chunk positions' partial tiles are added through
 //     LDS in K order at the end.
 // ---------------------------------------------------------------------------
-template <int BITS, typename ST>
+template <int BITS, int MT, typename ST>
 __global__ void __launch_bounds__(12 * 64) wide_kernel(LaunchArgs a) {
-  constexpr int MT = kWideRowTiles, TW = 2, NSLOT = 4, KP = 2, NWC = NSLOT * KP, NWL = 4;
+  constexpr int TW = 2, NSLOT = 4, KP = 2, NWC = NSLOT * KP, NWL = 4;
+  static_assert(MT % KP == 0 && MT <= kWideRowTiles, "whole row tiles per chunk position");
   constexpr int ROWS = 16 * MT;
   constexpr int SK = KP * kChunkK;  // k per slice (256)
   constexpr int VPR = SK / 8;       // 16-byte vectors per row per slice (32)
@@ -2023,13 +2024,13 @@ hipError_t launch_split_slab(int bits, bool sb_f32, int mt, int ns, int tw, cons
                 : split_slab_dispatch<4, uint16_t>(mt, ns, tw, a, grid, lds_bytes, st);
 }
 
-size_t wide_lds_bytes() { return (size_t)2 * 16 * kWideRowTiles * 32 * 16; }
+size_t wide_lds_bytes(int mt) { return (size_t)2 * 16 * mt * 32 * 16; }
 
 bool wide_fits(int nC) { return nC >= 2 && nC % 2 == 0; }
 
-template <int BITS, typename ST>
-static hipError_t wide_dispatch(const LaunchArgs& a, int grid, size_t lds, hipStream_t st) {
-  auto* kfn = &wide_kernel<BITS, ST>;
+template <int BITS, int MT, typename ST>
+static hipError_t wide_launch(const LaunchArgs& a, int grid, size_t lds, hipStream_t st) {
+  auto* kfn = &wide_kernel<BITS, MT, ST>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -2037,13 +2038,22 @@ static hipError_t wide_dispatch(const LaunchArgs& a, int grid, size_t lds, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_wide(int bits, bool sb_f32, const LaunchArgs& a, int grid, size_t lds_bytes,
-                       hipStream_t st) {
+// row tiles per launch: 6 (up to 96 rows) or 8
+template <int BITS, typename ST>
+static hipError_t wide_dispatch(int mt, const LaunchArgs& a, int grid, size_t lds,
+                                hipStream_t st) {
+  if (mt == 6) return wide_launch<BITS, 6, ST>(a, grid, lds, st);
+  if (mt == 8) return wide_launch<BITS, 8, ST>(a, grid, lds, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_wide(int bits, bool sb_f32, int mt, const LaunchArgs& a, int grid,
+                       size_t lds_bytes, hipStream_t st) {
   if (bits == 3)
-    return sb_f32 ? wide_dispatch<3, float>(a, grid, lds_bytes, st)
-                  : wide_dispatch<3, uint16_t>(a, grid, lds_bytes, st);
-  return sb_f32 ? wide_dispatch<4, float>(a, grid, lds_bytes, st)
-                : wide_dispatch<4, uint16_t>(a, grid, lds_bytes, st);
+    return sb_f32 ? wide_dispatch<3, float>(mt, a, grid, lds_bytes, st)
+                  : wide_dispatch<3, uint16_t>(mt, a, grid, lds_bytes, st);
+  return sb_f32 ? wide_dispatch<4, float>(mt, a, grid, lds_bytes, st)
+                : wide_dispatch<4, uint16_t>(mt, a, grid, lds_bytes, st);
 }
 
 hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid, hipStream_t st) {

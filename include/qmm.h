@@ -90,7 +90,9 @@ typedef enum {
                                4 with groups of 32 or 128) on MLX's own layout; 1..2 rows per
                                pass; the only family such plans run on */,
   QMM_VARIANT_WIDE = 7      /* matrix-core kernel for 65..128 rows per pass (the default above
-                               64 rows): eight 16-row tiles of W per workgroup, each weight
+                               64 rows where N/128 workgroups fill at least half the compute
+                               units; 96-row blocks up to 96 rows, else 128): eight 16-row
+                               tiles of W per workgroup, each weight
                                dequantized once to bf16 in registers (rounded to nearest
                                even) and the matrix cores accumulating over all of K;
                                K a multiple of 256; bf16 activations */

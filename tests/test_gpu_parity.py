@@ -412,22 +412,42 @@ WIDE = [
     (4, 5120, 48, 100, "f32"),
     (3, 256, 16, 130, "bf16"),
     (4, 2048, 400, 97, "bf16"),
+    (3, 5120, 208, 96, "bf16"),
+    (4, 1024, 144, 80, "f32"),
 ]
 
 
 @pytest.mark.parametrize("case", WIDE, ids=lambda c: "b%d_K%d_N%d_M%d_%s" % c)
 def test_wide_parity(case):
-    """The wide kernel (65..128 rows per launch, weights dequantized to bf16)
-    is the default above 64 rows."""
+    """The wide kernel (65..128 rows per launch, weights dequantized to bf16;
+    six row tiles up to 96 rows (65, 80, 96 and the 2-row tail of 130), eight
+    above), forced: these N are too small for it to be the default."""
     bits, K, N, M, sd = case
     p = synth.small(800 + M, bits=bits, K=K, N=N, M=M, sb_dtype=sd)
     r = Runner(p)
     say("wide", case)
-    y = r.run()
+    y = r.run(variant="wide")
     assert r.lin.plan.stats()["last_variant"] == "wide"
     check_against_oracle(p, y, label="wide %s" % (case,))
     # the same rows through the slab or MFMA families agree within the bound too
     check_against_oracle(p, r.run(variant="mfma"), label="mfma %s" % (case,))
+
+
+def test_rows_above_64_dispatch():
+    """Above 64 rows the wide kernel is the default only where its grid (eight
+    W tiles per workgroup) fills at least half the compute units; else the
+    rows run in 64-row blocks on another family."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    big_n = 16 * 8 * ((cus + 1) // 2)           # exactly half the units
+    for N, want_wide in ((big_n, True), (big_n // 2, False)):
+        p = synth.small(900 + N % 97, bits=4, K=256, N=N, M=100)
+        r = Runner(p)
+        say("rows above 64, N", N)
+        y = r.run()
+        fam = r.lin.plan.stats()["last_variant"]
+        assert (fam == "wide") == want_wide, (N, fam)
+        check_against_oracle(p, y, label="dispatch N=%d (%s)" % (N, fam))
 
 
 def test_wide_rejects_k_not_multiple_of_256():
