@@ -328,14 +328,26 @@ size_t cfg_workspace(const qmm_plan* p, const Cfg& c, int rows) {
   return ticket_bytes(p) + (size_t)c.S * r * p->d.N * sizeof(float);
 }
 
+// The family of one row block of a call in several blocks: a choice left to
+// the library is remade for a block shorter than the call's blocks (a
+// 65-row call on the slab family: one 64-row block, then one row on the
+// streaming kernel); a forced family runs every block.
+int block_variant(const qmm_plan* p, int call_variant, bool chosen, int rows, int rb) {
+  if (!chosen || rb == rows || p->force_variant) return call_variant;
+  if (call_variant != QMM_VARIANT_SLAB && call_variant != QMM_VARIANT_MFMA) return call_variant;
+  return pick_variant(p, rb, QMM_VARIANT_AUTO);
+}
+
 // Largest workspace any row block of a `rows`-row call needs (blocks of a
 // call run one after another on the stream and share the workspace).
-size_t call_workspace(const qmm_plan* p, int rows, int variant, int ntw, int wk, int s) {
+size_t call_workspace(const qmm_plan* p, int rows, int variant, bool chosen, int ntw, int wk,
+                      int s) {
   const Cfg c = plan_config(p, rows, variant, ntw, wk, s);
   size_t need = 0;
   for (int r0 = 0; r0 < rows; r0 += c.rows_per_launch) {
     const int rb = std::min(c.rows_per_launch, rows - r0);
-    need = std::max(need, cfg_workspace(p, plan_config(p, rb, variant, ntw, wk, s), rb));
+    const int vb = block_variant(p, variant, chosen, rows, rb);
+    need = std::max(need, cfg_workspace(p, plan_config(p, rb, vb, ntw, wk, s), rb));
   }
   return need;
 }
@@ -400,8 +412,9 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   const int wk_eff = wk_req ? wk_req : p->env_kwaves;
   const int s_eff = s_req ? s_req : p->env_splitk;
   const int variant = pick_variant(p, rows, variant_req);
+  const bool chosen = variant_req == QMM_VARIANT_AUTO;
   const Cfg c = plan_config(p, rows, variant, ntw_eff, wk_eff, s_eff);
-  const size_t need = call_workspace(p, rows, variant, ntw_eff, wk_eff, s_eff);
+  const size_t need = call_workspace(p, rows, variant, chosen, ntw_eff, wk_eff, s_eff);
   if (need > 0) {
     if (!ws || ws_bytes < need)
       return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
@@ -413,7 +426,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   for (int r0 = 0; r0 < rows; r0 += c.rows_per_launch) {
     const int rb = std::min(c.rows_per_launch, rows - r0);
-    const Cfg cb = plan_config(p, rb, variant, ntw_eff, wk_eff, s_eff);
+    const int vb = block_variant(p, variant, chosen, rows, rb);
+    const Cfg cb = plan_config(p, rb, vb, ntw_eff, wk_eff, s_eff);
     qmm::LaunchArgs a{};
     a.x = static_cast<const char*>(x) + (size_t)r0 * p->d.K * xe;
     a.codes = static_cast<const uint32_t*>(codes);
@@ -431,29 +445,29 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (variant == QMM_VARIANT_GENERIC)
+    if (vb == QMM_VARIANT_GENERIC)
       e = qmm::launch_generic(p->d.bits, p->d.group_size, xf, sf, rb, a, st);
-    else if (variant == QMM_VARIANT_WIDE)
+    else if (vb == QMM_VARIANT_WIDE)
       e = qmm::launch_wide(p->d.bits, sf, cb.tile_rows, a, cb.grid, cb.lds, st);
-    else if (variant == QMM_VARIANT_SLAB && cb.split)
+    else if (vb == QMM_VARIANT_SLAB && cb.split)
       e = qmm::launch_split_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, cb.ntw, a, cb.grid, cb.lds,
                                  st);
-    else if (variant == QMM_VARIANT_SLAB)
+    else if (vb == QMM_VARIANT_SLAB)
       e = qmm::launch_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, a, cb.grid, cb.lds, st);
-    else if (variant == QMM_VARIANT_RESIDENT)
+    else if (vb == QMM_VARIANT_RESIDENT)
       e = qmm::launch_resident(p->d.bits, sf, cb.wk, cb.cpw, cb.ntw, a, cb.grid, cb.lds, st);
-    else if (variant == QMM_VARIANT_STREAM)
+    else if (vb == QMM_VARIANT_STREAM)
       e = qmm::launch_stream(p->d.bits, sf, cb.wk, cb.ntw, a, cb.lds, st);
-    else if (variant == QMM_VARIANT_MFMA)
+    else if (vb == QMM_VARIANT_MFMA)
       e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, st);
     else
       e = qmm::launch_gemv(p->d.bits, xf, sf, cb.tile_rows, cb.ntw, a, cb.lds, st);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
-    p->launches[variant].fetch_add(1);
-    p->last_variant = variant;
+    p->launches[vb].fetch_add(1);
+    p->last_variant = vb;
     p->last_ntw = cb.ntw;
     p->last_splitk = cb.S;
-    p->last_grid = (variant == QMM_VARIANT_RESIDENT || variant == QMM_VARIANT_SLAB)
+    p->last_grid = (vb == QMM_VARIANT_RESIDENT || vb == QMM_VARIANT_SLAB)
                        ? cb.grid : cb.nTB * cb.S;
   }
   if (getenv("QMM_LOG"))
@@ -560,8 +574,8 @@ size_t qmm_workspace_bytes_ex(const qmm_plan* p, int32_t variant, int32_t ntw, i
                               int32_t splitk, int32_t rows) {
   if (!p || rows < 1) return 0;
   const int v = pick_variant(p, rows, variant);
-  return call_workspace(p, rows, v, ntw ? ntw : p->env_ntw, kwaves ? kwaves : p->env_kwaves,
-                        splitk ? splitk : p->env_splitk);
+  return call_workspace(p, rows, v, variant == QMM_VARIANT_AUTO, ntw ? ntw : p->env_ntw,
+                        kwaves ? kwaves : p->env_kwaves, splitk ? splitk : p->env_splitk);
 }
 
 size_t qmm_workspace_bytes(const qmm_plan* p, int32_t rows) {

@@ -450,6 +450,22 @@ def test_rows_above_64_dispatch():
         check_against_oracle(p, y, label="dispatch N=%d (%s)" % (N, fam))
 
 
+def test_blocks_of_a_long_call_pick_their_own_family():
+    """A 65- and an 80-row call where the wide kernel is not the default run
+    a 64-row block on the slab family, then the last block on the family of
+    its own row count (one row: streaming; 16 rows: resident)."""
+    for M, last in ((65, "stream"), (80, "resident")):
+        p = synth.small(950 + M, bits=3, K=5120, N=208, M=M)
+        r = Runner(p)
+        say("long call", M)
+        before = dict(r.lin.plan.stats()["launches"])
+        y = r.run()
+        st = r.lin.plan.stats()
+        assert st["last_variant"] == last, (M, st)
+        assert st["launches"]["slab"] == before["slab"] + 1, (M, st)
+        check_against_oracle(p, y, label="long call M=%d" % M)
+
+
 def test_wide_rejects_k_not_multiple_of_256():
     p = synth.small(16, bits=4, K=640, N=32, M=70)
     r = Runner(p)
