@@ -160,7 +160,10 @@ qmm_status qmm_prepack(const qmm_plan* plan, const uint32_t* w, const void* scal
  * stream.  Calls that overlap in time must not share a workspace. */
 size_t qmm_workspace_bytes(const qmm_plan* plan, int32_t rows);
 
-/* y[rows, N] = x[rows, K] . W^T with W given in the native layout.
+/* y[rows, N] = x[rows, K] . W^T with W given in the native layout.  Rows
+ * beyond one launch of the chosen family run as consecutive row blocks on
+ * `stream`; a shorter last block runs on the family chosen for its own row
+ * count.
  *   x: x_dtype [rows, K] row-contiguous, 16-byte aligned;
  *   y: x_dtype [rows, N] row-contiguous; only rows < `rows` are written;
  *   workspace: >= qmm_workspace_bytes(plan, rows) bytes (may be NULL when
@@ -171,7 +174,7 @@ qmm_status qmm_run(const qmm_plan* plan, const void* x, const void* codes, const
                    void* stream);
 
 /* qmm_run with a forced kernel family and launch shape, for tests and
- * measurement.  ntw: tiles of 16 rows of W per wavefront (1, 2, 4; for the
+ * measurement (a forced family runs every row block).  ntw: tiles of 16 rows of W per wavefront (1, 2, 4; for the
  * RESIDENT family: tiles a workgroup holds at once, 1..4; for SLAB: 1 = the
  * unsplit form, 2 = the split form where it is built for this K and splitk,
  * else the unsplit form); kwaves: wavefronts of a workgroup that split K
