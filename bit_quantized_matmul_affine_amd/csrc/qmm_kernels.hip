@@ -1313,10 +1313,10 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
 // all-ones MFMA, no epilogue.  The rounding of w to bf16 (relative 2^-9) is
 // inside the accuracy bound of bf16 activations.
 //   * one workgroup owns TG = 8 W tiles (4 slots of 2) over all of K and all
-//     16*MT = 128 rows; 8 compute waves = 4 tile-pair slots x 2 chunk
-//     positions, 4 loader waves;
-//   * activation slices of 256 columns x 128 rows (64 KB) through a 2-slot
-//     LDS ring by LDS-direct loads; each A fragment read from LDS serves the
+//     16*MT rows (MT = 6 up to 96 rows, else 8); 8 compute waves = 4
+//     tile-pair slots x 2 chunk positions, 4 loader waves;
+//   * activation slices of 256 columns x 16*MT rows (48 or 64 KB) through a
+//     2-slot LDS ring by LDS-direct loads; each A fragment read from LDS serves the
 //     wave's 2 tiles; one barrier per slice; the slice loop is a run-time
 //     loop (with a 2-slot ring every wait is the same count);
 //   * within a slice the work goes k-step by k-step (32 k): dequantize the
