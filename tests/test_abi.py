@@ -98,6 +98,24 @@ def test_workspace_sizes_are_bounded():
         assert ws < 10240 * 5120 * 2 // 8
 
 
+def test_automatic_workspace_follows_the_row_blocks():
+    """Host dispatch, no GPU: the automatic choice's workspace is the split
+    slab form's partial tiles at 33..64 rows (48-row blocks needing less than
+    64-row ones), none for the streaming and resident kernels, and for a long
+    call the largest of its blocks (a 65- or 80-row call: one 64-row block,
+    then a tail on the streaming or resident kernel); a wide-kernel call on
+    a shape whose grid fills the chip needs none."""
+    p = b.Plan(3, 5120, 208, 128, "bf16")
+    auto = lambda rows: b.lib().qmm_workspace_bytes_ex(p.handle, 0, 0, 0, 0, rows)
+    assert auto(1) == 0 and auto(9) == 0 and auto(16) == 0
+    w48, w64 = auto(48), auto(64)
+    assert 0 < w48 < w64
+    assert auto(33) == w48
+    assert auto(65) == w64 and auto(80) == w64 and auto(128) == w64
+    q = b.Plan(4, 8192, 28672, 128, "bf16")
+    assert b.lib().qmm_workspace_bytes_ex(q.handle, 0, 0, 0, 0, 128) == 0
+
+
 @pytest.mark.parametrize("bits,gs", [(2, 32), (2, 64), (2, 128), (3, 32), (3, 128), (4, 32),
                                      (4, 128), (8, 32), (8, 64), (8, 128)])
 def test_format_variants_plan_on_the_generic_kernel(bits, gs):
