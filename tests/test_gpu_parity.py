@@ -232,6 +232,19 @@ def test_stream_rejects_shapes_it_does_not_cover():
     check_against_oracle(p, r.run(rows=1, variant="stream"), rows=1, label="one row fits")
 
 
+def test_large_n_every_default_family():
+    """131072 outputs (8192 W tiles, grids far beyond one pass over the
+    compute units): the default family at 1, 9, 40 and 100 rows (streaming,
+    resident, MFMA, wide), checked on sampled outputs."""
+    p = synth.small(14, bits=4, K=256, N=131072, M=100)
+    r = Runner(p)
+    for rows, fam in ((1, "stream"), (9, "resident"), (40, "mfma"), (100, "wide")):
+        say("large N rows", rows)
+        y = r.run(rows=rows)
+        assert r.lin.plan.stats()["last_variant"] == fam, (rows, r.lin.plan.stats())
+        check_against_oracle(p, y, rows=rows, sample=(2000, rows), label="large N rows %d" % rows)
+
+
 def test_stats_report_the_family_that_ran():
     p = synth.small(10, bits=4, K=512, N=64, M=4)
     r = Runner(p)
