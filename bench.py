@@ -61,17 +61,27 @@ def cpu_baseline(problem, seconds: float = 12.0):
                       % (reps, N, ",".join(map(str, ROWS)), dt)}
 
 
+def kernel_source_hash() -> str:
+    """sha256[:16] over the matmul kernels' sources (the shared device header
+    and every family's file, in name order)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "bit_quantized_matmul_affine_amd", "csrc")
+    h = hashlib.sha256()
+    for name in ("qmm_device.h", "qmm_internal.h", "qmm_layout.hip", "qmm_mfma.hip",
+                 "qmm_resident.hip", "qmm_slab.hip", "qmm_stream.hip", "qmm_wide.hip"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(rows: int):
     """HBM bytes per launch of the kernel that serves `rows` rows, from the
     committed FETCH_SIZE/WRITE_SIZE measurement, or None when the kernel
     source has changed since it was taken."""
-    import hashlib
     try:
         with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
             rec = json.load(f)
-        with open(os.path.join(ROOT, "bit_quantized_matmul_affine_amd", "csrc", "qmm_kernels.hip"),
-                  "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()[:16]
+        h = kernel_source_hash()
     except OSError:
         return None
     if rec.get("kernel_source_sha256_16") != h:

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libqmm.so")
 QMM_OK, QMM_ERR_INVALID_ARG, QMM_ERR_UNSUPPORTED = 0, -1, -2
 QMM_ERR_HIP, QMM_ERR_WORKSPACE, QMM_ERR_NO_DEVICE = -3, -4, -5
 QMM_F32, QMM_BF16 = 0, 1
+QMM_FLAG_F32_OUT = 1
 (VARIANT_AUTO, VARIANT_GEMV, VARIANT_MFMA, VARIANT_STREAM, VARIANT_RESIDENT, VARIANT_SLAB,
  VARIANT_GENERIC, VARIANT_WIDE) = (0, 1, 2, 3, 4, 5, 6, 7)
 VARIANTS = {"auto": VARIANT_AUTO, "gemv": VARIANT_GEMV, "mfma": VARIANT_MFMA,
@@ -144,16 +145,18 @@ class Plan:
     """One projection shape: qmm_create / qmm_destroy plus the calls on it."""
 
     def __init__(self, bits: int, K: int, N: int, max_rows: int, x_dtype: str = "bf16",
-                 sb_dtype: str | None = None, group_size: int = 64):
+                 sb_dtype: str | None = None, group_size: int = 64, f32_out: bool = False):
         self.bits, self.K, self.N, self.max_rows = bits, K, N, max_rows
         self.x_dtype = x_dtype
         self.sb_dtype = sb_dtype or x_dtype
+        self.f32_out = bool(f32_out)
         d = QmmDesc(bits, group_size, K, N, max_rows, _DTYPES[x_dtype],
-                    _DTYPES[self.sb_dtype], 0)
+                    _DTYPES[self.sb_dtype], QMM_FLAG_F32_OUT if f32_out else 0)
         h = ctypes.c_void_p()
         _check(lib().qmm_create(ctypes.byref(d), ctypes.byref(h)))
         self._h = h
-        self._ws = {}
+        self._ws = {}        # (device, stream) -> zero-filled workspace
+        self._retired = []   # replaced workspaces: a captured graph may still use them
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -188,15 +191,23 @@ class Plan:
             return lib().qmm_workspace_bytes_ex(self._h, variant, ntw, kwaves, splitk, rows)
         return lib().qmm_workspace_bytes(self._h, rows)
 
-    def workspace(self, nbytes: int, device):
-        """A zero-filled workspace of at least nbytes, cached per device."""
+    def workspace(self, nbytes: int, device, stream=None):
+        """A zero-filled workspace of at least nbytes, one per (device,
+        stream): calls on different streams may overlap in time, so they never
+        share one.  It is zero-filled on that stream (ordered before the calls
+        that use it), and a replaced, smaller one is kept alive, since a
+        captured graph may still hold its address."""
         import torch
         if nbytes == 0:
             return None
-        key = str(device)
+        st = stream if stream is not None else torch.cuda.current_stream(device)
+        key = (str(device), int(st.cuda_stream))
         ws = self._ws.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            if ws is not None:
+                self._retired.append(ws)
+            with torch.cuda.stream(st):
+                ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
             self._ws[key] = ws
         return ws
 
@@ -206,10 +217,12 @@ class Plan:
         import torch
         rows = x.numel() // self.K
         if out is None:
-            out = torch.empty(*x.shape[:-1], self.N, dtype=x.dtype, device=x.device)
+            out = torch.empty(*x.shape[:-1], self.N,
+                              dtype=torch.float32 if self.f32_out else x.dtype, device=x.device)
         v = VARIANTS[variant] if isinstance(variant, str) else int(variant)
         if workspace is None:
-            workspace = self.workspace(self.workspace_bytes(rows, v, ntw, kwaves, splitk), x.device)
+            workspace = self.workspace(self.workspace_bytes(rows, v, ntw, kwaves, splitk), x.device,
+                                       stream)
         wsb = workspace.numel() if workspace is not None else 0
         _check(lib().qmm_run_ex(self._h, v, ntw, kwaves, splitk, _ptr(x), _ptr(codes), _ptr(sb),
                                 _ptr(out), rows, _ptr(workspace), wsb, _stream(stream)))
@@ -305,10 +318,10 @@ class QuantizedLinear:
     """A projection ready to run: plan + weights in the native layout."""
 
     def __init__(self, problem_or_shape, w=None, scales=None, biases=None, max_rows=None,
-                 device="cuda"):
+                 device="cuda", f32_out: bool = False):
         p = problem_or_shape
         self.plan = Plan(p.bits, p.K, p.N, max_rows or max(p.M, 1), p.x_dtype, p.sb_dtype,
-                         group_size=getattr(p, "group_size", 64))
+                         group_size=getattr(p, "group_size", 64), f32_out=f32_out)
         wd = to_device(p.w if w is None else w, device)
         sd = to_device(p.scales if scales is None else scales, device)
         bd = to_device(p.biases if biases is None else biases, device)

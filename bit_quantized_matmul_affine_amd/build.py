@@ -1,36 +1,64 @@
-"""Build libqmm.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc."""
+"""Build libqmm.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+Every source is compiled to an object in parallel (one hipcc per source),
+then the objects are linked into the shared library."""
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmm.so")
-SOURCES = ["qmm_kernels.hip", "qmm_norm.hip", "qmm_attention.hip", "qmm_generic.hip", "qmm_api.cpp"]
+SOURCES = ["qmm_layout.hip", "qmm_mfma.hip", "qmm_stream.hip", "qmm_resident.hip",
+           "qmm_slab.hip", "qmm_wide.hip", "qmm_norm.hip", "qmm_attention.hip",
+           "qmm_generic.hip", "qmm_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed-FP32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+def _compile(src: str, obj: str, verbose: bool):
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libqmm.so")
-    os.replace(tmp, LIB)
+    return subprocess.run(cmd, capture_output=True, text=True)
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    tmpdir = tempfile.mkdtemp(prefix="qmm_build_")
+    try:
+        objs = [os.path.join(tmpdir, s + ".o") for s in SOURCES]
+        jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
+        bad = [(s, r) for s, r in zip(SOURCES, results) if r.returncode != 0]
+        for s, r in bad:
+            sys.stderr.write("--- %s\n%s%s" % (s, r.stdout, r.stderr))
+        if bad:
+            raise RuntimeError("hipcc failed on " + ", ".join(s for s, _ in bad))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed linking libqmm.so")
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

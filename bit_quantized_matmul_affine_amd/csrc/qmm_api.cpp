@@ -63,6 +63,8 @@ struct qmm_plan {
   mutable std::atomic<uint64_t> launches[8];
   bool generic;  // not 3/4-bit group 64: MLX's own layout and the generic kernel
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
+  int cus;      // compute units of the device current at qmm_create
+  bool f32_out; // QMM_FLAG_F32_OUT: y is f32 whatever x_dtype
 };
 
 namespace {
@@ -133,7 +135,7 @@ bool slab_fits(const qmm_plan* p) {
 // of its workgroups per compute unit; when the tiles fit in one pass over the
 // compute units anyway, a workgroup may take a whole unit's LDS.
 size_t stream_max_lds(const qmm_plan* p) {
-  return p->nT <= device_cus() ? qmm::kMaxLdsBytes : (size_t)64 * 1024;
+  return p->nT <= p->cus ? qmm::kMaxLdsBytes : (size_t)64 * 1024;
 }
 
 int pick_variant(const qmm_plan* p, int rows, int forced) {
@@ -159,7 +161,7 @@ int pick_variant(const qmm_plan* p, int rows, int forced) {
   // as two 64-row split slab launches; 4-bit 8192->28672, 224 workgroups:
   // 85 against 155 us)
   if (rows > qmm::kMaxMfmaRows && qmm::wide_fits(p->nC) &&
-      2 * ((p->nT + qmm::kWideTiles - 1) / qmm::kWideTiles) >= device_cus())
+      2 * ((p->nT + qmm::kWideTiles - 1) / qmm::kWideTiles) >= p->cus)
     return QMM_VARIANT_WIDE;
   if (slab_fits(p)) return QMM_VARIANT_SLAB;
   return QMM_VARIANT_MFMA;
@@ -179,7 +181,7 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     // compute units take a second pass
     c.rows_per_launch = 16;
     c.tile_rows = 1;
-    const int g = std::min(device_cus(), nT);
+    const int g = std::min(p->cus, nT);
     const int r = std::min(rows, 16);
     int tm = std::min(qmm::kResidentMaxSlots, (nT + g - 1) / g);
     // four slots per unit: two workgroups of two slots each keep twice the
@@ -331,9 +333,12 @@ size_t cfg_workspace(const qmm_plan* p, const Cfg& c, int rows) {
 // The family of one row block of a call in several blocks: a choice left to
 // the library is remade for a block shorter than the call's blocks (a
 // 65-row call on the slab family: one 64-row block, then one row on the
-// streaming kernel); a forced family runs every block.
+// streaming kernel; a 129-row call on the wide kernel: one 128-row block,
+// then one row on the streaming kernel); a forced family runs every block.
 int block_variant(const qmm_plan* p, int call_variant, bool chosen, int rows, int rb) {
   if (!chosen || rb == rows || p->force_variant) return call_variant;
+  if (call_variant == QMM_VARIANT_WIDE && rb <= qmm::kMaxMfmaRows)
+    return pick_variant(p, rb, QMM_VARIANT_AUTO);
   if (call_variant != QMM_VARIANT_SLAB && call_variant != QMM_VARIANT_MFMA) return call_variant;
   return pick_variant(p, rb, QMM_VARIANT_AUTO);
 }
@@ -422,7 +427,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (!aligned(ws, 256)) return fail(QMM_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   }
   const bool xf = p->d.x_dtype == QMM_F32, sf = p->d.sb_dtype == QMM_F32;
-  const size_t xe = xf ? 4 : 2;
+  const size_t xe = xf ? 4 : 2, ye = (xf || p->f32_out) ? 4 : 2;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   for (int r0 = 0; r0 < rows; r0 += c.rows_per_launch) {
     const int rb = std::min(c.rows_per_launch, rows - r0);
@@ -432,7 +437,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     a.x = static_cast<const char*>(x) + (size_t)r0 * p->d.K * xe;
     a.codes = static_cast<const uint32_t*>(codes);
     a.sb = sb;
-    a.y = static_cast<char*>(y) + (size_t)r0 * p->d.N * xe;
+    a.y = static_cast<char*>(y) + (size_t)r0 * p->d.N * ye;
+    a.y_f32 = p->f32_out ? 1 : 0;
     a.tickets = static_cast<uint32_t*>(ws);
     a.part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + ticket_bytes(p)) : nullptr;
     a.M = rb;
@@ -478,6 +484,10 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
 
 }  // namespace
 
+namespace qmm {
+qmm_status set_error(qmm_status st, const char* msg) { return fail(st, "%s", msg); }
+}  // namespace qmm
+
 extern "C" {
 
 qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
@@ -496,7 +506,8 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
   if ((d->x_dtype != QMM_F32 && d->x_dtype != QMM_BF16) ||
       (d->sb_dtype != QMM_F32 && d->sb_dtype != QMM_BF16))
     return fail(QMM_ERR_INVALID_ARG, "unknown dtype");
-  if (d->flags != 0) return fail(QMM_ERR_INVALID_ARG, "flags must be 0");
+  if ((d->flags & ~(uint32_t)QMM_FLAG_F32_OUT) != 0)
+    return fail(QMM_ERR_INVALID_ARG, "flags=0x%x: only QMM_FLAG_F32_OUT is defined", d->flags);
   if (b != 2 && b != 3 && b != 4 && b != 8)
     return fail(QMM_ERR_UNSUPPORTED, "bits=%d: 2, 3, 4 and 8 are implemented", b);
   if (d->K % qmm::kChunkK != 0)
@@ -528,6 +539,8 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
   p->last_ntw = 0;
   p->last_splitk = 0;
   p->last_grid = 0;
+  p->cus = device_cus();
+  p->f32_out = (d->flags & QMM_FLAG_F32_OUT) != 0;
   *out = p;
   return QMM_OK;
 }
@@ -614,6 +627,8 @@ qmm_status qmm_run_gate_up(const qmm_plan* p, const void* x, const void* gate_co
     return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up kernel takes bf16 activations");
   if (p->generic)
     return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up kernel takes 3- and 4-bit group-64 weights");
+  if (p->f32_out)
+    return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up output is bf16 by definition (no QMM_FLAG_F32_OUT)");
   if (tile_pairs < 0 || tile_pairs > 2)
     return fail(QMM_ERR_INVALID_ARG, "tile_pairs must be 0 (plan's choice), 1 or 2");
   const int nT = p->nT, nC = p->nC;

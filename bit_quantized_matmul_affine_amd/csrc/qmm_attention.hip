@@ -20,12 +20,14 @@
 //   * 16 lanes per cached row (a wave covers 4 rows at once, the 16 lanes
 //     reading one row's words as one contiguous run); lane j owns values
 //     j*D/16 .. (j+1)*D/16 - 1 of a row for the score and of the output;
-//   * scores: codes become bf16 pairs 128 + c by one and-or per pair and are
-//     multiplied against q pairs with v_dot2_f32_bf16 (8-bit codes as two
-//     nibbles, the high one against 16 q); each lane removes the offset with
-//     its slice's sum of q and applies its group's scale and bias, then the
-//     16 lanes add their parts with DPP row operations, and the score is
-//     rounded to bf16;
+//   * scores in the page's factored form s * sum_d c_d q_d + b * sum_d q_d
+//     with exact products: each code becomes its exact bf16 value (one
+//     v_cvt_f32_ubyteN on the word's byte or nibble planes, then two codes
+//     per v_cvt_pk_bf16_f32; every code below 256 is exact in bf16), pairs of
+//     codes meet pairs of query values in v_dot2_f32_bf16 (8-bit by 8-bit
+//     significands: exact products), each lane applies its group's scale and
+//     bias, the 16 lanes add their parts with DPP row operations, and the
+//     score is rounded to bf16;
 //   * two passes over the block's rows held in registers: the scores first
 //     (block maximum through LDS), then the weights e^(s - M) and the values,
 //     accumulated per lane as sum p s_v c (one FMA per value) plus one
@@ -98,59 +100,13 @@ __device__ __forceinline__ void load_words(const uint32_t* __restrict__ p, uint3
   }
 }
 
-// Constants moved into an SGPR or a VGPR by instructions the compiler cannot
-// see through, so that the and-or of a pair stays one v_and_or_b32 (VOP3
-// takes no literal and at most one SGPR on this chip): mask in an SGPR,
-// or-value in a VGPR.
+// The nibble mask moved into an SGPR by an instruction the compiler cannot
+// see through, so that it is materialized once rather than as a literal in
+// every and.
 __device__ __forceinline__ uint32_t sgpr_const(uint32_t v) {
   uint32_t r;
   asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "i"(v));
   return r;
-}
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
-// Offset-128 bf16 pairs of a lane's codes.  4-bit word j: pair 4j + t holds
-// codes 8j + t (low half) and 8j + t + 4 (high half).  8-bit word j: pairs
-// 4j + t, t = 0..3, hold the low (t = 0, 1) or high (t = 2, 3) nibbles of
-// codes 4j + (t & 1) (low half) and 4j + (t & 1) + 2 (high half).
-template <int BITS, int WPL>
-__device__ __forceinline__ void code_pairs(const uint32_t* w, uint32_t* P, uint32_t mask,
-                                           uint32_t orv) {
-#pragma unroll
-  for (int j = 0; j < WPL; ++j) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int sh = BITS == 4 ? 4 * t : 8 * (t & 1) + 4 * (t >> 1);
-      P[4 * j + t] = ((w[j] >> sh) & mask) | orv;
-    }
-  }
-}
-
-// The q pairs in the same order, from the raw bf16 bits (8-bit high nibbles
-// against 16 q: exact in bf16, so the upper half of the f32 product).
-template <int BITS, int WPL>
-__device__ __forceinline__ void q_pairs(const uint32_t* qb, const float* qv, uint32_t* Q) {
-#pragma unroll
-  for (int j = 0; j < WPL; ++j) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if constexpr (BITS == 4) {
-        const int e0 = 8 * j + t, e1 = e0 + 4;
-        Q[4 * j + t] = qb[e0] | (qb[e1] << 16);
-      } else {
-        const int e0 = 4 * j + (t & 1), e1 = e0 + 2;
-        if (t >> 1)
-          Q[4 * j + t] = (__float_as_uint(qv[e0] * 16.f) >> 16) |
-                         (__float_as_uint(qv[e1] * 16.f) & 0xFFFF0000u);
-        else
-          Q[4 * j + t] = qb[e0] | (qb[e1] << 16);
-      }
-    }
-  }
 }
 
 // The lane's codes as floats, in value order: bytes of a word (8-bit), or of
@@ -180,11 +136,19 @@ __device__ __forceinline__ void code_floats(const uint32_t* w, float* c, uint32_
   }
 }
 
+// Two exact bf16 values in one word (low half first): integers below 256
+// convert exactly.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2_v v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <int BITS, int D, int REP>
 __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
   constexpr int EPL = D / kAttnLanesPerRow;  // values per lane
   constexpr int WPL = EPL * BITS / 32;       // words per lane
-  constexpr int NP = 4 * WPL;                // bf16 pairs per lane
+  constexpr int NP = EPL / 2;                // bf16 pairs per lane
   constexpr int R = kAttnRowsPerGroup;
   extern __shared__ float lds[];             // [kAttnGroups][REP][D] partial outputs
   __shared__ float red_max[kAttnThreads / 64][REP];
@@ -203,28 +167,23 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
   const uint16_t* __restrict__ vsg = reinterpret_cast<const uint16_t*>(a.vs);
   const uint16_t* __restrict__ vbg = reinterpret_cast<const uint16_t*>(a.vb);
 
-  // query slices of the REP heads: pairs for the scores and their sums
+  // query slices of the REP heads: value-order bf16 pairs for the scores,
+  // and their sums (the bias term)
   uint32_t Q[REP][NP];
   float qsum[REP];
 #pragma unroll
   for (int r = 0; r < REP; ++r) {
     const int h = kv * REP + r;
     uint32_t qb[EPL];
-    float qv[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      qb[e] = qg[(long)h * D + d0 + e];
-      qv[e] = bf16_bits_to_f32(qb[e]);
-    }
-    q_pairs<BITS, WPL>(qb, qv, Q[r]);
+    for (int e = 0; e < EPL; ++e) qb[e] = qg[(long)h * D + d0 + e];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) Q[r][p] = qb[2 * p] | (qb[2 * p + 1] << 16);
     float s = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s += qv[e];
+    for (int e = 0; e < EPL; ++e) s += bf16_bits_to_f32(qb[e]);
     qsum[r] = s;
   }
-  // offset each pair carries: 128 per code, and 16 * 128 more for the high
-  // nibbles of 8-bit codes (they multiply 16 q)
-  constexpr float kOff = BITS == 4 ? 128.f : 128.f * 17.f;
 
   // this lane group's rows: n0 + lg + 16 i (32-bit offsets from the KV
   // head's uniform base; rows past the cache re-read the last row)
@@ -258,7 +217,6 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
     vb[i] = bf16_bits_to_f32(vbh[sofs[i]]);
   }
 
-  const uint32_t pair_mask = sgpr_const(0x000F000Fu), pair_or = vgpr_const(0x43004300u);
   const uint32_t nib_mask = sgpr_const(0x0F0F0F0Fu);
 
   // pass 1: scores (bf16-rounded) and the block maximum
@@ -268,14 +226,17 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
   for (int r = 0; r < REP; ++r) mx[r] = -INFINITY;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
+    float c[EPL];
+    code_floats<BITS, WPL>(KW[i], c, nib_mask);
     uint32_t P[NP];
-    code_pairs<BITS, WPL>(KW[i], P, pair_mask, pair_or);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) P[p] = pack_bf16(c[2 * p], c[2 * p + 1]);
 #pragma unroll
     for (int r = 0; r < REP; ++r) {
       float dsum = 0.f;
 #pragma unroll
       for (int p = 0; p < NP; ++p) dsum = dot2(P[p], Q[r][p], dsum);
-      const float part = ks[i] * (dsum - kOff * qsum[r]) + kb[i] * qsum[r];
+      const float part = fmaf(ks[i], dsum, kb[i] * qsum[r]);
       const float s = round_bf16(row_sum16(part));
       sc[r][i] = valid[i] ? s : -INFINITY;
       mx[r] = fmaxf(mx[r], sc[r][i]);

@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(kGenThreads) generic_kernel(LaunchArgs a, int 
       const float v = wave_sum(acc[j][m]);
       if (lane == 0 && m < M) {
         const long idx = (long)m * a.ldy + n0 + j;
-        if constexpr (XF)
+        if (XF || a.y_f32)
           reinterpret_cast<float*>(a.y)[idx] = v;
         else
           reinterpret_cast<uint16_t*>(a.y)[idx] = to_bf16(v);

@@ -1,5 +1,5 @@
 // qmm_internal.h -- declarations shared by the C-ABI front end (qmm_api.cpp)
-// and the HIP kernels (qmm_kernels.hip).  Not installed.
+// and the HIP kernels (qmm_*.hip).  Not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,6 +29,7 @@ struct LaunchArgs {
   int ldx, ldy;           // row strides of x and y in elements
   const uint32_t* codes2; // fused gate/up: the up projection's codes (codes = gate)
   const void* sb2;        // fused gate/up: the up projection's scales/biases
+  int y_f32;              // 1: y is f32 whatever x's dtype (QMM_FLAG_F32_OUT)
 };
 
 // All launchers return hipSuccess or the launch error.
@@ -128,5 +129,6 @@ hipError_t launch_probe(const void* buf, size_t bytes, uint32_t* sink, int grid,
 
 // Bytes of LDS the vector-ALU kernel needs for `mr` rows over `kslice` columns.
 size_t gemv_lds_bytes(bool x_f32, int mr, int kslice);
+
 
 }  // namespace qmm

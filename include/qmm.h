@@ -98,6 +98,15 @@ typedef enum {
                                K a multiple of 256; bf16 activations */
 } qmm_variant;
 
+/* qmm_desc.flags.  QMM_FLAG_F32_OUT: y is written as f32 [rows, N] whatever
+ * x_dtype (the f32 sums before the output rounding), so that a test can judge
+ * the accumulation apart from the rounding to bf16 (the pages fix no output
+ * tolerance: "@mlx-bun/inference 0.0.0-stage -> 1.0.0" page,
+ * affine-split-mma.ts header comment, results are not bit-identical to
+ * MLX's).  qmm_run_gate_up rejects such plans (its output is bf16 by
+ * definition). */
+#define QMM_FLAG_F32_OUT 1u
+
 /* Shape and format of one projection.  bits: 2, 3, 4 or 8 (5 and 6 are
  * UNSUPPORTED).  group_size: 32, 64 or 128.  3- and 4-bit group-64 weights
  * run on the matrix-core families in the native layout; every other format
@@ -105,7 +114,7 @@ typedef enum {
  * multiple of 16.
  * max_rows: the largest row count qmm_run will be given (>= 1).
  * x_dtype: dtype of x and y.  sb_dtype: dtype of scales and biases.
- * flags: must be 0. */
+ * flags: 0 or QMM_FLAG_F32_OUT (other bits: QMM_ERR_INVALID_ARG). */
 typedef struct {
   int32_t bits;
   int32_t group_size;
@@ -128,7 +137,10 @@ typedef struct {
 } qmm_stats;
 
 /* Validate `desc` and build a plan (host state only; no device memory).
- * Returns QMM_OK and *out, or an error and *out = NULL. */
+ * The plan records the compute-unit count of the device current at this
+ * call (256 when no device answers), so that qmm_run validates and plans
+ * without any HIP query.  Returns QMM_OK and *out, or an error and
+ * *out = NULL. */
 qmm_status qmm_create(const qmm_desc* desc, qmm_plan** out);
 
 /* Free a plan.  NULL is allowed. */
@@ -155,17 +167,22 @@ qmm_status qmm_prepack(const qmm_plan* plan, const uint32_t* w, const void* scal
 
 /* Device workspace that qmm_run needs for `rows` rows (split-K partial sums
  * and per-tile tickets).  0 means none.  The workspace must be zero-filled
- * before its first use; every completed qmm_run leaves its ticket words at
- * zero again, so it can be reused by later calls of the same plan on the same
- * stream.  Calls that overlap in time must not share a workspace. */
+ * before its first use (a ticket counts the workgroups of one tile block that
+ * have stored their partials, and the one that finds the count complete does
+ * the fold; a count that does not start at zero cannot be told apart from
+ * one in progress).  The kernel re-arms every ticket it used to zero before
+ * it ends, so a completed qmm_run leaves the workspace ready for the next call
+ * of any plan; there is no separate clearing launch.  Calls that overlap in
+ * time must not share a workspace. */
 size_t qmm_workspace_bytes(const qmm_plan* plan, int32_t rows);
 
 /* y[rows, N] = x[rows, K] . W^T with W given in the native layout.  Rows
  * beyond one launch of the chosen family run as consecutive row blocks on
  * `stream`; a shorter last block runs on the family chosen for its own row
- * count.
+ * count.  Every argument is validated before the first HIP call.
  *   x: x_dtype [rows, K] row-contiguous, 16-byte aligned;
- *   y: x_dtype [rows, N] row-contiguous; only rows < `rows` are written;
+ *   y: x_dtype [rows, N] (f32 with QMM_FLAG_F32_OUT) row-contiguous, 4-byte
+ *   aligned; only rows < `rows` are written;
  *   workspace: >= qmm_workspace_bytes(plan, rows) bytes (may be NULL when
  *   that is 0).
  * 1 <= rows <= max_rows, else QMM_ERR_INVALID_ARG (the page's "no rows"). */

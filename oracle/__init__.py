@@ -12,6 +12,13 @@ from .oracle import (  # noqa: F401
     matmul_at,
     bound_terms,
     tolerance,
+    accumulation_terms,
+    accumulation_terms_at,
+    f32_sum_bound,
+    BF16_WEIGHT_ROUNDING,
+    rounding_step,
+    strict_tolerance,
+    check_outputs,
     build,
     load_library,
     tolerance_coefficient,
@@ -26,4 +33,5 @@ from .oracle import (  # noqa: F401
     dequant_rows,
     decode_attention,
     decode_attention_tolerance,
+    score_terms,
 )

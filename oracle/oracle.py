@@ -151,6 +151,129 @@ def bound_terms(bits: int, K: int, x, w, scales, biases, group_size: int = 64):
     return sx, mw
 
 
+def _abs_inputs(bits, K, x, w, scales, biases, group_size):
+    x, w, s, b, M, N = _prep(bits, K, x, w, scales, biases, group_size)
+    return np.abs(x), w, np.abs(s), np.abs(b)
+
+
+def accumulation_terms(bits: int, K: int, x, w, scales, biases, group_size: int = 64,
+                       threads: int = 1) -> np.ndarray:
+    """A(m,n) = sum_k (|s(n,g)| q(n,k) + |b(n,g)|) |x(m,k)|, g = k // group_size,
+    for every row and column ([M, N]).
+
+    A is the sum of the magnitudes of the terms that the pages' factored form
+    adds up, y = sum_g s_g (sum_k q_k x_k) + b_g (sum_k x_k) ("@mlx-bun/inference
+    0.0.0-stage -> 1.0.0" page, affine3-rows.ts header comment: the algebra of
+    MLX's kernels, scale times the sum of q x plus bias times the sum of x), so
+    the rounding error of any f32 evaluation of that form is bounded by a
+    multiple of A (f32_sum_bound).  Every term is non-negative, so A is the
+    oracle's own matmul over |x|, |s| and |b| (codes are non-negative)."""
+    xa, w, sa, ba = _abs_inputs(bits, K, x, w, scales, biases, group_size)
+    return matmul(bits, K, xa, w, sa, ba, group_size, threads)
+
+
+def accumulation_terms_at(bits: int, K: int, x, w, scales, biases, ms, ns,
+                          group_size: int = 64) -> np.ndarray:
+    """A(ms[i], ns[i]) of accumulation_terms for sampled output coordinates."""
+    xa, w, sa, ba = _abs_inputs(bits, K, x, w, scales, biases, group_size)
+    return matmul_at(bits, K, xa, w, sa, ba, ms, ns, group_size)
+
+
+F32_UNIT = 2.0 ** -24   # unit roundoff of f32 (round to nearest)
+
+
+BF16_WEIGHT_ROUNDING = 2.0 ** -9   # relative rounding of a weight stored as bf16
+
+
+def f32_sum_bound(K: int, acc_terms, weight_rounding: float = 0.0) -> np.ndarray:
+    """Bound on |fl(y) - y| for an f32 evaluation, in any order, of the
+    factored form over exact bf16/f32 inputs.  Along the path from any term to
+    the result there are at most K + 3 roundings: the product q*x, at most
+    group_size - 1 additions inside its group, the product with the scale or
+    bias, and at most 2*K/group_size - 1 additions of the group terms (fewer
+    than K + 3 for every group size and K >= group_size).  The standard bound
+    for such a computation (a sum whose every term passes through at most p
+    roundings of relative size u: |error| <= p u / (1 - p u) times the sum of
+    the terms' magnitudes) with p = K + 3 gives gamma * A.
+
+    weight_rounding = r: every weight is first rounded to a type of relative
+    precision r (bf16 weight operands of a matrix-core product: r = 2^-9),
+    which moves the exact sum by at most r * sum_k |x_k w_k| <= r * A (|w| <=
+    |s| q + |b|), and the f32 sums then run over terms up to (1 + r) times
+    larger: (r + gamma (1 + r)) * A."""
+    p = K + 3
+    gamma = p * F32_UNIT / (1.0 - p * F32_UNIT)
+    r = float(weight_rounding)
+    return (r + gamma * (1.0 + r)) * np.asarray(acc_terms, dtype=np.float64)
+
+
+def rounding_step(v, out_dtype: str) -> np.ndarray:
+    """The spacing of the output type's values at magnitude |v| (one unit in
+    the last place): bf16 keeps 8 significant bits, f32 24; below the
+    smallest normal the subnormal spacing (2^-133 for bf16, 2^-149 for f32)."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    sig = {"bf16": 8, "f32": 24}[out_dtype]
+    tiny = {"bf16": 2.0 ** -133, "f32": 2.0 ** -149}[out_dtype]
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    step = np.ldexp(1.0, (e - (sig - 1)).astype(np.int64))
+    return np.where((v > 0) & (step > tiny), step, tiny)
+
+
+def strict_tolerance(y_ref, acc_terms, K: int, out_dtype: str,
+                     weight_rounding: float = 0.0) -> np.ndarray:
+    """Element-wise bound a correct kernel meets whatever its summation order:
+    its f32 result differs from y_ref by at most E = f32_sum_bound(K, A); an
+    f32 output is that result itself (bound E), a bf16 output rounds it to
+    nearest, moving it by at most half a bf16 step at |y_ref| + E
+    (bound E + step/2).  weight_rounding: see f32_sum_bound."""
+    E = f32_sum_bound(K, acc_terms, weight_rounding)
+    if out_dtype == "f32":
+        return E
+    return E + 0.5 * rounding_step(np.abs(y_ref) + E, out_dtype)
+
+
+def check_outputs(y, y_ref, acc_terms, ns_tol, K: int, out_dtype: str,
+                  weight_rounding: float = 0.0):
+    """The acceptance of an output block against the oracle; returns a dict
+    with the three figures and whether each passes:
+      * bound:  max |y - y_ref| / ns_tol <= 1 (the acceptance bound above,
+        ns_tol = tolerance(...));
+      * strict: max |y - y_ref| / strict_tolerance <= 1 (a correct f32
+        evaluation of the factored form meets it in any summation order);
+      * median: the median of |y - y_ref| / ns_tol (bf16 outputs) or of
+        |y - y_ref| / E (f32 outputs) at most 0.01 or 0.05: the bulk of the
+        outputs must sit at the rounding level, not merely under the bound,
+        so a kernel-sized mistake cannot hide under a bound that grows with
+        K.
+    weight_rounding: 0 for kernels whose products use the exact weights (or
+    codes), BF16_WEIGHT_ROUNDING for a kernel that multiplies bf16-rounded
+    weights (see f32_sum_bound)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    st = strict_tolerance(y_ref, acc_terms, K, out_dtype, weight_rounding)
+    r_bound = err / ns_tol
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r_strict = np.where(err == 0, 0.0, err / st)
+    if out_dtype == "f32":
+        E = f32_sum_bound(K, acc_terms, weight_rounding)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r_med = np.where(err == 0, 0.0, err / E)
+        med_cap = 0.05
+    else:
+        r_med = r_bound
+        med_cap = 0.01
+    out = {"finite": bool(np.all(np.isfinite(y))),
+           "bound": float(np.max(r_bound)) if err.size else 0.0,
+           "strict": float(np.max(r_strict)) if err.size else 0.0,
+           "median": float(np.median(r_med)) if err.size else 0.0,
+           "median_cap": med_cap}
+    out["ok"] = (out["finite"] and out["bound"] <= 1.0 and out["strict"] <= 1.0
+                 and out["median"] <= med_cap)
+    return out
+
+
 def tolerance_coefficient(x_dtype: str) -> float:
     """c of the acceptance bound: 1e-3 for f32 activations, 8e-3 for bf16."""
     return {"f32": 1e-3, "bf16": 8e-3}[x_dtype]
@@ -307,23 +430,40 @@ def decode_attention(q, k_words, k_scales, k_biases, v_words, v_scales, v_biases
     return (out, scores) if return_scores else out
 
 
+def score_terms(q, k_words, k_scales, k_biases, bits: int, group_size: int) -> np.ndarray:
+    """T[h, n] = sum_d (|s_nd| c_nd + |b_nd|) |q_hd| over the KV head of head
+    h: the sum of the magnitudes of the terms of the page's factored score,
+    s * sum_d c_d q_d + b * sum_d q_d ("mlx-bun 0.0.4" page,
+    fused-decode-kernel.ts, SCORE_PREAMBLE comment: the dequant is factored
+    out of the inner loop).  Any f32 evaluation of that form is within
+    f32_sum_bound(D, T) of the exact score."""
+    q = np.asarray(q, dtype=np.float64)
+    H, D = q.shape
+    KV = k_words.shape[0]
+    rep = H // KV
+    codes = unpack_lsb(k_words, bits, D).astype(np.float64)          # [KV, N, D]
+    s = np.repeat(np.abs(np.asarray(k_scales, dtype=np.float64)), group_size, axis=-1)
+    b = np.repeat(np.abs(np.asarray(k_biases, dtype=np.float64)), group_size, axis=-1)
+    mag = s * codes + b                                                # [KV, N, D]
+    return np.stack([mag[h // rep] @ np.abs(q[h]) for h in range(H)])
+
+
 def decode_attention_tolerance(out_ref, q, k_words, k_scales, k_biases, v_words, v_scales,
                                v_biases, bits: int, group_size: int) -> np.ndarray:
-    """Bound on |out - out_ref| for an implementation whose score sums chain at
-    most D/16 + 8 f32 roundings per term (sums over slices of D/16 values,
-    then a tree over the slices and the affine step), in the factored form
-    that offsets each code by up to 2176 (an 8-bit code as two nibbles
-    offset by 128, the high one against 16 q, before the slice's offset is
-    removed with its sum of q): terms are at most |q_d| (|k_nd| + 2560
-    |scale_nd|), so score n's sum is off by at most
-    eps_n = (D/16 + 8) 2^-24 sum_d |q_d| (|k_nd| + 2560 |scale_nd|), which
-    moves its bf16 rounding by at most delta_n = eps_n + 2^-7 (|score_n| + eps_n).  With softmax
-    weights w_n, shifting score n by at most delta_n scales w_n by at most
-    e^(delta_n + delta_w), delta_w = log sum_m w_m e^(delta_m) (the change of
-    the normaliser), so the unrounded output moves by at most
-    sum_n w_n (e^(delta_n + delta_w) - 1) |v_n - out|; the f32 sums of the
-    weights and weighted values add (N + 8) 2^-24 max|v|; the final bf16
-    rounding of either side adds one bf16 step, 2^-7 |out|."""
+    """Bound on |out - out_ref| for an implementation that evaluates each
+    score in f32 in the page's factored form (any order) and the softmax sums
+    in f32.  The score's f32 sum is off by at most
+    eps_n = f32_sum_bound(D, T_n) (T = score_terms, the magnitudes of the
+    factored form's terms), so its bf16 rounding moves by at most
+    delta_n = eps_n + 2^-7 (|score_n| + eps_n) (one bf16 step where the two
+    sides round differently).  With softmax weights w_n, shifting score n by
+    at most delta_n scales w_n by at most e^(delta_n + delta_w),
+    delta_w = log sum_m w_m e^(delta_m) (the change of the normaliser), so
+    the unrounded output moves by at most sum_n w_n (e^(delta_n + delta_w) - 1)
+    |v_n - out|; the f32 sums of the weights and weighted values add
+    (N + 8) 2^-24 max|v|; the final bf16 rounding of either side adds one bf16
+    step, 2^-7 |out|.  Nothing here depends on how a kernel orders or splits
+    its sums."""
     q = np.asarray(q, dtype=np.float64)
     H, D = q.shape
     KV = k_words.shape[0]
@@ -331,12 +471,12 @@ def decode_attention_tolerance(out_ref, q, k_words, k_scales, k_biases, v_words,
     k = dequant_rows(k_words, k_scales, k_biases, bits, D, group_size)
     v = dequant_rows(v_words, v_scales, v_biases, bits, D, group_size)
     N = k.shape[1]
+    T = score_terms(q, k_words, k_scales, k_biases, bits, group_size)
     tol = np.empty((H, D))
     for h in range(H):
         kv = h // rep
         sig = k[kv] @ q[h]
-        ksc = np.repeat(np.abs(np.asarray(k_scales, dtype=np.float64)[kv]), group_size, axis=-1)
-        eps = (D / 16 + 8) * 2.0 ** -24 * ((np.abs(k[kv]) + 2560.0 * ksc) @ np.abs(q[h]))
+        eps = f32_sum_bound(D, T[h])
         delta = eps + 2.0 ** -7 * (np.abs(sig) + eps)
         s = round_bf16(sig)
         w = np.exp(s - s.max())

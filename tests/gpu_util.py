@@ -54,10 +54,10 @@ def y_to_f64(y_bits: np.ndarray, x_dtype: str) -> np.ndarray:
 class Runner:
     """A problem on the device: plan, native weights, activations."""
 
-    def __init__(self, p, max_rows=None, device="cuda"):
+    def __init__(self, p, max_rows=None, device="cuda", f32_out=False):
         import torch
         self.p = p
-        self.lin = b.QuantizedLinear(p, max_rows=max_rows or p.M, device=device)
+        self.lin = b.QuantizedLinear(p, max_rows=max_rows or p.M, device=device, f32_out=f32_out)
         self.x = b.to_device(p.x, device)
         torch.cuda.synchronize()
 
@@ -69,36 +69,69 @@ class Runner:
         return b.to_numpy_bits(y)
 
 
-def check_against_oracle(p, y_bits, rows=None, sample=None, threads=8, label=""):
-    """Element-wise |y - y_ref| <= tol; sample=(count, seed) checks a random
-    subset computed one by one by the oracle."""
+# oracle results of the last few full checks (the same problem is checked
+# once per kernel family); keyed by the input arrays, verified on every hit
+_ORACLE_CACHE = {}
+
+
+def check_against_oracle(p, y_bits, rows=None, sample=None, threads=8, label="",
+                         out_dtype=None, bf16_weights=False):
+    """The output block against the float64 oracle (oracle.check_outputs):
+    every element within the acceptance bound c*sum|x|*max|W| + 1e-6, every
+    element within the strict bound of an f32 evaluation of the factored form
+    (plus half a bf16 step for bf16 outputs), and the median error at the
+    rounding level.  sample=(count, seed) checks a random subset computed one
+    by one by the oracle.  out_dtype: the dtype y was written in (x's dtype
+    unless the plan asked for f32 outputs).  bf16_weights: the output came
+    from the wide kernel, whose matrix-core products take bf16-rounded
+    weights (the strict bound then adds their rounding, 2^-9 of the terms).
+    Returns the worst ratio to the acceptance bound."""
+    wr = oracle.BF16_WEIGHT_ROUNDING if bf16_weights else 0.0
     rows = rows or p.M
-    y = y_to_f64(y_bits, p.x_dtype)[:rows]
+    out_dtype = out_dtype or p.x_dtype
+    y = y_to_f64(y_bits, out_dtype)[:rows]
     x = p.x[:rows]
     gs = getattr(p, "group_size", 64)
     sx, mw = oracle.bound_terms(p.bits, p.K, x, p.w, p.scales, p.biases, group_size=gs)
     c = oracle.tolerance_coefficient(p.x_dtype)
-    if sample is None:
-        ref = oracle.matmul(p.bits, p.K, x, p.w, p.scales, p.biases, group_size=gs,
-                            threads=threads)
-        tol = c * np.outer(sx, mw) + 1e-6
-        err = np.abs(y - ref)
-        assert np.all(np.isfinite(y)), label + ": non-finite output"
-        worst = np.unravel_index(np.argmax(err / tol), err.shape)
-        ratio = float((err / tol)[worst])
-        assert ratio <= 1.0, "%s: err %.3g > tol %.3g at %s (ratio %.3f)" % (
-            label, err[worst], tol[worst], worst, ratio)
-        return ratio
-    count, seed = sample
-    rng = np.random.default_rng(seed)
-    ms = rng.integers(0, rows, count)
-    ns = rng.integers(0, p.N, count)
-    ref = oracle.matmul_at(p.bits, p.K, x, p.w, p.scales, p.biases, ms, ns, group_size=gs)
-    tol = c * sx[ms] * mw[ns] + 1e-6
-    got = y[ms, ns]
-    err = np.abs(got - ref)
     assert np.all(np.isfinite(y)), label + ": non-finite output"
-    i = int(np.argmax(err / tol))
-    ratio = float(err[i] / tol[i])
-    assert ratio <= 1.0, "%s: err %.3g > tol %.3g at (%d,%d)" % (label, err[i], tol[i], ms[i], ns[i])
-    return ratio
+    if sample is None:
+        key = (p.bits, p.K, p.N, rows, gs, p.w.ctypes.data, x.ctypes.data, p.scales.ctypes.data,
+               p.biases.ctypes.data, p.x_dtype, p.sb_dtype)
+        hit = _ORACLE_CACHE.get(key)
+        if hit is None or not all(np.array_equal(u, v) for u, v in zip(hit[0], (p.w, x, p.scales,
+                                                                               p.biases))):
+            ref = oracle.matmul(p.bits, p.K, x, p.w, p.scales, p.biases, group_size=gs,
+                                threads=threads)
+            acc = oracle.accumulation_terms(p.bits, p.K, x, p.w, p.scales, p.biases,
+                                            group_size=gs, threads=threads)
+            if len(_ORACLE_CACHE) >= 4:
+                _ORACLE_CACHE.pop(next(iter(_ORACLE_CACHE)))
+            _ORACLE_CACHE[key] = ((p.w.copy(), x.copy(), p.scales.copy(), p.biases.copy()),
+                                  ref, acc)
+        else:
+            ref, acc = hit[1], hit[2]
+        tol = c * np.outer(sx, mw) + 1e-6
+        got = y
+    else:
+        count, seed = sample
+        rng = np.random.default_rng(seed)
+        ms = rng.integers(0, rows, count)
+        ns = rng.integers(0, p.N, count)
+        ref = oracle.matmul_at(p.bits, p.K, x, p.w, p.scales, p.biases, ms, ns, group_size=gs)
+        acc = oracle.accumulation_terms_at(p.bits, p.K, x, p.w, p.scales, p.biases, ms, ns,
+                                           group_size=gs)
+        tol = c * sx[ms] * mw[ns] + 1e-6
+        got = y[ms, ns]
+    r = oracle.check_outputs(got, ref, acc, tol, p.K, out_dtype, wr)
+    err = np.abs(got - ref)
+    worst = np.unravel_index(np.argmax(err / tol), err.shape)
+    assert r["bound"] <= 1.0, "%s: err %.3g > tol %.3g at %s (ratio %.3f)" % (
+        label, err[worst], tol[worst], worst, r["bound"])
+    st = oracle.strict_tolerance(ref, acc, p.K, out_dtype, wr)
+    ws = np.unravel_index(np.argmax(err / st), err.shape)
+    assert r["strict"] <= 1.0, "%s: err %.3g > strict %.3g at %s (ratio %.3f)" % (
+        label, err[ws], st[ws], ws, r["strict"])
+    assert r["median"] <= r["median_cap"], "%s: median error ratio %.3g > %.3g" % (
+        label, r["median"], r["median_cap"])
+    return r["bound"]

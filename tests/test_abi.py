@@ -126,3 +126,20 @@ def test_format_variants_plan_on_the_generic_kernel(bits, gs):
     assert cb == 64 * 512 * bits // 8
     assert sbb == 2 * 64 * (512 // gs) * 2
     assert p.workspace_bytes(4) == 0
+
+
+def test_f32_output_flag():
+    """QMM_FLAG_F32_OUT is the one defined flag; the fused gate/up entry point
+    (bf16 output by definition) rejects such plans before any HIP call."""
+    L = b.lib()
+    h = ctypes.c_void_p()
+    d = b.QmmDesc(3, 64, 5120, 10240, 16, b.QMM_BF16, b.QMM_BF16, 2)
+    assert L.qmm_create(ctypes.byref(d), ctypes.byref(h)) == b.QMM_ERR_INVALID_ARG
+    assert h.value is None
+    p = b.Plan(3, 5120, 10240, 16, "bf16", f32_out=True)
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.qmm_run_gate_up(p.handle, fake, fake, fake, fake, fake, fake, 4, 0,
+                             None) == b.QMM_ERR_UNSUPPORTED
+    assert b"F32_OUT" in L.qmm_last_error()
+    # the same validation as any plan otherwise
+    assert L.qmm_run(p.handle, fake, fake, fake, fake, 0, None, 0, None) == b.QMM_ERR_INVALID_ARG

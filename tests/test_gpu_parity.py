@@ -242,7 +242,8 @@ def test_large_n_every_default_family():
         say("large N rows", rows)
         y = r.run(rows=rows)
         assert r.lin.plan.stats()["last_variant"] == fam, (rows, r.lin.plan.stats())
-        check_against_oracle(p, y, rows=rows, sample=(2000, rows), label="large N rows %d" % rows)
+        check_against_oracle(p, y, rows=rows, sample=(2000, rows), label="large N rows %d" % rows,
+                             bf16_weights=fam == "wide")
 
 
 def test_stats_report_the_family_that_ran():
@@ -375,7 +376,8 @@ def test_workload4_sampled(variant):
     say("workload 4", variant)
     r = Runner(p)
     y = r.run(variant=variant)
-    check_against_oracle(p, y, sample=(3000, 4), label="w4 sampled " + variant)
+    check_against_oracle(p, y, sample=(3000, 4), label="w4 sampled " + variant,
+                         bf16_weights=variant in ("auto", "wide"))
     # every output row and column is finite and rows are distinct results
     yf = oracle.decode_bf16(y)
     assert np.all(np.isfinite(yf))
@@ -441,7 +443,7 @@ def test_wide_parity(case):
     say("wide", case)
     y = r.run(variant="wide")
     assert r.lin.plan.stats()["last_variant"] == "wide"
-    check_against_oracle(p, y, label="wide %s" % (case,))
+    check_against_oracle(p, y, label="wide %s" % (case,), bf16_weights=True)
     # the same rows through the slab or MFMA families agree within the bound too
     check_against_oracle(p, r.run(variant="mfma"), label="mfma %s" % (case,))
 
@@ -460,7 +462,8 @@ def test_rows_above_64_dispatch():
         y = r.run()
         fam = r.lin.plan.stats()["last_variant"]
         assert (fam == "wide") == want_wide, (N, fam)
-        check_against_oracle(p, y, label="dispatch N=%d (%s)" % (N, fam))
+        check_against_oracle(p, y, label="dispatch N=%d (%s)" % (N, fam),
+                             bf16_weights=fam == "wide")
 
 
 def test_blocks_of_a_long_call_pick_their_own_family():
@@ -486,3 +489,109 @@ def test_wide_rejects_k_not_multiple_of_256():
         r.run(variant="wide")
     assert ei.value.status == b.QMM_ERR_UNSUPPORTED
     check_against_oracle(p, r.run(), label="K=640 above 64 rows")
+
+
+# ------------------------------------------------------------------ f32 outputs
+
+def _families(p, rows):
+    """Every family that takes `rows` rows of problem p (bf16 activations)."""
+    out = ["auto", "mfma"]
+    if rows <= 8:
+        out.append("gemv")
+    if stream_ok(p.K, rows, p.N):
+        out.append("stream")
+    if resident_ok(p.K, rows):
+        out.append("resident")
+    if p.K in (5120, 8192) and rows >= 9:
+        out.append("slab")
+    return out
+
+
+@pytest.mark.parametrize("widx,rows", [(1, 1), (2, 1), (2, 9), (2, 16), (2, 32), (2, 48),
+                                       (2, 64)])
+def test_f32_outputs_full_workloads(widx, rows):
+    """QMM_FLAG_F32_OUT: the f32 sums themselves at the full 5120 -> 10240
+    shapes, every family that takes the row count, against the strict bound
+    of an f32 evaluation of the factored form (no bf16 rounding to hide
+    behind) and the median check at the rounding level."""
+    (p,) = synth.workload(widx, M=64) if widx == 2 else synth.workload(widx)
+    r = Runner(p, max_rows=max(rows, p.M), f32_out=True)
+    q = p.rows(rows)
+    for v in _families(q, rows):
+        say("f32 out workload", widx, "rows", rows, v)
+        y = r.run(rows=rows, variant=v)
+        assert y.dtype == np.float32
+        check_against_oracle(q, y, rows=rows, label="f32 out w%d M=%d %s" % (widx, rows, v),
+                             out_dtype="f32")
+
+
+def test_f32_outputs_mlp_trio():
+    for p in synth.workload(3):
+        r = Runner(p, f32_out=True)
+        for v in _families(p, p.M):
+            say("f32 out workload 3", p.name, v)
+            check_against_oracle(p, r.run(variant=v), label="f32 out w3 %s %s" % (p.name, v),
+                                 out_dtype="f32")
+        del r
+
+
+@pytest.mark.parametrize("variant", ["auto", "wide", "slab", "mfma"])
+def test_f32_outputs_workload4_sampled(variant):
+    (p,) = synth.workload(4)
+    say("f32 out workload 4", variant)
+    r = Runner(p, f32_out=True)
+    check_against_oracle(p, r.run(variant=variant), sample=(3000, 5),
+                         label="f32 out w4 " + variant, out_dtype="f32",
+                         bf16_weights=variant in ("auto", "wide"))
+
+
+@pytest.mark.parametrize("case", [(4, 512, 64, 1, "f32", "f32"), (3, 640, 208, 5, "bf16", "bf16"),
+                                  (4, 1280, 96, 16, "bf16", "f32"), (3, 768, 48, 64, "bf16", "bf16"),
+                                  (4, 256, 32, 100, "bf16", "bf16")],
+                         ids=lambda c: "b%d_K%d_N%d_M%d_%s_%s" % c)
+def test_f32_outputs_small(case):
+    """f32 outputs on ragged small shapes, every family and K split."""
+    bits, K, N, M, xd, sd = case
+    p = synth.small(400 + M, bits=bits, K=K, N=N, M=M, x_dtype=xd, sb_dtype=sd)
+    r = Runner(p, f32_out=True)
+    fams = ["gemv"] if xd == "f32" else _families(p, M) + (["wide"] if M > 64 else [])
+    for v in fams:
+        for s in (0, 2):
+            if v not in ("gemv", "mfma") and s:
+                continue
+            label = "f32 out %s %s S=%d" % (case, v, s)
+            say(label)
+            check_against_oracle(p, r.run(variant=v, splitk=s), label=label, out_dtype="f32",
+                                 bf16_weights=v == "wide")
+
+
+def test_f32_output_rows_past_m_untouched():
+    import torch
+    p = synth.small(18, bits=3, K=5120, N=96, M=40)
+    r = Runner(p, max_rows=48, f32_out=True)
+    for v in ("auto", "slab", "mfma", "resident"):
+        rows = 16 if v == "resident" else 40
+        say("f32 out canary", v)
+        out = torch.full((rows + 3, 96), 7.0, dtype=torch.float32, device="cuda")
+        r.lin.plan.run(r.x[:rows], r.lin.codes, r.lin.sb, out=out[:rows], variant=v)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        assert np.all(o[rows:] == 7.0)
+        check_against_oracle(p.rows(rows), o[:rows], label="f32 canary " + v, out_dtype="f32")
+
+
+def test_wide_call_tail_picks_its_own_family():
+    """A 129-row call on a shape where the wide kernel is the default: one
+    128-row block on the wide kernel, then the one-row tail on the streaming
+    kernel (not a second wide launch padded to 96 rows)."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    N = 16 * 8 * cus
+    p = synth.small(129, bits=4, K=256, N=N, M=129)
+    r = Runner(p)
+    before = dict(r.lin.plan.stats()["launches"])
+    y = r.run()
+    st = r.lin.plan.stats()
+    assert st["launches"]["wide"] == before["wide"] + 1, st
+    assert st["last_variant"] == "stream", st
+    check_against_oracle(p, y, sample=(3000, 129), label="129 rows", bf16_weights=True)

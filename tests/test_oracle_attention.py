@@ -143,3 +143,71 @@ def test_tolerance_covers_every_score_rounding_flip():
         worst = max(worst, float(np.max(np.abs(moved - base) / tol)))
     assert worst <= 1.0
     assert worst > 0.05  # the bound is not vacuous: a flip uses a visible part of it
+
+
+def test_score_terms_hand_worked():
+    # one KV head, one cached row of 8 values in one group of 8 (4-bit codes
+    # 0..7), scale -0.5, bias 2; query 1, -1, 0.5, 0, 0, 0, 0, 2
+    codes = np.arange(8).reshape(1, 1, 8)
+    words = synth.pack_lsb(codes, 4)
+    s = np.array([[[-0.5]]])
+    b = np.array([[[2.0]]])
+    q = np.array([[1.0, -1.0, 0.5, 0, 0, 0, 0, 2.0]])
+    T = oracle.score_terms(q, words, s, b, 4, 8)
+    # (0.5*0 + 2)*1 + (0.5*1 + 2)*1 + (0.5*2 + 2)*0.5 + (0.5*7 + 2)*2
+    assert T.shape == (1, 1) and T[0, 0] == 2 + 2.5 + 1.5 + 11
+    # the score itself: sum_d (s c + b) q
+    k = oracle.dequant_rows(words, s, b, 4, 8, 8)
+    assert k[0, 0] @ q[0] == 2 * 1 + 1.5 * -1 + 1 * 0.5 + -1.5 * 2
+
+
+def _page_scores_f32(q, words, scales, biases, D, gs, rng):
+    """Scores of the page's factored form in float32: 4-bit codes masked in
+    place inside 16-bit words (nibble j of a half-word read as c * 16^j)
+    against the query pre-divided by 16^j, summed per group in a shuffled
+    order, then s * sum + b * sum(q), the group terms added in a shuffled
+    order."""
+    KV, N, W = words.shape
+    H = q.shape[0]
+    rep = H // KV
+    halves = np.stack([words & 0xFFFF, words >> 16], axis=-1).reshape(KV, N, 2 * W)
+    out = np.zeros((H, N))
+    for h in range(H):
+        kv = h // rep
+        qf = q[h].astype(np.float32)
+        for n in range(N):
+            terms = []
+            for g in range(D // gs):
+                ds = rng.permutation(np.arange(g * gs, (g + 1) * gs))
+                acc = np.float32(0)
+                qs = np.float32(0)
+                for d in ds:
+                    j = d % 4
+                    masked = np.float32(int(halves[kv, n, d // 4]) & (0xF << (4 * j)))
+                    acc = np.float32(acc + masked * np.float32(qf[d] / np.float32(16.0 ** j)))
+                    qs = np.float32(qs + qf[d])
+                terms += [np.float32(np.float32(scales[kv, n, g]) * acc),
+                          np.float32(np.float32(biases[kv, n, g]) * qs)]
+            tot = np.float32(0)
+            for i in rng.permutation(len(terms)):
+                tot = np.float32(tot + terms[i])
+            out[h, n] = tot
+    return out
+
+
+def test_score_bound_holds_for_f32_page_form():
+    """The score bound of decode_attention_tolerance, f32_sum_bound(D,
+    score_terms), contains f32 evaluations of the page's own factored score in
+    several summation orders; the rounding is visible (not every score is
+    exact)."""
+    q, k, v = synth.attention_inputs(21, H=4, KV=2, N=24, D=128, bits=4, group_size=64)
+    qd, ks, kb = _dec(q), _dec(k[1]), _dec(k[2])
+    kf = oracle.dequant_rows(k[0], ks, kb, 4, 128, 64)
+    exact = np.stack([kf[h // 2] @ qd[h] for h in range(4)])
+    eps = oracle.f32_sum_bound(128, oracle.score_terms(qd, k[0], ks, kb, 4, 64))
+    differs = False
+    for seed in (0, 1, 2):
+        got = _page_scores_f32(qd, k[0], ks, kb, 128, 64, np.random.default_rng(seed))
+        assert np.all(np.abs(got - exact) <= eps)
+        differs |= bool(np.any(got != exact))
+    assert differs
