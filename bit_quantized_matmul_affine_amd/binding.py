@@ -46,6 +46,7 @@ SIGNATURES = {
     "qmm_run": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _P, _c.c_size_t, _P]),
     "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P,
                               _P, _c.c_int32, _P, _c.c_size_t, _P]),
+    "qmm_run_noalloc": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _P]),
     "qmm_run_gate_up": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _c.c_int32, _c.c_int32, _P]),
     "qmm_residual_rms_norm": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _c.c_int64, _c.c_float,
                                          _c.c_int32, _P]),
@@ -226,6 +227,18 @@ class Plan:
         wsb = workspace.numel() if workspace is not None else 0
         _check(lib().qmm_run_ex(self._h, v, ntw, kwaves, splitk, _ptr(x), _ptr(codes), _ptr(sb),
                                 _ptr(out), rows, _ptr(workspace), wsb, _stream(stream)))
+        return out
+
+    def run_noalloc(self, x, codes, sb, out=None, stream=None):
+        """y = x . W^T through qmm_run_noalloc (the library's own device
+        workspace; nothing is allocated by the library)."""
+        import torch
+        rows = x.numel() // self.K
+        if out is None:
+            out = torch.empty(*x.shape[:-1], self.N,
+                              dtype=torch.float32 if self.f32_out else x.dtype, device=x.device)
+        _check(lib().qmm_run_noalloc(self._h, _ptr(x), _ptr(codes), _ptr(sb), _ptr(out), rows,
+                                     _stream(stream)))
         return out
 
     def run_gate_up(self, x, gate_codes, gate_sb, up_codes, up_sb, out=None, tile_pairs: int = 0,

@@ -267,6 +267,27 @@ qmm_status qmm_decode_attention(const void* q, const uint32_t* k_words, const vo
                                 int32_t group_size, void* workspace, size_t workspace_bytes,
                                 void* stream);
 
+/* The largest workspace qmm_run_noalloc holds on a device. */
+#define QMM_NOALLOC_MAX_WORKSPACE (8u << 20)
+
+/* qmm_run for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc.  Same
+ * arguments and results as qmm_run, without the workspace: the split-K
+ * workspace (ticket words, then partial tiles) comes from a device array of
+ * QMM_NOALLOC_MAX_WORKSPACE bytes that the library holds on every device it
+ * runs on until the process ends.  It allocates nothing (no hipMalloc,
+ * hipFree or allocating library call).  Errors: those of qmm_run, and
+ * QMM_ERR_WORKSPACE, before any HIP call, when the call needs more workspace
+ * than the array holds (qmm_workspace_bytes_ex(plan, QMM_VARIANT_AUTO, 0, 0,
+ * 0, rows) > QMM_NOALLOC_MAX_WORKSPACE; the 3-bit 5120 -> 10240 projection
+ * at 64 rows needs 5.3 MB).  All calls on one device share that device's array, which
+ * keeps the last call's contents: calls that overlap in time on one device
+ * (two streams, two host threads) race, and the caller must order them.
+ * The array's ticket words start at zero, and every completed call leaves
+ * them at zero. */
+qmm_status qmm_run_noalloc(const qmm_plan* plan, const void* x, const void* codes,
+                           const void* sb, void* y, int32_t rows, void* stream);
+
 /* Workspace needed by qmm_run_ex with the same variant/ntw/kwaves/splitk. */
 size_t qmm_workspace_bytes_ex(const qmm_plan* plan, int32_t variant, int32_t ntw,
                               int32_t kwaves, int32_t splitk, int32_t rows);

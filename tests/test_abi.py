@@ -143,3 +143,17 @@ def test_f32_output_flag():
     assert b"F32_OUT" in L.qmm_last_error()
     # the same validation as any plan otherwise
     assert L.qmm_run(p.handle, fake, fake, fake, fake, 0, None, 0, None) == b.QMM_ERR_INVALID_ARG
+
+
+def test_noalloc_refuses_oversized_calls_without_gpu():
+    """qmm_run_noalloc checks the workspace a call needs against its array
+    (QMM_NOALLOC_MAX_WORKSPACE, 8 MiB) before any HIP call."""
+    L = b.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    assert L.qmm_run_noalloc(None, fake, fake, fake, fake, 1, None) == b.QMM_ERR_INVALID_ARG
+    p = b.Plan(3, 5120, 65536, 64, "bf16")
+    assert L.qmm_workspace_bytes_ex(p.handle, 0, 0, 0, 0, 64) > 8 << 20
+    assert L.qmm_run_noalloc(p.handle, fake, fake, fake, fake, 64, None) == b.QMM_ERR_WORKSPACE
+    assert b"qmm_run_noalloc holds" in L.qmm_last_error()
+    q = b.Plan(3, 5120, 10240, 64, "bf16")
+    assert 0 < L.qmm_workspace_bytes_ex(q.handle, 0, 0, 0, 0, 64) <= 8 << 20
