@@ -40,11 +40,10 @@ def algorithmic_bytes(m: int) -> int:
     return weight_bytes() + m * K * 2 + m * N * 2
 
 
-def cpu_baseline(problem, seconds: float = 12.0):
-    """The float64 oracle on the host cores: one full step (all five row
-    counts, every output), repeated until about `seconds` have passed."""
+def _oracle_steps(problem, threads: int, seconds: float):
+    """Full steps of the float64 oracle (all five row counts, every output)
+    until about `seconds` have passed: (steps, seconds)."""
     import oracle
-    threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     reps = 0
     while True:
@@ -54,11 +53,50 @@ def cpu_baseline(problem, seconds: float = 12.0):
         reps += 1
         if time.perf_counter() - t0 >= seconds or reps >= 200:
             break
-    dt = time.perf_counter() - t0
+    return reps, time.perf_counter() - t0
+
+
+def cpu_baseline(problem, seconds: float = 10.0):
+    """The float64 oracle on the host cores, timed on all of them (the value)
+    and on one thread; the same weight-stream GB/s formula as the GPU line."""
+    threads = len(os.sched_getaffinity(0))
+    reps, dt = _oracle_steps(problem, threads, seconds)
+    reps1, dt1 = _oracle_steps(problem, 1, seconds)
     gbps = reps * len(ROWS) * weight_bytes() / dt / 1e9
+    gbps1 = reps1 * len(ROWS) * weight_bytes() / dt1 / 1e9
     return {"value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "%d full step(s): all %d outputs at each of M=%s, float64 oracle, %.1f s"
-                      % (reps, N, ",".join(map(str, ROWS)), dt)}
+                      % (reps, N, ",".join(map(str, ROWS)), dt),
+            "us_per_step": round(dt / reps * 1e6, 1),
+            "one_thread": {"value": round(gbps1, 4), "unit": "GB/s", "cores": 1,
+                           "us_per_step": round(dt1 / reps1 * 1e6, 1),
+                           "sample": "%d full step(s) on one thread, %.1f s" % (reps1, dt1)}}
+
+
+def trace_summary(path: str) -> str:
+    """Per-dispatch kernel durations from a rocprofv3 kernel trace (CSV): one
+    row per (kernel, dynamic LDS size) -- the LDS size tells the row counts of
+    one kernel apart -- with the count, median, p10, p90, min and max in us."""
+    import csv
+    groups = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (r["Kernel_Name"], int(r.get("LDS_Block_Size") or 0),
+                   int(r.get("Grid_Size_X") or 0) // max(1, int(r.get("Workgroup_Size_X") or 1)))
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            groups.setdefault(key, []).append(d)
+
+    def q(v, f):
+        return v[min(len(v) - 1, int(f * len(v)))]
+
+    lines = ["| kernel | LDS bytes | workgroups | dispatches | median us | p10 us | p90 us | min us | max us |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (name, lds, wgs), v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+        v.sort()
+        short = name.replace("void ", "").split("(")[0]
+        lines.append("| `%s` | %d | %d | %d | %.2f | %.2f | %.2f | %.2f | %.2f |" % (
+            short, lds, wgs, len(v), q(v, 0.5), q(v, 0.1), q(v, 0.9), v[0], v[-1]))
+    return "\n".join(lines)
 
 
 def kernel_source_hash() -> str:
@@ -322,6 +360,7 @@ def other_workloads(torch, binding, synth, probe):
 
 
 def main() -> int:
+    global ROWS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -334,10 +373,21 @@ def main() -> int:
                          "cache-resident numbers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read probe")
+    ap.add_argument("--rows", default=",".join(map(str, ROWS)),
+                    help="row counts of a step (default 1,9,16,32,64, the measured workload; a "
+                         "single row count serves per-row-count kernel traces)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-dispatch duration statistics (median, p10, p90) of a "
+                         "rocprofv3 --kernel-trace CSV and exit (no GPU needed)")
     ap.add_argument("--probe-only", action="store_true",
                     help="only run the HBM read probe on a 1 GiB buffer five times (a kernel of "
                          "known traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return 0
+    ROWS = tuple(int(v) for v in args.rows.split(","))
+    assert all(1 <= m <= 64 for m in ROWS), "row counts of the workload: 1..64"
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path",
