@@ -263,41 +263,116 @@ def time_norm(torch, binding, synth, rows, D, reps=5):
 def time_attention(torch, binding, synth, H, KV, N, D, bits, gs, reps=5):
     """Mean us per decode-attention call (qmm_decode_attention, both kernels)
     over a cache of KV heads x N rows; algorithmic bytes: the key and value
-    codes, scales and biases once, plus q and the output."""
+    codes, scales and biases once, plus q and the output.  Cold: each call
+    reads its own copy of the cache from a ring of copies of at least 1 GiB
+    (four times the 256 MB last-level cache); also a warm figure with one
+    cache reused (resident in the last-level cache)."""
     q, k, v = synth.attention_inputs(13, H=H, KV=KV, N=N, D=D, bits=bits, group_size=gs)
     qd = binding.to_device(q)
     kd = tuple(binding.to_device(x) for x in k)
     vd = tuple(binding.to_device(x) for x in v)
+    nbytes = sum(x.nbytes for x in k) + sum(x.nbytes for x in v) + 2 * q.nbytes
+    ring = max(2, -(-RING_BYTES // nbytes))
+    caches = [(kd, vd)] + [(tuple(x.clone() for x in kd), tuple(x.clone() for x in vd))
+                           for _ in range(ring - 1)]
     out = torch.empty_like(qd)
     need = binding.lib().qmm_attention_workspace_bytes(H, N, D)
     ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
-    n = 32
 
-    def calls():
-        for _ in range(n):
-            binding.decode_attention(qd, kd, vd, bits, gs, out=out, workspace=ws)
+    def timed(n, pick):
+        def calls():
+            for i in range(n):
+                kc, vc = pick(i)
+                binding.decode_attention(qd, kc, vc, bits, gs, out=out, workspace=ws)
 
-    calls()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
         calls()
-    g.replay()
-    torch.cuda.synchronize()
-    d = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
         g.replay()
-        e1.record()
-        e1.synchronize()
-        d.append(e0.elapsed_time(e1) * 1e3 / n)
-    del g
-    us = sum(d) / len(d)
-    nbytes = sum(x.nbytes for x in k) + sum(x.nbytes for x in v) + 2 * q.nbytes
-    return {"us": round(us, 3), "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "frac_of_8TBps": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-            "note": "cache %.1f MB stays in the 256 MB last-level cache across calls" % (nbytes / 1e6)}
+        torch.cuda.synchronize()
+        d = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            d.append(e0.elapsed_time(e1) * 1e3 / n)
+        del g
+        return sum(d) / len(d)
+
+    cold = timed(ring, lambda i: caches[i])
+    warm = timed(32, lambda i: caches[0])
+    del caches
+    torch.cuda.synchronize()
+    gb = nbytes / (cold * 1e-6) / 1e9
+    return {"us": round(cold, 3), "bytes": nbytes, "GBps": round(gb, 1),
+            "frac_of_8TBps": round(gb / HBM_PEAK_GBPS, 4),
+            "cold": "a ring of %d cache copies (%.2f GiB): each call reads its cache from HBM"
+                    % (ring, ring * nbytes / 2**30),
+            "us_cache_resident": round(warm, 3),
+            "GBps_cache_resident": round(nbytes / (warm * 1e-6) / 1e9, 1)}
+
+
+def wave_timeline(torch, binding, synth):
+    """Per-wave phase times of the streaming kernel (1 row) and the resident
+    kernel (9 and 16 rows) on the 3-bit 5120 -> 10240 workload, cold (a ring
+    of weight copies), from the timing build: each wave stamps a 100 MHz
+    device-wide counter at its phase boundaries and writes the stamps at its
+    end.  Times in us from the earliest wave start of the last launch,
+    percentiles 0/10/50/90/100 over waves.  The timing build waits for each
+    chunk's weights explicitly before stamping them (the ordinary build
+    waits at the first use)."""
+    import numpy as np
+    names = {"stream": {0: "start", 1: "activation loads issued", 2: "weight loads issued",
+                        3: "activations landed (in LDS with sums)", 12: "compute done",
+                        13: "workgroup barrier", 14: "stores issued (storing wave)"},
+             "resident": {0: "start", 1: "loads issued", 2: "activations landed",
+                          12: "compute done", 13: "workgroup barrier",
+                          14: "stores issued (storing waves)"}}
+    first_chunk = {"stream": 4, "resident": 3}
+    (prob,) = synth.workload(2, M=64)
+    out = {}
+    for fam, rows in (("stream", 1), ("resident", 9), ("resident", 16)):
+        lin = binding.QuantizedLinear(prob, max_rows=64)
+        ring = max(2, -(-RING_BYTES // weight_bytes()))
+        copies = [(lin.codes, lin.sb)] + [(lin.codes.clone(), lin.sb.clone())
+                                          for _ in range(ring - 1)]
+        x = binding.to_device(prob.x[:rows])
+        y = torch.empty(rows, N, dtype=torch.bfloat16, device="cuda")
+        ws = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            for c, sbv in copies:
+                lin.plan.run(x, c, sbv, out=y, variant=fam, workspace=ws)
+        torch.cuda.synchronize()
+        st = lin.plan.stats()
+        nw, cpw = 8, 5
+        grid = st["last_grid"] if fam == "resident" else N // 16
+        tick = ((N // 16) * 4 + 255) // 256 * 256
+        raw = ws.cpu().numpy()[tick:].view(np.uint64)[: grid * nw * 16]
+        s16 = raw.reshape(grid, nw, 16).astype(np.int64)
+        t0 = s16[:, :, 0].min()
+        rel = (s16 - t0) * 0.01                      # 100 MHz ticks -> us
+        rec = {"family": fam, "rows": rows, "workgroups": grid, "waves": grid * nw}
+        stamps = dict(names[fam])
+        for j in range(cpw):
+            stamps[first_chunk[fam] + j] = "chunk %d weights landed" % j
+        for k in sorted(stamps):
+            v = rel[:, :, k][s16[:, :, k] > 0]
+            rec[stamps[k]] = [round(float(np.percentile(v, q)), 2) for q in (0, 10, 50, 90, 100)]
+        rec["workgroup start"] = [round(float(np.percentile(rel[:, :, 0].min(axis=1), q)), 2)
+                                  for q in (0, 10, 50, 90, 100)]
+        land = 3 if fam == "stream" else 2
+        rec["activations landed, median by wave index"] = [
+            round(float(np.median(rel[:, w, land])), 2) for w in range(nw)]
+        rec["compute done, median by wave index"] = [
+            round(float(np.median(rel[:, w, 12])), 2) for w in range(nw)]
+        out["%s %d row(s)" % (fam, rows)] = rec
+        del copies, lin
+        torch.cuda.synchronize()
+    return out
 
 
 def other_workloads(torch, binding, synth, probe):
@@ -376,6 +451,9 @@ def main() -> int:
     ap.add_argument("--rows", default=",".join(map(str, ROWS)),
                     help="row counts of a step (default 1,9,16,32,64, the measured workload; a "
                          "single row count serves per-row-count kernel traces)")
+    ap.add_argument("--wave-timeline", action="store_true",
+                    help="print per-wave phase times of the streaming and resident kernels from "
+                         "the timing build (libqmm_stamps.so) and exit")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-dispatch duration statistics (median, p10, p90) of a "
                          "rocprofv3 --kernel-trace CSV and exit (no GPU needed)")
@@ -396,9 +474,14 @@ def main() -> int:
 
     import torch
     from bit_quantized_matmul_affine_amd import binding, synth
+    from bit_quantized_matmul_affine_amd import build as qbuild
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.wave_timeline:
+        binding.LIB_PATH = qbuild.STAMPS_LIB
+        print(json.dumps(wave_timeline(torch, binding, synth)), flush=True)
+        return 0
     if args.probe_only:
         gbps = measure_hbm(torch, binding, gib=1)
         print(json.dumps({"probe_bytes_per_launch": 1 << 30, "launches": 5,

@@ -123,7 +123,8 @@ bool stream_shape(const qmm_plan* p, int* nw, int* cpw) {
 // Whether a block of `rows` (<= 16) rows fits the resident kernel's LDS.
 bool resident_fits(const qmm_plan* p, int rows) {
   int nw, cpw;
-  return (size_t)rows * p->d.K * 2 <= qmm::kMaxLdsBytes && qmm::resident_shape(p->nC, 1, &nw, &cpw);
+  return (size_t)qmm::resident_rows(rows) * p->d.K * 2 <= qmm::kMaxLdsBytes &&
+         qmm::resident_shape(p->nC, 1, &nw, &cpw);
 }
 
 bool slab_fits(const qmm_plan* p) {
@@ -187,7 +188,7 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     // four slots per unit: two workgroups of two slots each keep twice the
     // waves per unit at the same tiles per unit (measured faster) where two
     // activation blocks fit its LDS
-    if (tm == 4 && 2 * (size_t)r * p->d.K * 2 <= qmm::kMaxLdsBytes) tm = 2;
+    if (tm == 4 && 2 * (size_t)qmm::resident_rows(r) * p->d.K * 2 <= qmm::kMaxLdsBytes) tm = 2;
     if (ntw_req) tm = std::max(1, std::min(ntw_req, qmm::kResidentMaxSlots));
     int nw = 0, cpw = 0;
     while (tm > 1 && !qmm::resident_shape(nC, tm, &nw, &cpw)) --tm;
@@ -634,7 +635,8 @@ qmm_status qmm_run_gate_up(const qmm_plan* p, const void* x, const void* gate_co
   const int nT = p->nT, nC = p->nC;
   const int r_max = std::min(rows, 16);
   int nw = 0, cpw = 0;
-  if ((size_t)r_max * p->d.K * 2 > qmm::kMaxLdsBytes || !qmm::gate_up_shape(nC, 1, &nw, &cpw))
+  if ((size_t)qmm::resident_rows(r_max) * p->d.K * 2 > qmm::kMaxLdsBytes ||
+      !qmm::gate_up_shape(nC, 1, &nw, &cpw))
     return fail(QMM_ERR_UNSUPPORTED,
                 "the fused gate/up kernel needs K <= 8192 and rows*K*2 bytes of activations "
                 "(rows capped at 16 per pass) to fit one compute unit's 160 KB of LDS");
@@ -662,7 +664,7 @@ qmm_status qmm_run_gate_up(const qmm_plan* p, const void* x, const void* gate_co
     a.ldy = (int)p->d.N;
     const int grid = (nT + pairs - 1) / pairs;
     a.nTB = grid;
-    const size_t lds = std::max((size_t)rb * p->d.K * 2, (size_t)2 * pairs * nw * 64 * 16);
+    const size_t lds = qmm::resident_lds_bytes(nw, 2 * pairs, rb, (int)p->d.K);
     if (hipError_t e = qmm::launch_gate_up(p->d.bits, sf, nw, cpw, pairs, a, grid, lds, st))
       return hip_fail(e, "kernel launch");
     p->launches[QMM_VARIANT_RESIDENT].fetch_add(1);

@@ -287,6 +287,39 @@ __device__ __forceinline__ ChunkRange wave_chunks(int c0, int c1, int wk, int WK
   return cr;
 }
 
+// Per-wave timestamps of the timing build (compiled with QMM_WAVE_STAMPS; in
+// ordinary builds every call below is empty).  mark(k) reads s_memrealtime,
+// a 100 MHz counter common to the whole device, into a register; flush()
+// writes the 16 stamps of the wave once, at its end, from lane 0 to
+// a.part[16 * wave_index ...] (the caller passes a workspace large enough;
+// no store happens while the kernel runs, so the stamps do not delay it).
+struct WaveStamps {
+#ifdef QMM_WAVE_STAMPS
+  uint64_t t[16];
+  uint64_t* dst;
+  __device__ __forceinline__ WaveStamps(const LaunchArgs& a, long wave_index) {
+    dst = a.part ? reinterpret_cast<uint64_t*>(a.part) + wave_index * 16 : nullptr;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t[k] = 0;
+  }
+  __device__ __forceinline__ void mark(int k) {
+    __builtin_amdgcn_sched_barrier(0);
+    t[k] = __builtin_amdgcn_s_memrealtime();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __device__ __forceinline__ void flush(int lane) {
+    if (dst && lane == 0) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dst[k] = t[k];
+    }
+  }
+#else
+  __device__ __forceinline__ WaveStamps(const LaunchArgs&, long) {}
+  __device__ __forceinline__ void mark(int) {}
+  __device__ __forceinline__ void flush(int) {}
+#endif
+};
+
 // Wait and barrier helpers of the resident and slab kernels.
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
@@ -312,6 +345,15 @@ __device__ __forceinline__ void wait_slices(int n) {
     else
       wait_slices<RPL, C - 1>(n);
   }
+}
+
+// Timing build only: wait until at most n vector-memory loads of the wave are
+// outstanding (n = the loads issued after the ones whose arrival is stamped).
+template <int N>
+__device__ __forceinline__ void stamp_wait() {
+#ifdef QMM_WAVE_STAMPS
+  wait_vm<(N < 63 ? N : 63)>();
+#endif
 }
 
 // s_waitcnt for every outstanding LDS access (vector-memory counter untouched).

@@ -57,6 +57,8 @@ hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const
 // that covers nC chunks of K (false if none does), and its dynamic LDS bytes
 // for M rows (the activation block, reused for the partial tiles).
 bool resident_shape(int nC, int tm, int* nw, int* cpw);
+// Rows of LDS a block of M rows takes (M, at most 16 per launch).
+int resident_rows(int M);
 size_t resident_lds_bytes(int nw, int tm, int M, int K);
 constexpr int kResidentMaxSlots = 4;
 // Residual add + RMS normalization (qmm_norm.hip): D a multiple of 8, at most

@@ -44,6 +44,18 @@ __device__ __forceinline__ float silu_mul(float gate, float up) {
   return silu * u;  // rounded to bf16 by the store
 }
 
+// Timing build: the wait for chunk j's weights (2*TM loads per later chunk
+// outstanding); j is a constant once the caller's loop is unrolled.
+template <int CPW, int TM, int J = 0>
+__device__ __forceinline__ void stamp_chunk(int j) {
+  if constexpr (J < CPW) {
+    if (j == J)
+      stamp_wait<(CPW - 1 - J) * TM * 2>();
+    else
+      stamp_chunk<CPW, TM, J + 1>(j);
+  }
+}
+
 template <int BITS, int NW, int CPW, int TM, typename ST, bool GU = false>
 __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   constexpr int TMH = GU ? TM / 2 : TM;  // distinct tiles per workgroup
@@ -54,6 +66,8 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   const int r = lane & 15, kg = lane >> 4;
   const int G = gridDim.x, g = blockIdx.x;
   const int nT = a.N / kTileN, nC = a.K / kChunkK;
+  WaveStamps ts(a, (long)blockIdx.x * NW + w);  // timing build only
+  ts.mark(0);
   const int M = a.M;
   const int count = nC > w ? (nC - w + NW - 1) / NW : 0;  // chunks w, w+NW, ...
   const int clast = count > 0 ? w + (count - 1) * NW : 0;  // waves without chunks re-read chunk 0
@@ -105,10 +119,12 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  ts.mark(1);
 
   // 2. this wave's activation slices have landed once at most its weight
   //    loads (two per chunk and tile) are outstanding
   wait_vm<CPW * TM * 2>();
+  ts.mark(2);
 
   // 3. compute in load order; rows past the last one read the last row
   //    (never stored)
@@ -124,6 +140,8 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   for (int j = 0; j < CPW; ++j) {
     const bool live = j < count;
     const int c = min(w + j * NW, clast);
+    stamp_chunk<CPW, TM>(j);  // timing build: wait for chunk j's weights, then
+    ts.mark(3 + j);           // stamp their arrival
     const u32x4* xrow = reinterpret_cast<const u32x4*>(lds + (size_t)c * M * 256) + xm * 16;
     u32x4 A[4];
 #pragma unroll
@@ -159,15 +177,19 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  ts.mark(12);
   // 4. add the NW partial tiles of each tile in wave order (slices are dead)
   __syncthreads();
+  ts.mark(13);
   f32x4* red = reinterpret_cast<f32x4*>(lds);  // [TM][NW][64]
 #pragma unroll
   for (int t = 0; t < TM; ++t) red[(t * NW + w) * 64 + lane] = acc[t];
   __syncthreads();
-  if (w >= TMH) return;
+  if (w >= TMH || g + w * G >= nT) {
+    ts.flush(lane);
+    return;
+  }
   const int tile = g + w * G;
-  if (tile >= nT) return;
   f32x4 v = red[(w * NW) * 64 + lane];
   for (int i = 1; i < NW; ++i) v += red[(w * NW + i) * 64 + lane];
   const int n = tile * kTileN + r;
@@ -182,6 +204,8 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
     const int m = 4 * kg + q;
     if (m < M) store_y<false>(a, (long)m * a.ldy + n, v[q]);
   }
+  ts.mark(14);
+  ts.flush(lane);
 }
 
 // (waves, chunks per wave, tile slots) shapes of the resident kernel.  The
@@ -208,8 +232,10 @@ bool resident_shape(int nC, int tm, int* nw, int* cpw) {
   return best_c > 0;
 }
 
+int resident_rows(int M) { return std::min(M, 16); }
+
 size_t resident_lds_bytes(int nw, int tm, int M, int K) {
-  return std::max((size_t)M * K * 2, (size_t)tm * nw * 64 * 16);
+  return std::max((size_t)resident_rows(M) * K * 2, (size_t)tm * nw * 64 * 16);
 }
 
 template <int BITS, typename ST>

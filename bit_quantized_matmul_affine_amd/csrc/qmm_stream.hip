@@ -40,6 +40,18 @@ __device__ __forceinline__ float dpp_sum8(float s) {
 template <int MQ, int CPW>
 struct StreamXL { static constexpr int value = (MQ * CPW * 16 + 63) / 64; };
 
+// Timing build: the wait for chunk j's weights (two loads per later chunk
+// outstanding); j is a constant once the caller's loop is unrolled.
+template <int CPW, int J = 0>
+__device__ __forceinline__ void stamp_chunk(int j) {
+  if constexpr (J < CPW) {
+    if (j == J)
+      stamp_wait<(CPW - 1 - J) * 2>();
+    else
+      stamp_chunk<CPW, J + 1>(j);
+  }
+}
+
 template <int BITS, int NW, int CPW, int MQ, typename ST>
 __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   constexpr int XL = StreamXL<MQ, CPW>::value;
@@ -54,6 +66,8 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   const int clast = count > 0 ? w + (count - 1) * NW : 0;  // waves without chunks re-read chunk 0
   const ST* __restrict__ sbp = reinterpret_cast<const ST*>(a.sb);
   const uint16_t* __restrict__ xg = reinterpret_cast<const uint16_t*>(a.x);
+  WaveStamps ts(a, (long)blockIdx.x * NW + w);  // timing build only
+  ts.mark(0);
   unsigned char* xw = lds + (size_t)w * a.M * ROWB;                           // [M][ROWB]
   float* xsum = reinterpret_cast<float*>(lds + (size_t)NW * a.M * ROWB) +
                 (size_t)w * a.M * CPW * 2;                                     // [M][CPW][2]
@@ -73,6 +87,7 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
     xo[i] = m * ROWB + j * 256 + 16 * e;
   }
   __builtin_amdgcn_sched_barrier(0);
+  ts.mark(1);
 
   // weight loads of every slot; slots past `count` re-read the last chunk
   const uint32_t* cbase = a.codes + ((long)tile * nC) * 64 * BITS + lane * BITS;
@@ -88,6 +103,7 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
     SBv[j].load(sbase + (long)c * kTileN * 4);
   }
   __builtin_amdgcn_sched_barrier(0);
+  ts.mark(2);
 
   // 2. slices and their group sums to this wave's LDS area.  The 8 lanes
   //    holding one (row, slot, group) are an aligned group of 8; lanes whose
@@ -118,6 +134,7 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  ts.mark(3);
   // 3. compute in load order; rows past the last one read the last row
   //    (never stored)
   const unsigned char* xrow = xw + min(r, a.M - 1) * ROWB + 32 * kg;
@@ -130,6 +147,8 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const bool live = j < count;
+    stamp_chunk<CPW>(j);  // timing build: wait for chunk j's weights, then
+    ts.mark(4 + j);       // stamp their arrival
     u32x4 A[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -158,11 +177,16 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  ts.mark(12);
   // 4. add the NW partial tiles in wave order and store rows < M
   f32x4* red = reinterpret_cast<f32x4*>(lds + (size_t)NW * a.M * (ROWB + CPW * 8));  // [NW-1][64]
   if (w > 0) red[(w - 1) * 64 + lane] = acc;
   __syncthreads();
-  if (w != 0) return;
+  ts.mark(13);
+  if (w != 0) {
+    ts.flush(lane);
+    return;
+  }
 #pragma unroll
   for (int i = 1; i < NW; ++i) acc += red[(i - 1) * 64 + lane];
   const int n = tile * kTileN + r;
@@ -171,6 +195,8 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
     const int m = 4 * kg + q;
     if (m < a.M) store_y<false>(a, (long)m * a.ldy + n, acc[q]);
   }
+  ts.mark(14);
+  ts.flush(lane);
 }
 
 size_t stream_lds_bytes(int nw, int cpw, int M) {
