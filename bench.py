@@ -412,14 +412,15 @@ def other_workloads(torch, binding, synth, probe):
         "us": round(us, 3), "weight_GBps": round(p4.weight_bytes / (us * 1e-6) / 1e9, 1),
         "tflops": round(tf, 2), "frac_of_bf16_mfma_peak": round(tf / 2500.0, 4), "variant": v}
     fmt = {}
-    for bits, gs in ((2, 64), (8, 64), (4, 128), (4, 32)):
-        pf = synth.small(900 + bits + gs, bits=bits, K=5120, N=10240, M=1, group_size=gs)
-        us, v = time_workload(torch, binding, pf, 1)
-        gb = pf.weight_bytes / (us * 1e-6) / 1e9
-        fmt["%d-bit group-%d" % (bits, gs)] = {
-            "us": round(us, 3), "weight_bytes": pf.weight_bytes, "weight_GBps": round(gb, 1),
-            "variant": v, "frac_of_measured_peak": round(gb / probe, 4) if probe else None}
-    out["format variants 5120->10240, 1 row, bf16 (generic kernel)"] = fmt
+    for bits, gs in ((2, 64), (2, 32), (8, 64), (8, 128), (3, 32), (4, 32), (4, 128), (3, 128)):
+        pf = synth.small(900 + bits + gs, bits=bits, K=5120, N=10240, M=16, group_size=gs)
+        for rows in (1, 16):
+            us, v = time_workload(torch, binding, pf, rows)
+            gb = pf.weight_bytes / (us * 1e-6) / 1e9
+            fmt["%d-bit group-%d, %d row%s" % (bits, gs, rows, "s" if rows > 1 else "")] = {
+                "us": round(us, 3), "weight_bytes": pf.weight_bytes, "weight_GBps": round(gb, 1),
+                "variant": v, "frac_of_measured_peak": round(gb / probe, 4) if probe else None}
+    out["format variants 5120->10240, bf16 (generic: the step-layout kernel)"] = fmt
     out["residual add + RMS norm, bf16"] = {
         "4x3840 (decode)": time_norm(torch, binding, synth, 4, 3840),
         "16384x5120 (HBM-bound)": time_norm(torch, binding, synth, 16384, 5120)}

@@ -22,7 +22,7 @@ STAMPS_LIB = os.path.join(PKG, "libqmm_stamps.so")
 STAMPED = ("qmm_stream.hip", "qmm_resident.hip")
 SOURCES = ["qmm_layout.hip", "qmm_mfma.hip", "qmm_stream.hip", "qmm_resident.hip",
            "qmm_slab.hip", "qmm_wide.hip", "qmm_norm.hip", "qmm_attention.hip",
-           "qmm_generic.hip", "qmm_noalloc.hip", "qmm_api.cpp"]
+           "qmm_generic.hip", "qmm_fmt.hip", "qmm_noalloc.hip", "qmm_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

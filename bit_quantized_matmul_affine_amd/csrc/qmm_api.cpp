@@ -61,7 +61,8 @@ struct qmm_plan {
   int force_variant;  // from QMM_FORCE_VARIANT, 0 = none
   int env_ntw, env_splitk, env_kwaves;
   mutable std::atomic<uint64_t> launches[8];
-  bool generic;  // not 3/4-bit group 64: MLX's own layout and the generic kernel
+  bool generic;  // other formats on MLX's own layout and the vector-ALU kernel
+  bool fmt;      // other formats on the step layout and the matrix-core kernel (qmm_fmt.hip)
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
   int cus;      // compute units of the device current at qmm_create
   bool f32_out; // QMM_FLAG_F32_OUT: y is f32 whatever x_dtype
@@ -140,7 +141,7 @@ size_t stream_max_lds(const qmm_plan* p) {
 }
 
 int pick_variant(const qmm_plan* p, int rows, int forced) {
-  if (p->generic) return QMM_VARIANT_GENERIC;
+  if (p->generic || p->fmt) return QMM_VARIANT_GENERIC;
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
   if (p->force_variant) return p->force_variant;
@@ -213,6 +214,27 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.nTB = (nT + qmm::kWideTiles - 1) / qmm::kWideTiles;
     c.grid = c.nTB;
     c.lds = qmm::wide_lds_bytes(c.tile_rows);
+    return c;
+  }
+  if (variant == QMM_VARIANT_GENERIC && p->fmt) {
+    // the resident kernel's plan: as few tile slots as fill every compute
+    // unit once (fewer where the wave's weights would not fit its registers)
+    c.rows_per_launch = qmm::fmt_rows(p->d.K);
+    c.tile_rows = 1;
+    const int g = std::min(p->cus, nT);
+    int tm = std::min(qmm::kFmtMaxSlots, (nT + g - 1) / g);
+    if (ntw_req) tm = std::max(1, std::min(ntw_req, qmm::kFmtMaxSlots));
+    const int bits = p->d.bits, gs = p->d.group_size;
+    int nw = 0, cpw = 0;
+    while (tm > 1 && !qmm::fmt_shape(bits, gs, nC, tm, &nw, &cpw)) --tm;
+    qmm::fmt_shape(bits, gs, nC, tm, &nw, &cpw);
+    c.ntw = tm;
+    c.cpw = cpw;
+    c.wk = nw;
+    c.grid = (nT + tm - 1) / tm;
+    c.nTB = c.grid;
+    c.S = 1;
+    c.lds = qmm::fmt_lds_bytes(nw, tm, std::min(rows, c.rows_per_launch), (int)p->d.K);
     return c;
   }
   if (variant == QMM_VARIANT_GENERIC) {
@@ -382,13 +404,15 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
   if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_WIDE)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
-  if (p->generic && variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GENERIC)
+  const bool other = p->generic || p->fmt;
+  if (other && variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GENERIC)
     return fail(QMM_ERR_UNSUPPORTED,
-                "bits=%d group_size=%d run only on the generic kernel (QMM_VARIANT_GENERIC)",
+                "bits=%d group_size=%d run only on the other formats' kernel (QMM_VARIANT_GENERIC)",
                 p->d.bits, p->d.group_size);
-  if (!p->generic && variant_req == QMM_VARIANT_GENERIC)
+  if (!other && variant_req == QMM_VARIANT_GENERIC)
     return fail(QMM_ERR_UNSUPPORTED,
-                "3- and 4-bit group-64 plans use the native layout, not the generic kernel");
+                "3- and 4-bit plans with groups of 64 or 128 use the native layout, not the "
+                "other formats' kernel");
   if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM ||
        variant_req == QMM_VARIANT_RESIDENT || variant_req == QMM_VARIANT_SLAB ||
        variant_req == QMM_VARIANT_WIDE) &&
@@ -452,7 +476,10 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (vb == QMM_VARIANT_GENERIC)
+    if (vb == QMM_VARIANT_GENERIC && p->fmt)
+      e = qmm::launch_fmt(p->d.bits, p->d.group_size, cb.wk, cb.cpw, cb.ntw, a, cb.grid, cb.lds,
+                          st);
+    else if (vb == QMM_VARIANT_GENERIC)
       e = qmm::launch_generic(p->d.bits, p->d.group_size, xf, sf, rb, a, st);
     else if (vb == QMM_VARIANT_WIDE)
       e = qmm::launch_wide(p->d.bits, sf, cb.tile_rows, a, cb.grid, cb.lds, st);
@@ -521,9 +548,17 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
   qmm_plan* p = new (std::nothrow) qmm_plan();
   if (!p) return fail(QMM_ERR_INVALID_ARG, "out of host memory");
   p->d = *d;
-  p->generic = !((b == 3 || b == 4) && d->group_size == 64);
   p->nT = (int)(d->N / qmm::kTileN);
   p->nC = (int)(d->K / qmm::kChunkK);
+  // 3- and 4-bit codes with groups of 64 or 128: the native layout; the
+  // other formats with bf16 activations and scales: the step layout where
+  // its kernel covers K; else MLX's layout on the vector-ALU kernel
+  const bool native = (b == 3 || b == 4) && (d->group_size == 64 || d->group_size == 128);
+  int fnw = 0, fcpw = 0;
+  p->fmt = !native && d->x_dtype == QMM_BF16 && d->sb_dtype == QMM_BF16 &&
+           qmm::fmt_format(b, d->group_size) && qmm::fmt_rows(d->K) >= 1 &&
+           qmm::fmt_shape(b, d->group_size, p->nC, 1, &fnw, &fcpw);
+  p->generic = !native && !p->fmt;
   p->force_variant = 0;
   if (const char* v = getenv("QMM_FORCE_VARIANT")) {
     if (!strcmp(v, "gemv")) p->force_variant = QMM_VARIANT_GEMV;
@@ -552,7 +587,10 @@ qmm_status qmm_packed_bytes(const qmm_plan* p, size_t* codes_bytes, size_t* sb_b
   if (qmm_status st = check_plan(p)) return st;
   if (!codes_bytes || !sb_bytes) return fail(QMM_ERR_INVALID_ARG, "NULL output pointer");
   *codes_bytes = (size_t)p->d.N * p->d.K * p->d.bits / 8;
-  *sb_bytes = (size_t)2 * p->d.N * (p->d.K / p->d.group_size) * (p->d.sb_dtype == QMM_F32 ? 4 : 2);
+  // the native layout holds a scale and a bias per 64 values (a group of
+  // 128 gives both halves its pair)
+  const int64_t per = (p->generic || p->fmt) ? p->d.group_size : 64;
+  *sb_bytes = (size_t)2 * p->d.N * (p->d.K / per) * (p->d.sb_dtype == QMM_F32 ? 4 : 2);
   return QMM_OK;
 }
 
@@ -577,9 +615,15 @@ qmm_status qmm_prepack(const qmm_plan* p, const uint32_t* w, const void* scales,
     if (e != hipSuccess) return hip_fail(e, "prepack copy");
     return QMM_OK;
   }
-  hipError_t e = qmm::launch_repack(p->d.bits, p->d.sb_dtype == QMM_F32, w, scales, biases,
-                                    static_cast<uint32_t*>(codes_out), sb_out, (int)p->d.N,
-                                    (int)p->d.K, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e;
+  if (p->fmt)
+    e = qmm::launch_repack_fmt(p->d.bits, p->d.group_size, w, scales, biases,
+                               static_cast<uint32_t*>(codes_out), sb_out, (int)p->d.N,
+                               (int)p->d.K, reinterpret_cast<hipStream_t>(stream));
+  else
+    e = qmm::launch_repack(p->d.bits, p->d.group_size, p->d.sb_dtype == QMM_F32, w, scales,
+                           biases, static_cast<uint32_t*>(codes_out), sb_out, (int)p->d.N,
+                           (int)p->d.K, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "repack launch");
   return QMM_OK;
 }
@@ -626,8 +670,9 @@ qmm_status qmm_run_gate_up(const qmm_plan* p, const void* x, const void* gate_co
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, h 4-byte aligned");
   if (p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up kernel takes bf16 activations");
-  if (p->generic)
-    return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up kernel takes 3- and 4-bit group-64 weights");
+  if (p->generic || p->fmt)
+    return fail(QMM_ERR_UNSUPPORTED,
+                "the fused gate/up kernel takes 3- and 4-bit weights with groups of 64 or 128");
   if (p->f32_out)
     return fail(QMM_ERR_UNSUPPORTED, "the fused gate/up output is bf16 by definition (no QMM_FLAG_F32_OUT)");
   if (tile_pairs < 0 || tile_pairs > 2)
@@ -764,12 +809,13 @@ qmm_status qmm_decode_attention(const void* q, const uint32_t* k_words, const vo
 qmm_status qmm_debug_unpack(const qmm_plan* p, const void* codes, uint8_t* out, void* stream) {
   if (qmm_status st = check_plan(p)) return st;
   if (p->generic)
-    return fail(QMM_ERR_UNSUPPORTED, "the generic kernel keeps MLX's layout: nothing to unpack");
+    return fail(QMM_ERR_UNSUPPORTED, "the vector-ALU kernel keeps MLX's layout: nothing to unpack");
   if (!codes || !out) return fail(QMM_ERR_INVALID_ARG, "NULL pointer");
   if (!aligned(codes, 4)) return fail(QMM_ERR_INVALID_ARG, "misaligned codes");
-  hipError_t e = qmm::launch_debug_unpack(p->d.bits, static_cast<const uint32_t*>(codes), out,
-                                          (int)p->d.N, (int)p->d.K,
-                                          reinterpret_cast<hipStream_t>(stream));
+  const uint32_t* cw = static_cast<const uint32_t*>(codes);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = p->fmt ? qmm::launch_debug_unpack_fmt(p->d.bits, cw, out, (int)p->d.N, (int)p->d.K, st)
+                        : qmm::launch_debug_unpack(p->d.bits, cw, out, (int)p->d.N, (int)p->d.K, st);
   if (e != hipSuccess) return hip_fail(e, "debug unpack launch");
   return QMM_OK;
 }

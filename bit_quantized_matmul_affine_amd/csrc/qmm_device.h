@@ -334,6 +334,13 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// wait_vm<N>() that also waits for every outstanding LDS access.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
 // wait_vm<n * RPL>() for a count n in 0..C known once the caller is unrolled.
 template <int RPL, int C>
 __device__ __forceinline__ void wait_slices(int n) {

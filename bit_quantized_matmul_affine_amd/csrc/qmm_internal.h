@@ -33,9 +33,11 @@ struct LaunchArgs {
 };
 
 // All launchers return hipSuccess or the launch error.
-hipError_t launch_repack(int bits, bool sb_f32, const uint32_t* w, const void* scales,
-                         const void* biases, uint32_t* codes, void* sb, int N, int K,
-                         hipStream_t st);
+// Native layout (3- and 4-bit codes, groups of 64 or 128 values): a group of
+// 128 gives both 64-value halves of a chunk its scale and bias.
+hipError_t launch_repack(int bits, int group_size, bool sb_f32, const uint32_t* w,
+                         const void* scales, const void* biases, uint32_t* codes, void* sb, int N,
+                         int K, hipStream_t st);
 hipError_t launch_debug_unpack(int bits, const uint32_t* codes, uint8_t* out, int N, int K,
                                hipStream_t st);
 hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, int wk, const LaunchArgs& a,
@@ -69,6 +71,30 @@ constexpr int kResidentMaxSlots = 4;
 constexpr int kGenericMaxRows = 2;
 hipError_t launch_generic(int bits, int group_size, bool x_f32, bool sb_f32, int rows,
                           const LaunchArgs& a, hipStream_t st);
+
+// Step layout and matrix-core kernel of the other formats (qmm_fmt.hip):
+// 2- and 8-bit codes with groups of 32, 64 or 128, 3- and 4-bit codes with
+// groups of 32; bf16 activations and bf16 scales/biases.  Up to fmt_rows(K)
+// activation rows (at most 16, their block in one compute unit's LDS) per
+// launch; (waves, chunks per wave) for `tm` tile slots from fmt_shape, which
+// keeps a wave's weight registers (cpw * tm * (bits + 128/group_size) words)
+// within fmt_regs_fit: 128 words with up to 8 waves (two per SIMD), 80 with
+// 16 (four per SIMD, 128 registers each).
+constexpr bool fmt_regs_fit(int bits, int group_size, int nw, int cpw, int tm) {
+  return cpw * tm * (bits + 128 / group_size) <= (nw >= 16 ? 80 : 128);
+}
+constexpr int kFmtMaxSlots = 3;
+bool fmt_format(int bits, int group_size);
+bool fmt_shape(int bits, int group_size, int nC, int tm, int* nw, int* cpw);
+int fmt_rows(long K);
+size_t fmt_lds_bytes(int nw, int tm, int M, int K);
+hipError_t launch_fmt(int bits, int group_size, int nw, int cpw, int tm, const LaunchArgs& a,
+                      int grid, size_t lds_bytes, hipStream_t st);
+hipError_t launch_repack_fmt(int bits, int group_size, const uint32_t* w, const void* scales,
+                             const void* biases, uint32_t* codes, void* sb, int N, int K,
+                             hipStream_t st);
+hipError_t launch_debug_unpack_fmt(int bits, const uint32_t* codes, uint8_t* out, int N, int K,
+                                   hipStream_t st);
 
 // Decode attention over an affine-quantized KV cache: kAttnBlock cached rows
 // per workgroup of the block kernel; partial outputs [H, G, D] and

@@ -18,7 +18,8 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint32_t* __restrict_
                                                      const ST* __restrict__ scales,
                                                      const ST* __restrict__ biases,
                                                      uint32_t* __restrict__ codes,
-                                                     ST* __restrict__ sb, int N, int K) {
+                                                     ST* __restrict__ sb, int N, int K,
+                                                     int gs) {
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   const int nC = K / kChunkK, nT = N / kTileN;
   if (gid >= (long)nT * nC * 64) return;
@@ -36,12 +37,14 @@ __global__ void __launch_bounds__(256) repack_kernel(const uint32_t* __restrict_
 #pragma unroll
   for (int j = 0; j < BITS; ++j) codes[blk * 64 * BITS + lane * BITS + j] = out[j];
   if (kg == 0) {
-    const int G = K / 64;
+    // the groups of the chunk's two 64-value halves (one group of 128 serves both)
+    const int G = K / gs;
+    const long g0 = (long)n * G + (long)kChunkK * c / gs, g1 = (long)n * G + (kChunkK * c + 64) / gs;
     ST* e = sb + (blk * kTileN + r) * 4;
-    e[0] = scales[(long)n * G + 2 * c];
-    e[1] = scales[(long)n * G + 2 * c + 1];
-    e[2] = biases[(long)n * G + 2 * c];
-    e[3] = biases[(long)n * G + 2 * c + 1];
+    e[0] = scales[g0];
+    e[1] = scales[g1];
+    e[2] = biases[g0];
+    e[3] = biases[g1];
   }
 }
 
@@ -98,19 +101,19 @@ __global__ void __launch_bounds__(256) probe_kernel(const u32x4* __restrict__ bu
 // ---------------------------------------------------------------------------
 static inline unsigned blocks_for(long threads, int per) { return (unsigned)((threads + per - 1) / per); }
 
-hipError_t launch_repack(int bits, bool sb_f32, const uint32_t* w, const void* scales,
+hipError_t launch_repack(int bits, int gs, bool sb_f32, const uint32_t* w, const void* scales,
                          const void* biases, uint32_t* codes, void* sb, int N, int K,
                          hipStream_t st) {
   const long threads = (long)(N / kTileN) * (K / kChunkK) * 64;
   const unsigned grid = blocks_for(threads, 256);
   if (bits == 3 && !sb_f32)
-    repack_kernel<3, uint16_t><<<grid, 256, 0, st>>>(w, (const uint16_t*)scales, (const uint16_t*)biases, codes, (uint16_t*)sb, N, K);
+    repack_kernel<3, uint16_t><<<grid, 256, 0, st>>>(w, (const uint16_t*)scales, (const uint16_t*)biases, codes, (uint16_t*)sb, N, K, gs);
   else if (bits == 3)
-    repack_kernel<3, float><<<grid, 256, 0, st>>>(w, (const float*)scales, (const float*)biases, codes, (float*)sb, N, K);
+    repack_kernel<3, float><<<grid, 256, 0, st>>>(w, (const float*)scales, (const float*)biases, codes, (float*)sb, N, K, gs);
   else if (!sb_f32)
-    repack_kernel<4, uint16_t><<<grid, 256, 0, st>>>(w, (const uint16_t*)scales, (const uint16_t*)biases, codes, (uint16_t*)sb, N, K);
+    repack_kernel<4, uint16_t><<<grid, 256, 0, st>>>(w, (const uint16_t*)scales, (const uint16_t*)biases, codes, (uint16_t*)sb, N, K, gs);
   else
-    repack_kernel<4, float><<<grid, 256, 0, st>>>(w, (const float*)scales, (const float*)biases, codes, (float*)sb, N, K);
+    repack_kernel<4, float><<<grid, 256, 0, st>>>(w, (const float*)scales, (const float*)biases, codes, (float*)sb, N, K, gs);
   return hipGetLastError();
 }
 

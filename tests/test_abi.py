@@ -119,13 +119,22 @@ def test_automatic_workspace_follows_the_row_blocks():
 @pytest.mark.parametrize("bits,gs", [(2, 32), (2, 64), (2, 128), (3, 32), (3, 128), (4, 32),
                                      (4, 128), (8, 32), (8, 64), (8, 128)])
 def test_format_variants_plan_on_the_generic_kernel(bits, gs):
-    """Every other MLX format builds a plan whose packed buffers are MLX's own
-    byte counts (codes; scales then biases) and that needs no workspace."""
-    p = b.Plan(bits, 512, 64, 4, "bf16", group_size=gs)
-    cb, sbb = p.packed_bytes()
-    assert cb == 64 * 512 * bits // 8
-    assert sbb == 2 * 64 * (512 // gs) * 2
-    assert p.workspace_bytes(4) == 0
+    """Every other MLX format builds a plan whose packed codes keep MLX's
+    byte count and that needs no workspace; its scales and biases keep their
+    count too.  3- and 4-bit groups of 128 go to the native layout, which
+    stores the pair once per 64 values (the group's pair for each half), with
+    the group-64 plan's workspace."""
+    for sb_dtype, size in (("bf16", 2), ("f32", 4)):
+        p = b.Plan(bits, 512, 64, 4, "bf16", sb_dtype=sb_dtype, group_size=gs)
+        cb, sbb = p.packed_bytes()
+        assert cb == 64 * 512 * bits // 8
+        native = bits in (3, 4) and gs == 128
+        assert sbb == 2 * 64 * (512 // (64 if native else gs)) * size
+        if native:  # the workspace of the group-64 plan of the same shape
+            q = b.Plan(bits, 512, 64, 4, "bf16", sb_dtype=sb_dtype)
+            assert p.workspace_bytes(4) == q.workspace_bytes(4)
+        else:
+            assert p.workspace_bytes(4) == 0
 
 
 def test_f32_output_flag():
