@@ -62,7 +62,9 @@ struct qmm_plan {
   int env_ntw, env_splitk, env_kwaves;
   mutable std::atomic<uint64_t> launches[8];
   bool generic;  // other formats on MLX's own layout and the vector-ALU kernel
-  bool fmt;      // other formats on the step layout and the matrix-core kernel (qmm_fmt.hip)
+  bool fmt;      // other formats on the step layout: streaming and resident kernels
+  int step_gs;   // fmt: the group size (selects the step-layout kernels); else 0
+  int groups;    // quantization groups per 128-value chunk in the kernels' layout
   mutable std::atomic<int> last_variant, last_ntw, last_splitk, last_grid;
   int cus;      // compute units of the device current at qmm_create
   bool f32_out; // QMM_FLAG_F32_OUT: y is f32 whatever x_dtype
@@ -121,11 +123,17 @@ bool stream_shape(const qmm_plan* p, int* nw, int* cpw) {
   return false;
 }
 
+// Rows the resident kernel takes per launch: 16 for the native layout (the
+// family is chosen only where they fit), for the step layout as many as fit
+// one compute unit's LDS (it is their only family beyond the streaming one).
+int resident_launch_rows(const qmm_plan* p) { return p->fmt ? qmm::fmt_rows(p->d.K) : 16; }
+
 // Whether a block of `rows` (<= 16) rows fits the resident kernel's LDS.
 bool resident_fits(const qmm_plan* p, int rows) {
   int nw, cpw;
-  return (size_t)qmm::resident_rows(rows) * p->d.K * 2 <= qmm::kMaxLdsBytes &&
-         qmm::resident_shape(p->nC, 1, &nw, &cpw);
+  const int r = std::min(qmm::resident_rows(rows), resident_launch_rows(p));
+  return r >= 1 && (size_t)r * p->d.K * 2 <= qmm::kMaxLdsBytes &&
+         qmm::resident_shape(p->d.bits, p->step_gs, p->nC, 1, &nw, &cpw);
 }
 
 bool slab_fits(const qmm_plan* p) {
@@ -140,22 +148,35 @@ size_t stream_max_lds(const qmm_plan* p) {
   return p->nT <= p->cus ? qmm::kMaxLdsBytes : (size_t)64 * 1024;
 }
 
+// Whether the streaming kernel takes a block of `rows` rows (at most
+// kStreamMaxRows) of this plan.
+bool stream_ok(const qmm_plan* p, int rows) {
+  int nw, cpw;
+  return stream_shape(p, &nw, &cpw) &&
+         qmm::stream_fits(nw, cpw, rows, p->groups, stream_max_lds(p)) &&
+         (!p->fmt || qmm::stream_step_fits(p->d.bits, p->d.group_size, nw, cpw));
+}
+
 int pick_variant(const qmm_plan* p, int rows, int forced) {
-  if (p->generic || p->fmt) return QMM_VARIANT_GENERIC;
+  if (p->generic) return QMM_VARIANT_GENERIC;
   if (p->d.x_dtype == QMM_F32) return QMM_VARIANT_GEMV;
   if (forced) return forced;
+  if (p->fmt) {
+    // the step layout runs on the streaming and resident kernels only
+    if (p->force_variant == QMM_VARIANT_STREAM || p->force_variant == QMM_VARIANT_RESIDENT)
+      return p->force_variant;
+    return rows <= 2 && stream_ok(p, rows) ? QMM_VARIANT_STREAM : QMM_VARIANT_RESIDENT;
+  }
   if (p->force_variant) return p->force_variant;
   // Measured on the 3-bit 5120->10240 sweep and the 4-bit MLP shapes: the
   // streaming kernel for one or two rows; the resident kernel up to 16 rows
   // while the activation block fits one compute unit's LDS; the streaming
   // kernel up to 4 rows beyond that; then the slab kernel where it is built
   // for this K; else MFMA.
-  int nw, cpw;
-  const bool stream_ok = stream_shape(p, &nw, &cpw) &&
-                         qmm::stream_fits(nw, cpw, rows, stream_max_lds(p));
-  if (rows <= 2 && stream_ok) return QMM_VARIANT_STREAM;
+  const bool streams = stream_ok(p, rows);
+  if (rows <= 2 && streams) return QMM_VARIANT_STREAM;
   if (rows <= 16 && resident_fits(p, rows)) return QMM_VARIANT_RESIDENT;
-  if (stream_ok) return QMM_VARIANT_STREAM;
+  if (streams) return QMM_VARIANT_STREAM;
   // more than 64 rows: the wide kernel (bf16 weights, no per-group epilogue)
   // where its grid (eight W tiles per workgroup) fills at least half the
   // compute units; else 64-row blocks on the slab or MFMA kernels (3-bit
@@ -181,10 +202,10 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     // as few tile slots as fill every compute unit once (fewer where no
     // built shape covers this K with that many); more tiles than slots x
     // compute units take a second pass
-    c.rows_per_launch = 16;
+    c.rows_per_launch = resident_launch_rows(p);
     c.tile_rows = 1;
     const int g = std::min(p->cus, nT);
-    const int r = std::min(rows, 16);
+    const int r = std::min(rows, c.rows_per_launch);
     int tm = std::min(qmm::kResidentMaxSlots, (nT + g - 1) / g);
     // four slots per unit: two workgroups of two slots each keep twice the
     // waves per unit at the same tiles per unit (measured faster) where two
@@ -192,8 +213,8 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     if (tm == 4 && 2 * (size_t)qmm::resident_rows(r) * p->d.K * 2 <= qmm::kMaxLdsBytes) tm = 2;
     if (ntw_req) tm = std::max(1, std::min(ntw_req, qmm::kResidentMaxSlots));
     int nw = 0, cpw = 0;
-    while (tm > 1 && !qmm::resident_shape(nC, tm, &nw, &cpw)) --tm;
-    qmm::resident_shape(nC, tm, &nw, &cpw);
+    while (tm > 1 && !qmm::resident_shape(p->d.bits, p->step_gs, nC, tm, &nw, &cpw)) --tm;
+    qmm::resident_shape(p->d.bits, p->step_gs, nC, tm, &nw, &cpw);
     c.ntw = tm;
     c.cpw = cpw;
     c.wk = nw;
@@ -214,27 +235,6 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.nTB = (nT + qmm::kWideTiles - 1) / qmm::kWideTiles;
     c.grid = c.nTB;
     c.lds = qmm::wide_lds_bytes(c.tile_rows);
-    return c;
-  }
-  if (variant == QMM_VARIANT_GENERIC && p->fmt) {
-    // the resident kernel's plan: as few tile slots as fill every compute
-    // unit once (fewer where the wave's weights would not fit its registers)
-    c.rows_per_launch = qmm::fmt_rows(p->d.K);
-    c.tile_rows = 1;
-    const int g = std::min(p->cus, nT);
-    int tm = std::min(qmm::kFmtMaxSlots, (nT + g - 1) / g);
-    if (ntw_req) tm = std::max(1, std::min(ntw_req, qmm::kFmtMaxSlots));
-    const int bits = p->d.bits, gs = p->d.group_size;
-    int nw = 0, cpw = 0;
-    while (tm > 1 && !qmm::fmt_shape(bits, gs, nC, tm, &nw, &cpw)) --tm;
-    qmm::fmt_shape(bits, gs, nC, tm, &nw, &cpw);
-    c.ntw = tm;
-    c.cpw = cpw;
-    c.wk = nw;
-    c.grid = (nT + tm - 1) / tm;
-    c.nTB = c.grid;
-    c.S = 1;
-    c.lds = qmm::fmt_lds_bytes(nw, tm, std::min(rows, c.rows_per_launch), (int)p->d.K);
     return c;
   }
   if (variant == QMM_VARIANT_GENERIC) {
@@ -292,7 +292,7 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.ntw = cpw;  // chunks per wave for this family
     c.nTB = nT;
     const int r = std::min(rows, qmm::kStreamMaxRows);
-    c.lds = qmm::stream_lds_bytes(nw, cpw, r);
+    c.lds = qmm::stream_lds_bytes(nw, cpw, r, p->groups);
     c.S = 1;
     return c;
   }
@@ -404,28 +404,29 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
   if (variant_req < QMM_VARIANT_AUTO || variant_req > QMM_VARIANT_WIDE)
     return fail(QMM_ERR_INVALID_ARG, "unknown variant %d", variant_req);
-  const bool other = p->generic || p->fmt;
-  if (other && variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GENERIC)
+  if (p->generic && variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_GENERIC)
     return fail(QMM_ERR_UNSUPPORTED,
-                "bits=%d group_size=%d run only on the other formats' kernel (QMM_VARIANT_GENERIC)",
+                "bits=%d group_size=%d with f32 activations or scales run only on the "
+                "vector-ALU kernel of MLX's layout (QMM_VARIANT_GENERIC)",
                 p->d.bits, p->d.group_size);
-  if (!other && variant_req == QMM_VARIANT_GENERIC)
+  if (p->fmt && variant_req != QMM_VARIANT_AUTO && variant_req != QMM_VARIANT_STREAM &&
+      variant_req != QMM_VARIANT_RESIDENT)
     return fail(QMM_ERR_UNSUPPORTED,
-                "3- and 4-bit plans with groups of 64 or 128 use the native layout, not the "
-                "other formats' kernel");
+                "bits=%d group_size=%d run on the streaming and resident kernels only",
+                p->d.bits, p->d.group_size);
+  if (!p->generic && variant_req == QMM_VARIANT_GENERIC)
+    return fail(QMM_ERR_UNSUPPORTED,
+                "QMM_VARIANT_GENERIC is the vector-ALU kernel of plans that keep MLX's layout "
+                "(formats without a matrix-core path, or f32 activations or scales)");
   if ((variant_req == QMM_VARIANT_MFMA || variant_req == QMM_VARIANT_STREAM ||
        variant_req == QMM_VARIANT_RESIDENT || variant_req == QMM_VARIANT_SLAB ||
        variant_req == QMM_VARIANT_WIDE) &&
       p->d.x_dtype != QMM_BF16)
     return fail(QMM_ERR_UNSUPPORTED, "the MFMA kernels take bf16 activations");
-  if (variant_req == QMM_VARIANT_STREAM) {
-    int nw, cpw;
-    if (!stream_shape(p, &nw, &cpw) ||
-        !qmm::stream_fits(nw, cpw, std::min(rows, qmm::kStreamMaxRows), stream_max_lds(p)))
-      return fail(QMM_ERR_UNSUPPORTED,
-                  "the streaming kernel needs K <= 16384 and its activation slices "
-                  "to fit its LDS budget");
-  }
+  if (variant_req == QMM_VARIANT_STREAM && !stream_ok(p, std::min(rows, qmm::kStreamMaxRows)))
+    return fail(QMM_ERR_UNSUPPORTED,
+                "the streaming kernel needs K <= 16384, its activation slices to fit its LDS "
+                "budget and, for the step layout, its weight registers to fit");
   if (variant_req == QMM_VARIANT_RESIDENT && !resident_fits(p, std::min(rows, 16)))
     return fail(QMM_ERR_UNSUPPORTED,
                 "the resident kernel needs K <= 16384 and rows*K*2 bytes of activations (rows "
@@ -476,10 +477,7 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     if (cb.S > 1 && cfg_workspace(p, cb, rb) > ws_bytes)
       return fail(QMM_ERR_WORKSPACE, "workspace too small for a %d-row block", rb);
     hipError_t e;
-    if (vb == QMM_VARIANT_GENERIC && p->fmt)
-      e = qmm::launch_fmt(p->d.bits, p->d.group_size, cb.wk, cb.cpw, cb.ntw, a, cb.grid, cb.lds,
-                          st);
-    else if (vb == QMM_VARIANT_GENERIC)
+    if (vb == QMM_VARIANT_GENERIC)
       e = qmm::launch_generic(p->d.bits, p->d.group_size, xf, sf, rb, a, st);
     else if (vb == QMM_VARIANT_WIDE)
       e = qmm::launch_wide(p->d.bits, sf, cb.tile_rows, a, cb.grid, cb.lds, st);
@@ -489,9 +487,10 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     else if (vb == QMM_VARIANT_SLAB)
       e = qmm::launch_slab(p->d.bits, sf, cb.tile_rows, cb.cpw, a, cb.grid, cb.lds, st);
     else if (vb == QMM_VARIANT_RESIDENT)
-      e = qmm::launch_resident(p->d.bits, sf, cb.wk, cb.cpw, cb.ntw, a, cb.grid, cb.lds, st);
+      e = qmm::launch_resident(p->d.bits, p->step_gs, sf, cb.wk, cb.cpw, cb.ntw, a, cb.grid,
+                               cb.lds, st);
     else if (vb == QMM_VARIANT_STREAM)
-      e = qmm::launch_stream(p->d.bits, sf, cb.wk, cb.ntw, a, cb.lds, st);
+      e = qmm::launch_stream(p->d.bits, p->step_gs, sf, cb.wk, cb.ntw, a, cb.lds, st);
     else if (vb == QMM_VARIANT_MFMA)
       e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, st);
     else
@@ -557,8 +556,10 @@ qmm_status qmm_create(const qmm_desc* d, qmm_plan** out) {
   int fnw = 0, fcpw = 0;
   p->fmt = !native && d->x_dtype == QMM_BF16 && d->sb_dtype == QMM_BF16 &&
            qmm::fmt_format(b, d->group_size) && qmm::fmt_rows(d->K) >= 1 &&
-           qmm::fmt_shape(b, d->group_size, p->nC, 1, &fnw, &fcpw);
+           qmm::resident_shape(b, d->group_size, p->nC, 1, &fnw, &fcpw);
   p->generic = !native && !p->fmt;
+  p->step_gs = p->fmt ? d->group_size : 0;
+  p->groups = p->fmt ? qmm::kChunkK / d->group_size : 2;
   p->force_variant = 0;
   if (const char* v = getenv("QMM_FORCE_VARIANT")) {
     if (!strcmp(v, "gemv")) p->force_variant = QMM_VARIANT_GEMV;
@@ -639,7 +640,7 @@ size_t qmm_workspace_bytes_ex(const qmm_plan* p, int32_t variant, int32_t ntw, i
 size_t qmm_workspace_bytes(const qmm_plan* p, int32_t rows) {
   if (!p || rows < 1) return 0;
   size_t need = qmm_workspace_bytes_ex(p, QMM_VARIANT_AUTO, 0, 0, 0, rows);
-  if (p->d.x_dtype == QMM_BF16) {
+  if (p->d.x_dtype == QMM_BF16 && !p->fmt) {
     need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_GEMV, 0, 0, 0, rows));
     need = std::max(need, qmm_workspace_bytes_ex(p, QMM_VARIANT_MFMA, 0, 0, 0, rows));
   }

@@ -44,21 +44,28 @@ hipError_t launch_mfma(int bits, bool sb_f32, int mt, int ntw, int wk, const Lau
                        hipStream_t st);
 hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const LaunchArgs& a,
                        size_t lds_bytes, hipStream_t st);
-hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
+// The streaming and resident kernels run the native layout (step_gs = 0:
+// 3- and 4-bit codes, bf16 or f32 scales) and the step layout of the other
+// formats (step_gs = the group size; bf16 scales; see fmt_format).
+hipError_t launch_stream(int bits, int step_gs, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
                          size_t lds_bytes, hipStream_t st);
 // Rows the streaming kernel takes per launch (its waves stage every row of
 // their own chunks' activation slices in registers on the way to LDS).
 constexpr int kStreamMaxRows = 4;
-size_t stream_lds_bytes(int nw, int cpw, int M);
+// LDS of the streaming kernel with `groups` quantization groups per chunk.
+size_t stream_lds_bytes(int nw, int cpw, int M, int groups);
 // Whether M rows fit the streaming kernel (M <= kStreamMaxRows and at most
 // max_lds bytes of LDS for NW waves of at most cpw chunks).
-bool stream_fits(int nw, int cpw, int M, size_t max_lds);
-hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const LaunchArgs& a,
-                           int grid, size_t lds_bytes, hipStream_t st);
+bool stream_fits(int nw, int cpw, int M, int groups, size_t max_lds);
+// Whether the streaming kernel is built for a step-layout format at this
+// (waves, chunks per wave): the wave's weight registers must fit.
+bool stream_step_fits(int bits, int group_size, int nw, int cpw);
+hipError_t launch_resident(int bits, int step_gs, bool sb_f32, int nw, int cpw, int tm,
+                           const LaunchArgs& a, int grid, size_t lds_bytes, hipStream_t st);
 // Resident kernel: the built (waves, chunks per wave) for `tm` tile slots
 // that covers nC chunks of K (false if none does), and its dynamic LDS bytes
 // for M rows (the activation block, reused for the partial tiles).
-bool resident_shape(int nC, int tm, int* nw, int* cpw);
+bool resident_shape(int bits, int step_gs, int nC, int tm, int* nw, int* cpw);
 // Rows of LDS a block of M rows takes (M, at most 16 per launch).
 int resident_rows(int M);
 size_t resident_lds_bytes(int nw, int tm, int M, int K);
@@ -72,24 +79,13 @@ constexpr int kGenericMaxRows = 2;
 hipError_t launch_generic(int bits, int group_size, bool x_f32, bool sb_f32, int rows,
                           const LaunchArgs& a, hipStream_t st);
 
-// Step layout and matrix-core kernel of the other formats (qmm_fmt.hip):
-// 2- and 8-bit codes with groups of 32, 64 or 128, 3- and 4-bit codes with
-// groups of 32; bf16 activations and bf16 scales/biases.  Up to fmt_rows(K)
-// activation rows (at most 16, their block in one compute unit's LDS) per
-// launch; (waves, chunks per wave) for `tm` tile slots from fmt_shape, which
-// keeps a wave's weight registers (cpw * tm * (bits + 128/group_size) words)
-// within fmt_regs_fit: 128 words with up to 8 waves (two per SIMD), 80 with
-// 16 (four per SIMD, 128 registers each).
-constexpr bool fmt_regs_fit(int bits, int group_size, int nw, int cpw, int tm) {
-  return cpw * tm * (bits + 128 / group_size) <= (nw >= 16 ? 80 : 128);
-}
-constexpr int kFmtMaxSlots = 3;
+// Step layout of the other formats (qmm_formats.h, qmm_fmt.hip): 2- and
+// 8-bit codes with groups of 32, 64 or 128, 3- and 4-bit codes with groups of
+// 32; bf16 activations and bf16 scales/biases.  They run on the streaming
+// and resident kernels; the resident kernel takes fmt_rows(K) rows per
+// launch (at most 16, their activation block in one compute unit's LDS).
 bool fmt_format(int bits, int group_size);
-bool fmt_shape(int bits, int group_size, int nC, int tm, int* nw, int* cpw);
 int fmt_rows(long K);
-size_t fmt_lds_bytes(int nw, int tm, int M, int K);
-hipError_t launch_fmt(int bits, int group_size, int nw, int cpw, int tm, const LaunchArgs& a,
-                      int grid, size_t lds_bytes, hipStream_t st);
 hipError_t launch_repack_fmt(int bits, int group_size, const uint32_t* w, const void* scales,
                              const void* biases, uint32_t* codes, void* sb, int N, int K,
                              hipStream_t st);

@@ -5,13 +5,14 @@
 
 #include <algorithm>
 
-#include "qmm_device.h"
+#include "qmm_formats.h"
 
 namespace qmm {
 
 // ---------------------------------------------------------------------------
 // Resident MFMA kernel for blocks of up to 16 activation rows whose whole
-// activation block fits in LDS (rows*K*2 <= 160 KB).  Workgroup g owns the
+// activation block fits in LDS (rows*K*2 <= 160 KB), over a weight-format
+// policy F (qmm_formats.h).  Workgroup g owns the
 // TM tiles g, g+G, g+2G, ... (G = grid size); its NW wavefronts split K:
 // wave w takes chunks w, w+NW, ... (at most CPW) of every one of those tiles,
 // so each activation fragment it reads, and each group sum it forms, serves
@@ -44,20 +45,23 @@ __device__ __forceinline__ float silu_mul(float gate, float up) {
   return silu * u;  // rounded to bf16 by the store
 }
 
-// Timing build: the wait for chunk j's weights (2*TM loads per later chunk
+// Timing build: the wait for chunk j's weights (LPT*TM loads per later chunk
 // outstanding); j is a constant once the caller's loop is unrolled.
-template <int CPW, int TM, int J = 0>
+template <int CPW, int TM, int LPT, int J = 0>
 __device__ __forceinline__ void stamp_chunk(int j) {
   if constexpr (J < CPW) {
     if (j == J)
-      stamp_wait<(CPW - 1 - J) * TM * 2>();
+      stamp_wait<(CPW - 1 - J) * TM * LPT>();
     else
-      stamp_chunk<CPW, TM, J + 1>(j);
+      stamp_chunk<CPW, TM, LPT, J + 1>(j);
   }
 }
 
-template <int BITS, int NW, int CPW, int TM, typename ST, bool GU = false>
+template <typename F, int NW, int CPW, int TM, bool GU = false>
 __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
+  constexpr int BITS = F::kBits, GC = F::kGroups, SPG = F::kSpg;
+  constexpr int LPT = F::kCodeLoads + 1;  // loads per (chunk, tile slot)
+  using ST = typename F::St;
   constexpr int TMH = GU ? TM / 2 : TM;  // distinct tiles per workgroup
   static_assert(!GU || TM % 2 == 0, "gate/up slots come in pairs");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -104,33 +108,34 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   }
   const ST* __restrict__ sbp2 = reinterpret_cast<const ST*>(a.sb2);
   uint32_t W[CPW][TM][BITS];
-  SBPair<ST> SBv[CPW][TM];
+  typename F::Sb SBv[CPW][TM];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int c = min(w + j * NW, clast);
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const bool second = GU && t >= TMH;  // compile-time once unrolled
-      const uint32_t* p = (second ? a.codes2 : a.codes) + ((long)tl[t] * nC + c) * 64 * BITS +
-                          lane * BITS;
-#pragma unroll
-      for (int q = 0; q < BITS; ++q) W[j][t][q] = __builtin_nontemporal_load(p + q);
-      SBv[j][t].load((second ? sbp2 : sbp) + (((long)tl[t] * nC + c) * kTileN + r) * 4);
+      const long blk = (long)tl[t] * nC + c;
+      F::load(second ? a.codes2 : a.codes, blk, lane, W[j][t]);
+      SBv[j][t].load((second ? sbp2 : sbp) + (blk * kTileN + r) * F::kSbElems);
     }
+    __builtin_amdgcn_sched_barrier(0);  // chunk j's loads issue before chunk j+1's
   }
-  __builtin_amdgcn_sched_barrier(0);
   ts.mark(1);
 
   // 2. this wave's activation slices have landed once at most its weight
-  //    loads (two per chunk and tile) are outstanding
-  wait_vm<CPW * TM * 2>();
+  //    loads (LPT per chunk and tile, counted low) are outstanding.  The
+  //    wait also drains the LDS counter: until it does, the compiler counts
+  //    the LDS-direct loads as pending on both counters and may turn later
+  //    weight waits into full ones (vmcnt(0)).
+  wait_vm_lds<(CPW * TM * LPT < 63 ? CPW * TM * LPT : 63)>();
   ts.mark(2);
 
   // 3. compute in load order; rows past the last one read the last row
   //    (never stored)
   const int xm = min(r, M - 1);
   const int sw = xm & 15;
-  const PairMasks mask_v = pair_mask_vgpr<BITS>();
+  const typename F::Masks mask_v = F::masks();
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[TM];
@@ -140,38 +145,41 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   for (int j = 0; j < CPW; ++j) {
     const bool live = j < count;
     const int c = min(w + j * NW, clast);
-    stamp_chunk<CPW, TM>(j);  // timing build: wait for chunk j's weights, then
-    ts.mark(3 + j);           // stamp their arrival
+    stamp_chunk<CPW, TM, LPT>(j);  // timing build: wait for chunk j's weights,
+    ts.mark(3 + j);                // then stamp their arrival
     const u32x4* xrow = reinterpret_cast<const u32x4*>(lds + (size_t)c * M * 256) + xm * 16;
     u32x4 A[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)  // vector of (group q>>1, quarter kg, half q&1)
-      A[q] = xrow[(8 * (q >> 1) + 2 * kg + (q & 1)) ^ sw];
+    for (int q = 0; q < 4; ++q) A[q] = xrow[F::a_vec(q, kg) ^ sw];
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 ex[2];
+    f32x4 ex[GC];
 #pragma unroll
-    for (int gp = 0; gp < 2; ++gp) {
-      const f32x4 e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, ones), zero, 0, 0, 0);
-      ex[gp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp + 1]), __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
+    for (int g = 0; g < GC; ++g) {
+      f32x4 e = zero;
+#pragma unroll
+      for (int u = 0; u < SPG; ++u)
+        e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[g * SPG + u]),
+                                                    __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
+      ex[g] = e;
     }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       uint32_t P[16];
-      unpack_pairs<BITS>(W[j][t], P, mask_v);
+      F::unpack(W[j][t], P, mask_v);
 #pragma unroll
-      for (int gp = 0; gp < 2; ++gp) {
-        const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
-        const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
-        f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
-                                                     __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
-        const Affine af = group_affine<BITS>(gp, SBv[j][t].s(gp), SBv[j][t].b(gp));
+      for (int g = 0; g < GC; ++g) {
+        f32x4 dd = zero;
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) {
+          const int st = g * SPG + u;
+          const u32x4 B = {P[4 * st], P[4 * st + 1], P[4 * st + 2], P[4 * st + 3]};
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[st]),
+                                                       __builtin_bit_cast(bf16x8, B), dd, 0, 0, 0);
+        }
+        const Affine af = F::affine(g, SBv[j][t]);
         const float sc = live ? af.sc : 0.f, bp = live ? af.bp : 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, dd[q], fmaf(bp, ex[gp][q], acc[t][q]));
+        for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, dd[q], fmaf(bp, ex[g][q], acc[t][q]));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -217,11 +225,14 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   X(8, 4, 1) X(8, 4, 2) X(8, 4, 3) X(8, 4, 4) X(8, 5, 1) X(8, 5, 2) X(8, 5, 3) X(8, 5, 4)     \
   X(8, 8, 1) X(8, 8, 2) X(16, 8, 1) X(16, 8, 2)
 
-bool resident_shape(int nC, int tm, int* nw, int* cpw) {
+// Step-layout formats: the built shapes whose weight registers fit.
+template <typename F>
+static bool resident_pick(int nC, int tm, int* nw, int* cpw) {
   // the fewest chunks per wave that cover K: four waves below 16 chunks
   int best_w = 0, best_c = 0;
 #define QMM_PICK(W, C, T)                                                                  \
-  if (T == tm && (nC < 16) == (W == 4) && W * C >= nC && (best_c == 0 || C < best_c)) { \
+  if (T == tm && (nC < 16) == (W == 4) && W * C >= nC && F::resident_fits(W, C, T) &&     \
+      (best_c == 0 || C < best_c)) {                                                      \
     best_w = W;                                                                           \
     best_c = C;                                                                           \
   }
@@ -232,36 +243,58 @@ bool resident_shape(int nC, int tm, int* nw, int* cpw) {
   return best_c > 0;
 }
 
+bool resident_shape(int bits, int step_gs, int nC, int tm, int* nw, int* cpw) {
+  if (step_gs) {
+#define QMM_STEP(B, GS) \
+  if (bits == B && step_gs == GS) return resident_pick<StepFmt<B, GS>>(nC, tm, nw, cpw);
+    QMM_STEP_FORMATS(QMM_STEP)
+#undef QMM_STEP
+    *nw = *cpw = 0;
+    return false;
+  }
+  return resident_pick<NativeFmt<4, uint16_t>>(nC, tm, nw, cpw);
+}
+
 int resident_rows(int M) { return std::min(M, 16); }
 
 size_t resident_lds_bytes(int nw, int tm, int M, int K) {
   return std::max((size_t)resident_rows(M) * K * 2, (size_t)tm * nw * 64 * 16);
 }
 
-template <int BITS, typename ST>
+template <typename F>
 static hipError_t resident_dispatch(int nw, int cpw, int tm, const LaunchArgs& a, int grid,
                                     size_t lds, hipStream_t st) {
-#define QMM_GO(W, C, T)                                                                     \
-  if (nw == W && cpw == C && tm == T) {                                                     \
-    auto* kfn = &resident_kernel<BITS, W, C, T, ST>;                                        \
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                  \
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-    if (e != hipSuccess) return e;                                                          \
-    kfn<<<grid, W * 64, lds, st>>>(a);                                                      \
-    return hipGetLastError();                                                               \
+#define QMM_GO(W, C, T)                                                                       \
+  if constexpr (F::resident_fits(W, C, T)) {                                                  \
+    if (nw == W && cpw == C && tm == T) {                                                     \
+      auto* kfn = &resident_kernel<F, W, C, T>;                                               \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                  \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e != hipSuccess) return e;                                                          \
+      kfn<<<grid, W * 64, lds, st>>>(a);                                                      \
+      return hipGetLastError();                                                               \
+    }                                                                                         \
   }
   QMM_RESIDENT_SHAPES(QMM_GO)
 #undef QMM_GO
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_resident(int bits, bool sb_f32, int nw, int cpw, int tm, const LaunchArgs& a,
-                           int grid, size_t lds_bytes, hipStream_t st) {
+hipError_t launch_resident(int bits, int step_gs, bool sb_f32, int nw, int cpw, int tm,
+                           const LaunchArgs& a, int grid, size_t lds_bytes, hipStream_t st) {
+  if (step_gs) {
+#define QMM_STEP(B, GS)                \
+  if (bits == B && step_gs == GS) \
+    return resident_dispatch<StepFmt<B, GS>>(nw, cpw, tm, a, grid, lds_bytes, st);
+    QMM_STEP_FORMATS(QMM_STEP)
+#undef QMM_STEP
+    return hipErrorInvalidValue;
+  }
   if (bits == 3)
-    return sb_f32 ? resident_dispatch<3, float>(nw, cpw, tm, a, grid, lds_bytes, st)
-                  : resident_dispatch<3, uint16_t>(nw, cpw, tm, a, grid, lds_bytes, st);
-  return sb_f32 ? resident_dispatch<4, float>(nw, cpw, tm, a, grid, lds_bytes, st)
-                : resident_dispatch<4, uint16_t>(nw, cpw, tm, a, grid, lds_bytes, st);
+    return sb_f32 ? resident_dispatch<NativeFmt<3, float>>(nw, cpw, tm, a, grid, lds_bytes, st)
+                  : resident_dispatch<NativeFmt<3, uint16_t>>(nw, cpw, tm, a, grid, lds_bytes, st);
+  return sb_f32 ? resident_dispatch<NativeFmt<4, float>>(nw, cpw, tm, a, grid, lds_bytes, st)
+                : resident_dispatch<NativeFmt<4, uint16_t>>(nw, cpw, tm, a, grid, lds_bytes, st);
 }
 
 // (waves, chunks per wave, tile pairs) shapes of the fused gate/up kernel.
@@ -287,7 +320,7 @@ static hipError_t gate_up_dispatch(int nw, int cpw, int pairs, const LaunchArgs&
                                    size_t lds, hipStream_t st) {
 #define QMM_GO(W, C, P)                                                                     \
   if (nw == W && cpw == C && pairs == P) {                                                  \
-    auto* kfn = &resident_kernel<BITS, W, C, 2 * P, ST, true>;                              \
+    auto* kfn = &resident_kernel<NativeFmt<BITS, ST>, W, C, 2 * P, true>;                              \
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                  \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                          \

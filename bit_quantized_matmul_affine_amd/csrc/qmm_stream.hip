@@ -4,12 +4,13 @@
 
 #include <algorithm>
 
-#include "qmm_device.h"
+#include "qmm_formats.h"
 
 namespace qmm {
 
 // ---------------------------------------------------------------------------
-// Streaming MFMA kernel for short activation blocks (at most 4 rows).  One
+// Streaming MFMA kernel for short activation blocks (at most 4 rows), over a
+// weight-format policy F (qmm_formats.h).  One
 // workgroup owns one tile of W (16 rows) and all of K; its NW wavefronts take
 // every NW-th chunk, at most CPW each.  Every wave works on its own data only
 // until the final sum:
@@ -25,35 +26,60 @@ namespace qmm {
 // No barrier precedes step 3: a wave's compute starts as soon as its own
 // slices arrive, not when the slowest wave of the workgroup has its.
 // LDS per wave: rows x (CPW*256 + 16) bytes of slices (the 16-byte pad puts
-// consecutive rows on different banks) and rows x CPW x 2 group sums.
+// consecutive rows on different banks) and rows x CPW x F::kGroups group sums.
 // ---------------------------------------------------------------------------
 constexpr int kStreamRowPad = 16;
-__device__ __forceinline__ float dpp_sum8(float s) {
-  // sum over each aligned group of 8 lanes: swap neighbours, pairs, halves
+// Sum over each aligned group of L (4, 8 or 16) lanes: swap neighbours,
+// pairs, half rows, rows.
+template <int L>
+__device__ __forceinline__ float dpp_sum(float s) {
   s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
   s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
-  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, true));
+  if constexpr (L >= 8)
+    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, true));
+  if constexpr (L >= 16)
+    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x140, 0xF, 0xF, true));
   return s;
+}
+
+// The G floats at p (G = 1, 2 or 4) in one load.
+template <int G>
+__device__ __forceinline__ void load_floats(const float* p, float* v) {
+  if constexpr (G == 4) {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  } else if constexpr (G == 2) {
+    const float2 f = *reinterpret_cast<const float2*>(p);
+    v[0] = f.x;
+    v[1] = f.y;
+  } else {
+    v[0] = *p;
+  }
 }
 
 // Vectors of 16 bytes per lane for rows (<= MQ) x CPW slices of 128 values.
 template <int MQ, int CPW>
 struct StreamXL { static constexpr int value = (MQ * CPW * 16 + 63) / 64; };
 
-// Timing build: the wait for chunk j's weights (two loads per later chunk
+// Timing build: the wait for chunk j's weights (LPC loads per later chunk
 // outstanding); j is a constant once the caller's loop is unrolled.
-template <int CPW, int J = 0>
+template <int CPW, int LPC, int J = 0>
 __device__ __forceinline__ void stamp_chunk(int j) {
   if constexpr (J < CPW) {
     if (j == J)
-      stamp_wait<(CPW - 1 - J) * 2>();
+      stamp_wait<(CPW - 1 - J) * LPC>();
     else
-      stamp_chunk<CPW, J + 1>(j);
+      stamp_chunk<CPW, LPC, J + 1>(j);
   }
 }
 
-template <int BITS, int NW, int CPW, int MQ, typename ST>
+template <typename F, int NW, int CPW, int MQ>
 __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
+  constexpr int BITS = F::kBits, GC = F::kGroups, SPG = F::kSpg;
+  using ST = typename F::St;
   constexpr int XL = StreamXL<MQ, CPW>::value;
   constexpr int ROWB = CPW * 256 + kStreamRowPad;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -70,7 +96,7 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   ts.mark(0);
   unsigned char* xw = lds + (size_t)w * a.M * ROWB;                           // [M][ROWB]
   float* xsum = reinterpret_cast<float*>(lds + (size_t)NW * a.M * ROWB) +
-                (size_t)w * a.M * CPW * 2;                                     // [M][CPW][2]
+                (size_t)w * a.M * CPW * GC;                                    // [M][CPW][GC]
 
   // 1. activation slices: vector v = (row m, slot j, part e); slots past
   //    `count` hold the last chunk's slice again (its results are dropped)
@@ -90,24 +116,23 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   ts.mark(1);
 
   // weight loads of every slot; slots past `count` re-read the last chunk
-  const uint32_t* cbase = a.codes + ((long)tile * nC) * 64 * BITS + lane * BITS;
-  const ST* sbase = sbp + ((long)tile * nC * kTileN + r) * 4;
+  const ST* sbase = sbp + ((long)tile * nC * kTileN + r) * F::kSbElems;
   uint32_t W[CPW][BITS];
-  SBPair<ST> SBv[CPW];
+  typename F::Sb SBv[CPW];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int c = min(w + j * NW, clast);
-    const uint32_t* p = cbase + (long)c * 64 * BITS;
-#pragma unroll
-    for (int q = 0; q < BITS; ++q) W[j][q] = __builtin_nontemporal_load(p + q);
-    SBv[j].load(sbase + (long)c * kTileN * 4);
+    F::load(a.codes, (long)tile * nC + c, lane, W[j]);
+    SBv[j].load(sbase + (long)c * kTileN * F::kSbElems);
+    __builtin_amdgcn_sched_barrier(0);  // chunk j's loads issue before chunk j+1's
   }
   __builtin_amdgcn_sched_barrier(0);
   ts.mark(2);
 
-  // 2. slices and their group sums to this wave's LDS area.  The 8 lanes
-  //    holding one (row, slot, group) are an aligned group of 8; lanes whose
-  //    vector index is past the end hold a repeated vector and write no sum.
+  // 2. slices and their group sums to this wave's LDS area.  The lanes
+  //    holding one (row, slot, group) are an aligned group of F::kGroupVecs;
+  //    lanes whose vector index is past the end hold a repeated vector and
+  //    write no sum.
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
   for (int i = 0; i < XL; ++i) {
@@ -121,11 +146,11 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
       s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xd),
                                           __builtin_bit_cast(bf16x2, od), s, false);
     }
-    s = dpp_sum8(s);
+    s = dpp_sum<F::kGroupVecs>(s);
     const int v = lane + 64 * i;
-    if (v < nv && (lane & 7) == 0) {
+    if (v < nv && (lane & (F::kGroupVecs - 1)) == 0) {
       const int m = v / (CPW * 16), rem = v - m * (CPW * 16);
-      xsum[(m * CPW + (rem >> 4)) * 2 + ((rem >> 3) & 1)] = s;
+      xsum[(m * CPW + (rem >> 4)) * GC + (rem & 15) / F::kGroupVecs] = s;
     }
   }
   // other lanes of this wave read what these lanes wrote: keep the compiler
@@ -137,40 +162,42 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   ts.mark(3);
   // 3. compute in load order; rows past the last one read the last row
   //    (never stored)
-  const unsigned char* xrow = xw + min(r, a.M - 1) * ROWB + 32 * kg;
+  const unsigned char* xrow = xw + min(r, a.M - 1) * ROWB;
   const float* srow[MQ];
 #pragma unroll
-  for (int q = 0; q < MQ; ++q) srow[q] = xsum + min(4 * kg + q, a.M - 1) * CPW * 2;
-  const PairMasks mask_v = pair_mask_vgpr<BITS>();
+  for (int q = 0; q < MQ; ++q) srow[q] = xsum + min(4 * kg + q, a.M - 1) * CPW * GC;
+  const typename F::Masks mask_v = F::masks();
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc = zero;
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const bool live = j < count;
-    stamp_chunk<CPW>(j);  // timing build: wait for chunk j's weights, then
-    ts.mark(4 + j);       // stamp their arrival
+    stamp_chunk<CPW, F::kCodeLoads + 1>(j);  // timing build: wait for chunk j's
+    ts.mark(4 + j);                          // weights, then stamp their arrival
     u32x4 A[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      A[t] = *reinterpret_cast<const u32x4*>(xrow + 256 * j + 128 * (t >> 1) + 16 * (t & 1));
-    float2 ex[MQ];
+      A[t] = *reinterpret_cast<const u32x4*>(xrow + 256 * j + 16 * F::a_vec(t, kg));
+    float ex[MQ][GC];
 #pragma unroll
-    for (int q = 0; q < MQ; ++q) ex[q] = *reinterpret_cast<const float2*>(srow[q] + 2 * j);
+    for (int q = 0; q < MQ; ++q) load_floats<GC>(srow[q] + GC * j, ex[q]);
     uint32_t P[16];
-    unpack_pairs<BITS>(W[j], P, mask_v);
+    F::unpack(W[j], P, mask_v);
 #pragma unroll
-    for (int gp = 0; gp < 2; ++gp) {
-      const u32x4 B0 = {P[8 * gp + 0], P[8 * gp + 1], P[8 * gp + 2], P[8 * gp + 3]};
-      const u32x4 B1 = {P[8 * gp + 4], P[8 * gp + 5], P[8 * gp + 6], P[8 * gp + 7]};
-      f32x4 dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, A[2 * gp]), __builtin_bit_cast(bf16x8, B0), zero, 0, 0, 0);
-      dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[2 * gp + 1]),
-                                                   __builtin_bit_cast(bf16x8, B1), dd, 0, 0, 0);
-      const Affine af = group_affine<BITS>(gp, SBv[j].s(gp), SBv[j].b(gp));
+    for (int g = 0; g < GC; ++g) {
+      f32x4 dd = zero;
+#pragma unroll
+      for (int u = 0; u < SPG; ++u) {
+        const int t = g * SPG + u;
+        const u32x4 B = {P[4 * t], P[4 * t + 1], P[4 * t + 2], P[4 * t + 3]};
+        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[t]),
+                                                     __builtin_bit_cast(bf16x8, B), dd, 0, 0, 0);
+      }
+      const Affine af = F::affine(g, SBv[j]);
       const float sc = af.sc, bp = af.bp;
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
-        const float v = fmaf(sc, dd[q], fmaf(bp, gp ? ex[q].y : ex[q].x, acc[q]));
+        const float v = fmaf(sc, dd[q], fmaf(bp, ex[q][g], acc[q]));
         acc[q] = live ? v : acc[q];
       }
     }
@@ -179,7 +206,8 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
 
   ts.mark(12);
   // 4. add the NW partial tiles in wave order and store rows < M
-  f32x4* red = reinterpret_cast<f32x4*>(lds + (size_t)NW * a.M * (ROWB + CPW * 8));  // [NW-1][64]
+  // [NW-1][64] after every wave's slices and group sums (stream_lds_bytes)
+  f32x4* red = reinterpret_cast<f32x4*>(lds + (size_t)NW * a.M * (ROWB + CPW * 4 * GC));
   if (w > 0) red[(w - 1) * 64 + lane] = acc;
   __syncthreads();
   ts.mark(13);
@@ -199,28 +227,31 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   ts.flush(lane);
 }
 
-size_t stream_lds_bytes(int nw, int cpw, int M) {
-  return (size_t)nw * M * (cpw * 256 + kStreamRowPad + cpw * 8) + (size_t)(nw - 1) * 64 * 16;
+size_t stream_lds_bytes(int nw, int cpw, int M, int groups) {
+  return (size_t)nw * M * (cpw * 256 + kStreamRowPad + cpw * 4 * groups) +
+         (size_t)(nw - 1) * 64 * 16;
 }
-bool stream_fits(int nw, int cpw, int M, size_t max_lds) {
-  return M >= 1 && M <= kStreamMaxRows && stream_lds_bytes(nw, cpw, M) <= max_lds;
+bool stream_fits(int nw, int cpw, int M, int groups, size_t max_lds) {
+  return M >= 1 && M <= kStreamMaxRows && stream_lds_bytes(nw, cpw, M, groups) <= max_lds;
 }
 
-
-template <int BITS, typename ST, int MQ>
+template <typename F, int MQ>
 static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_t lds,
                                      hipStream_t st) {
   const unsigned grid = (unsigned)(a.N / kTileN);
 #define QMM_STREAM(NWV, CPWV)                                                                \
-  if (nw == NWV && cpw == CPWV) {                                                            \
-    auto* kfn = &stream_kernel<BITS, NWV, CPWV, MQ, ST>;                                     \
-    if (lds > 64 * 1024) {                                                                   \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                 \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-      if (e != hipSuccess) return e;                                                         \
+  if constexpr (F::stream_fits(NWV, CPWV)) {                                                 \
+    if (nw == NWV && cpw == CPWV) {                                                          \
+      auto* kfn = &stream_kernel<F, NWV, CPWV, MQ>;                                          \
+      if (lds > 64 * 1024) {                                                                 \
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),               \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,       \
+                                           (int)lds);                                        \
+        if (e != hipSuccess) return e;                                                       \
+      }                                                                                      \
+      kfn<<<grid, NWV * 64, lds, st>>>(a);                                                   \
+      return hipGetLastError();                                                              \
     }                                                                                        \
-    kfn<<<grid, NWV * 64, lds, st>>>(a);                                                     \
-    return hipGetLastError();                                                                \
   }
   QMM_STREAM(4, 2) QMM_STREAM(4, 4) QMM_STREAM(8, 4) QMM_STREAM(8, 5) QMM_STREAM(8, 8)
   QMM_STREAM(16, 8)
@@ -228,18 +259,37 @@ static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_
   return hipErrorInvalidValue;
 }
 
-template <int BITS, typename ST>
+template <typename F>
 static hipError_t stream_dispatch(int nw, int cpw, const LaunchArgs& a, size_t lds,
                                   hipStream_t st) {
-  if (a.M == 1) return stream_dispatch_mq<BITS, ST, 1>(nw, cpw, a, lds, st);
-  if (a.M == 2) return stream_dispatch_mq<BITS, ST, 2>(nw, cpw, a, lds, st);
-  return stream_dispatch_mq<BITS, ST, 4>(nw, cpw, a, lds, st);
+  if (a.M == 1) return stream_dispatch_mq<F, 1>(nw, cpw, a, lds, st);
+  if (a.M == 2) return stream_dispatch_mq<F, 2>(nw, cpw, a, lds, st);
+  return stream_dispatch_mq<F, 4>(nw, cpw, a, lds, st);
 }
 
-hipError_t launch_stream(int bits, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
+bool stream_step_fits(int bits, int group_size, int nw, int cpw) {
+#define QMM_FIT(B, GS) \
+  if (bits == B && group_size == GS) return StepFmt<B, GS>::stream_fits(nw, cpw);
+  QMM_STEP_FORMATS(QMM_FIT)
+#undef QMM_FIT
+  return false;
+}
+
+hipError_t launch_stream(int bits, int step_gs, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
                          size_t lds_bytes, hipStream_t st) {
-  if (bits == 3) return sb_f32 ? stream_dispatch<3, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<3, uint16_t>(nw, cpw, a, lds_bytes, st);
-  return sb_f32 ? stream_dispatch<4, float>(nw, cpw, a, lds_bytes, st) : stream_dispatch<4, uint16_t>(nw, cpw, a, lds_bytes, st);
+  if (step_gs) {
+#define QMM_STEP(B, GS)                 \
+  if (bits == B && step_gs == GS) \
+    return stream_dispatch<StepFmt<B, GS>>(nw, cpw, a, lds_bytes, st);
+    QMM_STEP_FORMATS(QMM_STEP)
+#undef QMM_STEP
+    return hipErrorInvalidValue;
+  }
+  if (bits == 3)
+    return sb_f32 ? stream_dispatch<NativeFmt<3, float>>(nw, cpw, a, lds_bytes, st)
+                  : stream_dispatch<NativeFmt<3, uint16_t>>(nw, cpw, a, lds_bytes, st);
+  return sb_f32 ? stream_dispatch<NativeFmt<4, float>>(nw, cpw, a, lds_bytes, st)
+                : stream_dispatch<NativeFmt<4, uint16_t>>(nw, cpw, a, lds_bytes, st);
 }
 
 }  // namespace qmm

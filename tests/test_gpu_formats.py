@@ -5,10 +5,9 @@ by element at small sizes and on sampled outputs at the 5120 -> 10240 shape.
 Three paths: 3- and 4-bit weights with groups of 128 run on the native
 layout (each group's scale and bias serving both 64-value halves of a chunk)
 and every native kernel family; the other formats with bf16 activations and
-bf16 scales run on the step layout and its matrix-core kernel (up to 16 rows
-per launch); f32 activations or f32 scales keep MLX's layout on the
-vector-ALU kernel.  The step-layout kernel and the vector-ALU kernel both
-report the variant "generic"."""
+bf16 scales run on the step layout through the streaming kernel (1 or 2
+rows) and the resident kernel (up to 16 rows per launch); f32 activations or
+f32 scales keep MLX's layout on the vector-ALU kernel (variant "generic")."""
 import numpy as np
 import pytest
 
@@ -28,7 +27,9 @@ def _native(bits, gs):
 
 
 def _launches(r):
-    return r.lin.plan.stats()["launches"]["generic"]
+    """Launches of the kernels a step-layout or MLX-layout plan runs on."""
+    n = r.lin.plan.stats()["launches"]
+    return n["stream"] + n["resident"] + n["generic"]
 
 
 @pytest.mark.parametrize("bits,gs", STEP_FORMATS, ids=lambda v: str(v))
@@ -66,23 +67,31 @@ def test_small_every_format(bits, gs):
         last = r.lin.plan.stats()["last_variant"]
         if _native(bits, gs):
             assert last != "generic"
-        else:
+        elif x_dtype == "f32" or sb_dtype == "f32":
             assert last == "generic"
+        else:
+            assert last == "resident"
         check_against_oracle(p, y, label="b%d g%d %s/%s M=%d" % (bits, gs, x_dtype, sb_dtype, M))
 
 
 @pytest.mark.parametrize("bits,gs", STEP_FORMATS, ids=lambda v: str(v))
 def test_step_layout_rows(bits, gs):
-    """1..16 rows in one launch of the step-layout kernel (rows past the
-    last one never stored), 17 rows in two; f32 outputs as well."""
+    """1 and 2 rows on the streaming kernel, 3..16 in one launch of the
+    resident kernel (rows past the last one never stored), 17 rows in two;
+    both kernels forced at 4 rows; f32 outputs as well."""
     p = synth.small(90 + bits + gs, bits=bits, K=1024, N=208, M=17, group_size=gs)
     r = Runner(p)
-    for rows in (1, 5, 13, 16, 17):
+    for rows in (1, 2, 3, 5, 13, 16, 17):
         say("step rows", bits, gs, rows)
         before = _launches(r)
         y = r.run(rows=rows)
         assert _launches(r) - before == (1 if rows <= 16 else 2)
+        assert r.lin.plan.stats()["last_variant"] == ("stream" if rows <= 2 else "resident")
         check_against_oracle(p, y, rows=rows, label="b%d g%d rows=%d" % (bits, gs, rows))
+    for variant in ("stream", "resident"):
+        y = r.run(rows=4, variant=variant)
+        assert r.lin.plan.stats()["last_variant"] == variant
+        check_against_oracle(p, y, rows=4, label="b%d g%d rows=4 %s" % (bits, gs, variant))
     rf = Runner(p, f32_out=True)
     check_against_oracle(p, rf.run(rows=9), rows=9, out_dtype="f32",
                          label="b%d g%d rows=9 f32 out" % (bits, gs))
@@ -91,9 +100,9 @@ def test_step_layout_rows(bits, gs):
 @pytest.mark.parametrize("bits,gs", [(2, 64), (8, 64), (2, 128), (3, 32), (4, 32), (8, 32)],
                          ids=lambda v: str(v))
 def test_full_shape_sampled(bits, gs):
-    """The 5120 -> 10240 projection (640 tiles: three tile slots per
-    workgroup, 214 workgroups) at 1, 9 and 16 rows, and at 2 rows with f32
-    scales (vector-ALU kernel)."""
+    """The 5120 -> 10240 projection (640 tiles) at 1 row (streaming kernel),
+    9 and 16 rows (resident kernel, two or three tile slots per workgroup),
+    and at 2 rows with f32 scales (vector-ALU kernel)."""
     p = synth.small(77 + bits, bits=bits, K=5120, N=10240, M=16, group_size=gs)
     r = Runner(p)
     for rows in (1, 9, 16):
@@ -111,12 +120,14 @@ def test_full_shape_sampled(bits, gs):
 
 @pytest.mark.parametrize("K", [2048, 4096, 6144, 8192, 8320, 16384])
 def test_k_range(K):
-    """Every wave shape of the step-layout kernel (eight waves of 2, 4, 5, 8
-    chunks, sixteen waves of 8; 8320 leaves waves a chunk short) and, at K =
-    16384, five rows per launch (the LDS holds 5 x 32 KB of activations);
-    f32 scales run on the vector-ALU kernel with one to eight slice passes."""
+    """Every wave shape of the resident kernel on the step layout (eight waves
+    of 4, 5, 8 chunks, sixteen waves of 8; 8320 leaves waves a chunk short)
+    and, at K = 16384, five rows per launch (the LDS holds 5 x 32 KB of
+    activations); one row on the streaming kernel where its registers fit;
+    f32 scales on the vector-ALU kernel with one to eight slice passes."""
     cases = [(2, 32, "bf16", "bf16", 7), (8, 128, "bf16", "bf16", 6), (4, 32, "bf16", "bf16", 3),
-             (8, 128, "f32", "bf16", 1), (2, 64, "bf16", "f32", 1)]
+             (2, 128, "bf16", "bf16", 1), (8, 64, "bf16", "bf16", 1), (8, 128, "f32", "bf16", 1),
+             (2, 64, "bf16", "f32", 1)]
     for bits, gs, x_dtype, sb_dtype, M in cases:
         p = synth.small(500 + K // 128 + bits, bits=bits, K=K, N=32, M=M, x_dtype=x_dtype,
                         sb_dtype=sb_dtype, group_size=gs)
@@ -166,13 +177,25 @@ def test_group128_on_every_native_family(bits):
 
 
 def test_variant_rules():
+    """Step-layout plans run on the streaming and resident kernels only;
+    MLX-layout plans (f32 scales here) on the vector-ALU kernel only; the
+    native plans never on the vector-ALU kernel of MLX's layout; the fused
+    gate/up pair takes native plans only."""
     p = synth.small(3, bits=2, K=256, N=16, M=1, group_size=64)
     r = Runner(p)
-    for v in ("mfma", "gemv", "stream", "resident", "slab"):
+    for v in ("mfma", "gemv", "slab", "wide", "generic"):
         with pytest.raises(b.QmmError) as ei:
             r.run(variant=v)
         assert ei.value.status == b.QMM_ERR_UNSUPPORTED
-    check_against_oracle(p, r.run(variant="generic"), label="forced generic")
+    for v in ("stream", "resident"):
+        check_against_oracle(p, r.run(variant=v), label="forced " + v)
+    pf = synth.small(5, bits=2, K=256, N=16, M=1, group_size=64, sb_dtype="f32")
+    rf = Runner(pf)
+    for v in ("mfma", "gemv", "stream", "resident", "slab"):
+        with pytest.raises(b.QmmError) as ei:
+            rf.run(variant=v)
+        assert ei.value.status == b.QMM_ERR_UNSUPPORTED
+    check_against_oracle(pf, rf.run(variant="generic"), label="forced generic")
     q = synth.small(4, bits=4, K=256, N=16, M=1)
     rq = Runner(q)
     with pytest.raises(b.QmmError) as ei:

@@ -13,15 +13,19 @@ from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu
 
-# (family, split K, bits, K, N, rows, group size); every family is the
-# default for its shape except the wide one, forced at this small N
+# (family, split K, bits, K, N, rows, group size, scale dtype); every family
+# is the default for its shape except the wide one, forced at this small N;
+# the 2- and 8-bit cases run on the step layout (streaming and resident
+# kernels) and, with f32 scales, on MLX's layout (vector-ALU kernel)
 PROJECTIONS = [
-    ("stream", 1, 3, 5120, 160, 1, 64),
-    ("resident", 1, 3, 5120, 160, 9, 64),
-    ("slab", 1, 3, 5120, 208, 32, 64),
-    ("slab", 2, 3, 5120, 208, 64, 64),
-    ("wide", 1, 4, 2048, 256, 100, 64),
-    ("generic", 1, 2, 1024, 64, 2, 64),
+    ("stream", 1, 3, 5120, 160, 1, 64, "bf16"),
+    ("resident", 1, 3, 5120, 160, 9, 64, "bf16"),
+    ("slab", 1, 3, 5120, 208, 32, 64, "bf16"),
+    ("slab", 2, 3, 5120, 208, 64, 64, "bf16"),
+    ("wide", 1, 4, 2048, 256, 100, 64, "bf16"),
+    ("stream", 1, 2, 1024, 64, 2, 64, "bf16"),
+    ("resident", 1, 8, 1024, 64, 9, 32, "bf16"),
+    ("generic", 1, 2, 1024, 64, 2, 64, "f32"),
 ]
 FORCED = {"wide"}
 
@@ -31,8 +35,8 @@ def _work():
     and the output tensors each one needs."""
     import torch
     calls = []
-    for i, (fam, split, bits, K, N, M, gs) in enumerate(PROJECTIONS):
-        p = synth.small(700 + i, bits=bits, K=K, N=N, M=M, group_size=gs)
+    for i, (fam, split, bits, K, N, M, gs, sbd) in enumerate(PROJECTIONS):
+        p = synth.small(700 + i, bits=bits, K=K, N=N, M=M, group_size=gs, sb_dtype=sbd)
         lin = b.QuantizedLinear(p, max_rows=M)
         x = b.to_device(p.x)
         v = fam if fam in FORCED else "auto"
