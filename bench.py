@@ -436,7 +436,7 @@ def other_workloads(torch, binding, synth, probe):
 
 
 def main() -> int:
-    global ROWS
+    global ROWS, BITS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -449,6 +449,9 @@ def main() -> int:
                          "cache-resident numbers")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read probe")
+    ap.add_argument("--bits", type=int, default=3, choices=[3, 4],
+                    help="3: the measured 3-bit workload; 4: the 4-bit GEMV of the same shape "
+                         "(one row, for kernel comparisons at --rows 1)")
     ap.add_argument("--rows", default=",".join(map(str, ROWS)),
                     help="row counts of a step (default 1,9,16,32,64, the measured workload; a "
                          "single row count serves per-row-count kernel traces)")
@@ -467,6 +470,8 @@ def main() -> int:
         return 0
     ROWS = tuple(int(v) for v in args.rows.split(","))
     assert all(1 <= m <= 64 for m in ROWS), "row counts of the workload: 1..64"
+    BITS = args.bits
+    assert BITS == 3 or ROWS == (1,), "the 4-bit workload is the one-row GEMV: --rows 1"
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path",
@@ -489,7 +494,8 @@ def main() -> int:
                           "best_GBps": round(gbps, 1)}), flush=True)
         return 0
     log("drawing inputs")
-    (prob,) = synth.workload(2)               # M=64 draw; smaller M use its first rows
+    # 3-bit: the M=64 draw, smaller M use its first rows; 4-bit: the one-row GEMV
+    (prob,) = synth.workload(2 if BITS == 3 else 1)
     plan = binding.Plan(BITS, K, N, max(ROWS), "bf16", "bf16")
     lin = binding.QuantizedLinear(prob, max_rows=max(ROWS))
     ring = max(2, -(-RING_BYTES // weight_bytes()))
@@ -599,8 +605,8 @@ def main() -> int:
         cpu = cpu_baseline(prob)
 
     out = {
-        "metric": "weight-stream GB/s over the 3-bit 5120->10240 sweep M=1,9,16,32,64 "
-                  "(with us/matmul and % of HBM peak per M)",
+        "metric": "weight-stream GB/s over the %d-bit 5120->10240 sweep M=%s "
+                  "(with us/matmul and %% of HBM peak per M)" % (BITS, ",".join(map(str, ROWS))),
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -612,8 +618,9 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "3-bit group-64 affine qmm K=5120 N=10240, M in {1,9,16,32,64}, "
-                               "bf16 activations/scales/biases, cold weights (%d-copy ring)" % ring,
+        "config": {"workload": "%d-bit group-64 affine qmm K=5120 N=10240, M in {%s}, "
+                               "bf16 activations/scales/biases, cold weights (%d-copy ring)"
+                               % (BITS, ",".join(map(str, ROWS)), ring),
                    "variant": args.variant},
         "per_rows": per,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,

@@ -51,6 +51,8 @@ struct Cfg {
   int grid;       // RESIDENT, SLAB: workgroups
   int cpw;        // RESIDENT: chunks of K per wave; SLAB: slices per workgroup
   bool split;     // SLAB: the split slab kernel (ntw = tiles per wave, wk = tile slots)
+  bool valu_stream;  // GEMV: the streaming kernel's vector-ALU form (wk = waves, ntw = chunks
+                     // per wave)
 };
 
 }  // namespace
@@ -283,6 +285,21 @@ Cfg plan_config(const qmm_plan* p, int rows, int variant, int ntw_req, int wk_re
     c.lds = qmm::slab_lds_bytes(c.tile_rows);
     return c;
   }
+  if (variant == QMM_VARIANT_GEMV && p->d.x_dtype == QMM_BF16 && !p->fmt &&
+      stream_ok(p, std::min(rows, qmm::kStreamMaxRows))) {
+    // bf16 activations: the streaming kernel's structure, vector-ALU products
+    c.valu_stream = true;
+    c.rows_per_launch = qmm::kStreamMaxRows;
+    c.tile_rows = 1;
+    int nw = 8, cpw = 8;
+    stream_shape(p, &nw, &cpw);
+    c.wk = nw;
+    c.ntw = cpw;
+    c.nTB = nT;
+    c.lds = qmm::stream_lds_bytes(nw, cpw, std::min(rows, qmm::kStreamMaxRows), p->groups);
+    c.S = 1;
+    return c;
+  }
   if (variant == QMM_VARIANT_STREAM) {
     c.rows_per_launch = qmm::kStreamMaxRows;
     c.tile_rows = 1;
@@ -493,6 +510,8 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
       e = qmm::launch_stream(p->d.bits, p->step_gs, sf, cb.wk, cb.ntw, a, cb.lds, st);
     else if (vb == QMM_VARIANT_MFMA)
       e = qmm::launch_mfma(p->d.bits, sf, cb.tile_rows, cb.ntw, cb.wk, a, st);
+    else if (cb.valu_stream)
+      e = qmm::launch_stream_valu(p->d.bits, sf, cb.wk, cb.ntw, a, cb.lds, st);
     else
       e = qmm::launch_gemv(p->d.bits, xf, sf, cb.tile_rows, cb.ntw, a, cb.lds, st);
     if (e != hipSuccess) return hip_fail(e, "kernel launch");

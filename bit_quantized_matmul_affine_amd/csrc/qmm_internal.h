@@ -49,6 +49,10 @@ hipError_t launch_gemv(int bits, bool x_f32, bool sb_f32, int mr, int ntw, const
 // formats (step_gs = the group size; bf16 scales; see fmt_format).
 hipError_t launch_stream(int bits, int step_gs, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
                          size_t lds_bytes, hipStream_t st);
+// The streaming kernel's vector-ALU form (v_dot2_f32_bf16 on the same
+// operands, lane quarters added by cross-lane swaps) on the native layout.
+hipError_t launch_stream_valu(int bits, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
+                              size_t lds_bytes, hipStream_t st);
 // Rows the streaming kernel takes per launch (its waves stage every row of
 // their own chunks' activation slices in registers on the way to LDS).
 constexpr int kStreamMaxRows = 4;

@@ -25,6 +25,12 @@ namespace qmm {
 //   4. the NW partial tiles are added through LDS in wave order.
 // No barrier precedes step 3: a wave's compute starts as soon as its own
 // slices arrive, not when the slowest wave of the workgroup has its.
+// VALU = true is the vector-ALU form of step 3: per activation row, lane
+// (r, kg) takes the dot products of its B-operand pairs with the same A
+// fragments through v_dot2_f32_bf16, scales each group's dot by s, and lanes
+// kg = 0 add b' * (the group's sum of x); the four lane quarters of a row are
+// added by cross-lane swaps before the fold, and output row m comes from the
+// lanes kg = 0 of column r.
 // LDS per wave: rows x (CPW*256 + 16) bytes of slices (the 16-byte pad puts
 // consecutive rows on different banks) and rows x CPW x F::kGroups group sums.
 // ---------------------------------------------------------------------------
@@ -76,7 +82,7 @@ __device__ __forceinline__ void stamp_chunk(int j) {
   }
 }
 
-template <typename F, int NW, int CPW, int MQ>
+template <typename F, int NW, int CPW, int MQ, bool VALU = false>
 __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   constexpr int BITS = F::kBits, GC = F::kGroups, SPG = F::kSpg;
   using ST = typename F::St;
@@ -162,46 +168,99 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   ts.mark(3);
   // 3. compute in load order; rows past the last one read the last row
   //    (never stored)
-  const unsigned char* xrow = xw + min(r, a.M - 1) * ROWB;
-  const float* srow[MQ];
-#pragma unroll
-  for (int q = 0; q < MQ; ++q) srow[q] = xsum + min(4 * kg + q, a.M - 1) * CPW * GC;
-  const typename F::Masks mask_v = F::masks();
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const typename F::Masks mask_v = F::masks();
   f32x4 acc = zero;
+  if constexpr (!VALU) {
+    const unsigned char* xrow = xw + min(r, a.M - 1) * ROWB;
+    const float* srow[MQ];
 #pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const bool live = j < count;
-    stamp_chunk<CPW, F::kCodeLoads + 1>(j);  // timing build: wait for chunk j's
-    ts.mark(4 + j);                          // weights, then stamp their arrival
-    u32x4 A[4];
+    for (int q = 0; q < MQ; ++q) srow[q] = xsum + min(4 * kg + q, a.M - 1) * CPW * GC;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      A[t] = *reinterpret_cast<const u32x4*>(xrow + 256 * j + 16 * F::a_vec(t, kg));
-    float ex[MQ][GC];
+    for (int j = 0; j < CPW; ++j) {
+      const bool live = j < count;
+      stamp_chunk<CPW, F::kCodeLoads + 1>(j);  // timing build: wait for chunk j's
+      ts.mark(4 + j);                          // weights, then stamp their arrival
+      u32x4 A[4];
 #pragma unroll
-    for (int q = 0; q < MQ; ++q) load_floats<GC>(srow[q] + GC * j, ex[q]);
-    uint32_t P[16];
-    F::unpack(W[j], P, mask_v);
+      for (int t = 0; t < 4; ++t)
+        A[t] = *reinterpret_cast<const u32x4*>(xrow + 256 * j + 16 * F::a_vec(t, kg));
+      float ex[MQ][GC];
 #pragma unroll
-    for (int g = 0; g < GC; ++g) {
-      f32x4 dd = zero;
+      for (int q = 0; q < MQ; ++q) load_floats<GC>(srow[q] + GC * j, ex[q]);
+      uint32_t P[16];
+      F::unpack(W[j], P, mask_v);
 #pragma unroll
-      for (int u = 0; u < SPG; ++u) {
-        const int t = g * SPG + u;
-        const u32x4 B = {P[4 * t], P[4 * t + 1], P[4 * t + 2], P[4 * t + 3]};
-        dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[t]),
-                                                     __builtin_bit_cast(bf16x8, B), dd, 0, 0, 0);
+      for (int g = 0; g < GC; ++g) {
+        f32x4 dd = zero;
+#pragma unroll
+        for (int u = 0; u < SPG; ++u) {
+          const int t = g * SPG + u;
+          const u32x4 B = {P[4 * t], P[4 * t + 1], P[4 * t + 2], P[4 * t + 3]};
+          dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[t]),
+                                                       __builtin_bit_cast(bf16x8, B), dd, 0, 0, 0);
+        }
+        const Affine af = F::affine(g, SBv[j]);
+        const float sc = af.sc, bp = af.bp;
+#pragma unroll
+        for (int q = 0; q < MQ; ++q) {
+          const float v = fmaf(sc, dd[q], fmaf(bp, ex[q][g], acc[q]));
+          acc[q] = live ? v : acc[q];
+        }
       }
-      const Affine af = F::affine(g, SBv[j]);
-      const float sc = af.sc, bp = af.bp;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // rows q < MQ (rows past the last one read the last row, never stored)
+    const unsigned char* xrow[MQ];
+    const float* srow[MQ];
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) {
+      xrow[q] = xw + min(q, a.M - 1) * ROWB;
+      srow[q] = xsum + min(q, a.M - 1) * CPW * GC;
+    }
+    const float bias_lane = kg == 0 ? 1.f : 0.f;  // one quarter adds each group's bias term
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const bool live = j < count;
+      stamp_chunk<CPW, F::kCodeLoads + 1>(j);
+      ts.mark(4 + j);
+      uint32_t P[16];
+      F::unpack(W[j], P, mask_v);
 #pragma unroll
       for (int q = 0; q < MQ; ++q) {
-        const float v = fmaf(sc, dd[q], fmaf(bp, ex[q][g], acc[q]));
-        acc[q] = live ? v : acc[q];
+        u32x4 A[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          A[t] = *reinterpret_cast<const u32x4*>(xrow[q] + 256 * j + 16 * F::a_vec(t, kg));
+        float ex[GC];
+        load_floats<GC>(srow[q] + GC * j, ex);
+#pragma unroll
+        for (int g = 0; g < GC; ++g) {
+          float dot = 0.f;
+#pragma unroll
+          for (int u = 0; u < SPG; ++u) {
+            const int t = g * SPG + u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const uint32_t xa = A[t][i];  // (copied out: see the slice sums above)
+              dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, P[4 * t + i]),
+                                                    __builtin_bit_cast(bf16x2, xa), dot, false);
+            }
+          }
+          const Affine af = F::affine(g, SBv[j]);
+          const float v = fmaf(af.sc, dot, fmaf(af.bp * bias_lane, ex[g], acc[q]));
+          acc[q] = live ? v : acc[q];
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // add the four lane quarters of each row: lanes l, l^16, l^32, l^48
+#pragma unroll
+    for (int q = 0; q < MQ; ++q) {
+      acc[q] += __shfl_xor(acc[q], 16);
+      acc[q] += __shfl_xor(acc[q], 32);
+    }
   }
 
   ts.mark(12);
@@ -220,8 +279,9 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   const int n = tile * kTileN + r;
 #pragma unroll
   for (int q = 0; q < MQ; ++q) {
-    const int m = 4 * kg + q;
-    if (m < a.M) store_y<false>(a, (long)m * a.ldy + n, acc[q]);
+    // the matrix-core form holds rows 4kg + q, the vector-ALU form rows q (every quarter)
+    const int m = VALU ? q : 4 * kg + q;
+    if (m < a.M && (!VALU || kg == 0)) store_y<false>(a, (long)m * a.ldy + n, acc[q]);
   }
   ts.mark(14);
   ts.flush(lane);
@@ -235,14 +295,14 @@ bool stream_fits(int nw, int cpw, int M, int groups, size_t max_lds) {
   return M >= 1 && M <= kStreamMaxRows && stream_lds_bytes(nw, cpw, M, groups) <= max_lds;
 }
 
-template <typename F, int MQ>
+template <typename F, int MQ, bool VALU>
 static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_t lds,
                                      hipStream_t st) {
   const unsigned grid = (unsigned)(a.N / kTileN);
 #define QMM_STREAM(NWV, CPWV)                                                                \
   if constexpr (F::stream_fits(NWV, CPWV)) {                                                 \
     if (nw == NWV && cpw == CPWV) {                                                          \
-      auto* kfn = &stream_kernel<F, NWV, CPWV, MQ>;                                          \
+      auto* kfn = &stream_kernel<F, NWV, CPWV, MQ, VALU>;                                          \
       if (lds > 64 * 1024) {                                                                 \
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),               \
                                            hipFuncAttributeMaxDynamicSharedMemorySize,       \
@@ -259,12 +319,12 @@ static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_
   return hipErrorInvalidValue;
 }
 
-template <typename F>
+template <typename F, bool VALU = false>
 static hipError_t stream_dispatch(int nw, int cpw, const LaunchArgs& a, size_t lds,
                                   hipStream_t st) {
-  if (a.M == 1) return stream_dispatch_mq<F, 1>(nw, cpw, a, lds, st);
-  if (a.M == 2) return stream_dispatch_mq<F, 2>(nw, cpw, a, lds, st);
-  return stream_dispatch_mq<F, 4>(nw, cpw, a, lds, st);
+  if (a.M == 1) return stream_dispatch_mq<F, 1, VALU>(nw, cpw, a, lds, st);
+  if (a.M == 2) return stream_dispatch_mq<F, 2, VALU>(nw, cpw, a, lds, st);
+  return stream_dispatch_mq<F, 4, VALU>(nw, cpw, a, lds, st);
 }
 
 bool stream_step_fits(int bits, int group_size, int nw, int cpw) {
@@ -290,6 +350,15 @@ hipError_t launch_stream(int bits, int step_gs, bool sb_f32, int nw, int cpw, co
                   : stream_dispatch<NativeFmt<3, uint16_t>>(nw, cpw, a, lds_bytes, st);
   return sb_f32 ? stream_dispatch<NativeFmt<4, float>>(nw, cpw, a, lds_bytes, st)
                 : stream_dispatch<NativeFmt<4, uint16_t>>(nw, cpw, a, lds_bytes, st);
+}
+
+hipError_t launch_stream_valu(int bits, bool sb_f32, int nw, int cpw, const LaunchArgs& a,
+                              size_t lds_bytes, hipStream_t st) {
+  if (bits == 3)
+    return sb_f32 ? stream_dispatch<NativeFmt<3, float>, true>(nw, cpw, a, lds_bytes, st)
+                  : stream_dispatch<NativeFmt<3, uint16_t>, true>(nw, cpw, a, lds_bytes, st);
+  return sb_f32 ? stream_dispatch<NativeFmt<4, float>, true>(nw, cpw, a, lds_bytes, st)
+                : stream_dispatch<NativeFmt<4, uint16_t>, true>(nw, cpw, a, lds_bytes, st);
 }
 
 }  // namespace qmm
