@@ -105,11 +105,76 @@ def kernel_source_hash() -> str:
     import hashlib
     csrc = os.path.join(ROOT, "bit_quantized_matmul_affine_amd", "csrc")
     h = hashlib.sha256()
-    for name in ("qmm_device.h", "qmm_internal.h", "qmm_layout.hip", "qmm_mfma.hip",
-                 "qmm_resident.hip", "qmm_slab.hip", "qmm_stream.hip", "qmm_wide.hip"):
+    for name in ("qmm_device.h", "qmm_formats.h", "qmm_internal.h", "qmm_layout.hip",
+                 "qmm_mfma.hip", "qmm_resident.hip", "qmm_slab.hip", "qmm_stream.hip",
+                 "qmm_wide.hip"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+MATMUL_KERNELS = ("stream_kernel", "resident_kernel", "slab_kernel", "split_slab_kernel",
+                  "mfma_kernel", "gemv_kernel", "wide_kernel")
+
+
+def _counter_means(path: str, counter: str):
+    """Mean value of one counter per kernel name over a rocprofv3 --pmc CSV
+    (one row per dispatch and counter): {name: (dispatches, mean)}."""
+    import csv
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = r["Kernel_Name"].replace("void ", "").split("(")[0].replace("qmm::", "")
+            n, tot = acc.get(name, (0, 0.0))
+            acc[name] = (n + 1, tot + float(r["Counter_Value"]))
+    return {k: (n, tot / n) for k, (n, tot) in acc.items()}
+
+
+def traffic_summary(probe_csv: str, runs) -> str:
+    """HBM bytes per dispatch of the matmul kernel of each bench run.  runs:
+    (rows, FETCH_SIZE csv, WRITE_SIZE csv) of `bench.py --rows rows` under
+    `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE`; probe_csv: FETCH_SIZE
+    of `bench.py --probe-only` (1 GiB read per launch), which scales the
+    FETCH_SIZE KiB to bytes.  WRITE_SIZE is taken at face value (KiB).
+    Writes profiles/hbm_traffic.json and returns a markdown table."""
+    probe = [v for k, v in _counter_means(probe_csv, "FETCH_SIZE").items() if "probe_kernel" in k]
+    assert probe, "no probe_kernel dispatch in " + probe_csv
+    fetch_factor = (1 << 30) / 1024.0 / probe[0][1]
+    kernels = {}
+    for rows, fcsv, wcsv in runs:
+        fm = {k: v for k, v in _counter_means(fcsv, "FETCH_SIZE").items()
+              if k.split("<")[0] in MATMUL_KERNELS}
+        wm = {k: v for k, v in _counter_means(wcsv, "WRITE_SIZE").items()
+              if k.split("<")[0] in MATMUL_KERNELS}
+        assert len(fm) == 1 and list(fm) == list(wm), "one matmul kernel per run: %s" % list(fm)
+        name = next(iter(fm))
+        fk, wk = fm[name][1], wm[name][1]
+        e = kernels.setdefault(name, {"rows": [], "fetch_kib": [], "write_kib": []})
+        e["rows"].append(rows)
+        e["fetch_kib"].append(fk)
+        e["write_kib"].append(wk)
+    lines = ["| kernel | M | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | "
+             "algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|"]
+    out = {}
+    for name, e in kernels.items():
+        fk = sum(e["fetch_kib"]) / len(e["fetch_kib"])
+        wk = sum(e["write_kib"]) / len(e["write_kib"])
+        hbm = fk * 1024.0 * fetch_factor + wk * 1024.0
+        alg = sum(algorithmic_bytes(m) for m in e["rows"]) / len(e["rows"])
+        out[name] = {"rows": e["rows"], "fetch_kib": fk, "write_kib": wk, "hbm_bytes": hbm}
+        lines.append("| `%s` | %s | %.1f | %.1f | %d | %d | %.3f |" % (
+            name, ",".join(map(str, e["rows"])), fk, wk, hbm, alg, hbm / alg))
+    rec = {"kernel_source_sha256_16": kernel_source_hash(), "fetch_factor": fetch_factor,
+           "write_factor": 1.0, "kernels": out}
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines.append("")
+    lines.append("FETCH_SIZE scale: the probe reads 1 GiB per launch and FETCH_SIZE reports "
+                 "%.1f KiB for it: bytes = KiB x 1024 x %.4f.  Kernel sources: %s."
+                 % (probe[0][1], fetch_factor, rec["kernel_source_sha256_16"]))
+    return "\n".join(lines)
 
 
 def measured_traffic(rows: int):
@@ -461,12 +526,22 @@ def main() -> int:
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-dispatch duration statistics (median, p10, p90) of a "
                          "rocprofv3 --kernel-trace CSV and exit (no GPU needed)")
+    ap.add_argument("--traffic-summary", nargs="+", metavar="CSV",
+                    help="PROBE_FETCH_CSV ROWS:FETCH_CSV:WRITE_CSV ...: HBM bytes per dispatch "
+                         "from rocprofv3 --pmc runs; writes profiles/hbm_traffic.json (no GPU)")
     ap.add_argument("--probe-only", action="store_true",
                     help="only run the HBM read probe on a 1 GiB buffer five times (a kernel of "
                          "known traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return 0
+    if args.traffic_summary:
+        runs = []
+        for spec in args.traffic_summary[1:]:
+            m, fcsv, wcsv = spec.split(":")
+            runs.append((int(m), fcsv, wcsv))
+        print(traffic_summary(args.traffic_summary[0], runs))
         return 0
     ROWS = tuple(int(v) for v in args.rows.split(","))
     assert all(1 <= m <= 64 for m in ROWS), "row counts of the workload: 1..64"
