@@ -47,9 +47,14 @@ SIGNATURES = {
     "qmm_run_ex": (_c.c_int, [_P, _c.c_int32, _c.c_int32, _c.c_int32, _c.c_int32, _P, _P, _P,
                               _P, _c.c_int32, _P, _c.c_size_t, _P]),
     "qmm_run_noalloc": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _P]),
+    "qmm_run_sums": (_c.c_int, [_P, _P, _P, _c.c_int32, _P, _P, _P, _c.c_int32, _P, _c.c_size_t,
+                                _P]),
+    "qmm_sum_group": (_c.c_int32, [_P]),
     "qmm_run_gate_up": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _c.c_int32, _c.c_int32, _P]),
     "qmm_residual_rms_norm": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int32, _c.c_int64, _c.c_float,
                                          _c.c_int32, _P]),
+    "qmm_residual_rms_norm_ex": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int32, _c.c_int32,
+                                            _c.c_int32, _c.c_int64, _c.c_float, _c.c_int32, _P]),
     "qmm_debug_unpack": (_c.c_int, [_P, _P, _P, _P]),
     "qmm_get_stats": (_c.c_int, [_P, _P]),
     "qmm_last_error": (_c.c_char_p, []),
@@ -229,6 +234,29 @@ class Plan:
                                 _ptr(out), rows, _ptr(workspace), wsb, _stream(stream)))
         return out
 
+    def sum_group(self) -> int:
+        """Values per group of the group sums run_sums takes (qmm_sum_group)."""
+        return int(lib().qmm_sum_group(self._h))
+
+    def run_sums(self, x, x_sums, codes, sb, out=None, stream=None, workspace=None):
+        """y = x . W^T through qmm_run_sums: x_sums f32 [K / sum_group(), ld]
+        (ld a multiple of 16, >= rows rounded up to 16), as
+        residual_rms_norm(..., group_size=sum_group()) writes them."""
+        import torch
+        rows = x.numel() // self.K
+        if out is None:
+            out = torch.empty(*x.shape[:-1], self.N,
+                              dtype=torch.float32 if self.f32_out else x.dtype, device=x.device)
+        if x_sums.dtype != torch.float32 or x_sums.dim() != 2 or not x_sums.is_contiguous():
+            raise ValueError("x_sums must be a contiguous f32 [groups, ld] tensor")
+        if workspace is None:
+            workspace = self.workspace(self.workspace_bytes(rows), x.device, stream)
+        wsb = workspace.numel() if workspace is not None else 0
+        _check(lib().qmm_run_sums(self._h, _ptr(x), _ptr(x_sums), x_sums.shape[1], _ptr(codes),
+                                  _ptr(sb), _ptr(out), rows, _ptr(workspace), wsb,
+                                  _stream(stream)))
+        return out
+
     def run_noalloc(self, x, codes, sb, out=None, stream=None):
         """y = x . W^T through qmm_run_noalloc (the library's own device
         workspace; nothing is allocated by the library)."""
@@ -268,8 +296,10 @@ class Plan:
 
 
 def residual_rms_norm(x, update, weight, eps: float, residual=None, normalized=None,
-                      stream=None):
-    """(residual, normalized) of qmm_residual_rms_norm for [..., D] tensors."""
+                      stream=None, group_sums=None, group_size: int = 64):
+    """(residual, normalized) of qmm_residual_rms_norm for [..., D] tensors;
+    with group_sums (f32 [D / group_size, ld], ld >= rows) also the sum of
+    every group of group_size stored normalized values (qmm_residual_rms_norm_ex)."""
     import torch
     D = x.shape[-1]
     rows = x.numel() // D
@@ -285,9 +315,18 @@ def residual_rms_norm(x, update, weight, eps: float, residual=None, normalized=N
     if normalized is None:
         normalized = torch.empty_like(x)
     dt = {torch.bfloat16: QMM_BF16, torch.float32: QMM_F32}.get(x.dtype, -1)
-    _check(lib().qmm_residual_rms_norm(_ptr(x), _ptr(update), _ptr(weight), _ptr(residual),
-                                       _ptr(normalized), rows, D, float(eps), dt,
-                                       _stream(stream)))
+    if group_sums is None:
+        _check(lib().qmm_residual_rms_norm(_ptr(x), _ptr(update), _ptr(weight), _ptr(residual),
+                                           _ptr(normalized), rows, D, float(eps), dt,
+                                           _stream(stream)))
+    else:
+        if (group_sums.dtype != torch.float32 or group_sums.dim() != 2 or
+                not group_sums.is_contiguous()):
+            raise ValueError("group_sums must be a contiguous f32 [groups, ld] tensor")
+        _check(lib().qmm_residual_rms_norm_ex(_ptr(x), _ptr(update), _ptr(weight), _ptr(residual),
+                                              _ptr(normalized), _ptr(group_sums), group_size,
+                                              group_sums.shape[1], rows, D, float(eps), dt,
+                                              _stream(stream)))
     return residual, normalized
 
 

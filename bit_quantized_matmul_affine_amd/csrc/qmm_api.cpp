@@ -409,13 +409,23 @@ qmm_status hip_fail(hipError_t e, const char* what) {
               hipGetErrorString(e));
 }
 
+// Values per group of the group sums the plan's kernels use: 64 on the
+// native layout (a group of 128 is stored as two halves), else the plan's
+// group size.
+int sum_group(const qmm_plan* p) { return p->fmt || p->generic ? p->d.group_size : 64; }
+
 qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req, int s_req,
                     const void* x,
                     const void* codes, const void* sb, void* y, int32_t rows, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, void* stream, const float* xsums = nullptr,
+                    int32_t xsums_ld = 0) {
   if (qmm_status st = check_plan(p)) return st;
   if (rows < 1 || rows > p->d.max_rows)
     return fail(QMM_ERR_INVALID_ARG, "rows=%d outside 1..max_rows=%d", rows, p->d.max_rows);
+  if (xsums && (!aligned(xsums, 16) || xsums_ld % 16 != 0 || xsums_ld < (rows + 15) / 16 * 16))
+    return fail(QMM_ERR_INVALID_ARG,
+                "x_sums must be 16-byte aligned with sums_ld a multiple of 16 and at least rows "
+                "rounded up to 16 (rows=%d, sums_ld=%d)", rows, xsums_ld);
   if (!x || !codes || !sb || !y) return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(sb, 16) || !aligned(y, 4))
     return fail(QMM_ERR_INVALID_ARG, "x, codes and sb must be 16-byte aligned, y 4-byte aligned");
@@ -482,6 +492,12 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     a.sb = sb;
     a.y = static_cast<char*>(y) + (size_t)r0 * p->d.N * ye;
     a.y_f32 = p->f32_out ? 1 : 0;
+    // given group sums: the matrix-core streaming kernel, and the resident
+    // kernel where its 16-byte reads of four rows stay aligned
+    const bool takes_sums = (vb == QMM_VARIANT_STREAM) ||
+                            (vb == QMM_VARIANT_RESIDENT && r0 % 4 == 0);
+    a.xsums = xsums && takes_sums ? xsums + r0 : nullptr;
+    a.xsums_ld = xsums_ld;
     a.tickets = static_cast<uint32_t*>(ws);
     a.part = ws ? reinterpret_cast<float*>(static_cast<char*>(ws) + ticket_bytes(p)) : nullptr;
     a.M = rb;
@@ -671,6 +687,16 @@ qmm_status qmm_run(const qmm_plan* p, const void* x, const void* codes, const vo
   return run_impl(p, QMM_VARIANT_AUTO, 0, 0, 0, x, codes, sb, y, rows, ws, ws_bytes, stream);
 }
 
+qmm_status qmm_run_sums(const qmm_plan* p, const void* x, const float* x_sums, int32_t sums_ld,
+                        const void* codes, const void* sb, void* y, int32_t rows, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!x_sums) return fail(QMM_ERR_INVALID_ARG, "x_sums is NULL (use qmm_run)");
+  return run_impl(p, QMM_VARIANT_AUTO, 0, 0, 0, x, codes, sb, y, rows, ws, ws_bytes, stream,
+                  x_sums, sums_ld);
+}
+
+int32_t qmm_sum_group(const qmm_plan* p) { return p ? sum_group(p) : 0; }
+
 qmm_status qmm_run_ex(const qmm_plan* p, int32_t variant, int32_t ntw, int32_t kwaves,
                       int32_t splitk, const void* x, const void* codes, const void* sb, void* y,
                       int32_t rows, void* ws, size_t ws_bytes, void* stream) {
@@ -744,8 +770,26 @@ qmm_status qmm_run_gate_up(const qmm_plan* p, const void* x, const void* gate_co
 qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* weight,
                                  void* residual, void* normalized, int32_t rows, int64_t D,
                                  float eps, int32_t dtype, void* stream) {
+  return qmm_residual_rms_norm_ex(x, update, weight, residual, normalized, nullptr, 64, 0, rows,
+                                  D, eps, dtype, stream);
+}
+
+qmm_status qmm_residual_rms_norm_ex(const void* x, const void* update, const void* weight,
+                                    void* residual, void* normalized, float* group_sums,
+                                    int32_t group_size, int32_t sums_ld, int32_t rows, int64_t D,
+                                    float eps, int32_t dtype, void* stream) {
   if (!x || !update || !weight || !residual || !normalized)
     return fail(QMM_ERR_INVALID_ARG, "NULL data pointer");
+  if (group_sums) {
+    if (group_size != 32 && group_size != 64 && group_size != 128)
+      return fail(QMM_ERR_INVALID_ARG, "group_size=%d: 32, 64 or 128", group_size);
+    if (D % group_size != 0)
+      return fail(QMM_ERR_INVALID_ARG, "D=%lld is not a multiple of group_size=%d", (long long)D,
+                  group_size);
+    if (sums_ld < rows || !aligned(group_sums, 4))
+      return fail(QMM_ERR_INVALID_ARG, "sums_ld=%d must be >= rows=%d, group_sums 4-byte aligned",
+                  sums_ld, rows);
+  }
   if (!aligned(x, 16) || !aligned(update, 16) || !aligned(weight, 16) || !aligned(residual, 16) ||
       !aligned(normalized, 16))
     return fail(QMM_ERR_INVALID_ARG, "every buffer must be 16-byte aligned");
@@ -758,7 +802,8 @@ qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* 
     return fail(QMM_ERR_UNSUPPORTED, "D=%lld: a multiple of 8 from 8 to 16384 is supported",
                 (long long)D);
   if (hipError_t e = qmm::launch_residual_rms_norm(dtype == QMM_BF16, x, update, weight, residual,
-                                                   normalized, rows, (int)D, eps,
+                                                   normalized, rows, (int)D, eps, group_sums,
+                                                   group_size, sums_ld,
                                                    reinterpret_cast<hipStream_t>(stream)))
     return hip_fail(e, "kernel launch");
   return QMM_OK;

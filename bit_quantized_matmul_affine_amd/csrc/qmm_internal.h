@@ -30,6 +30,8 @@ struct LaunchArgs {
   const uint32_t* codes2; // fused gate/up: the up projection's codes (codes = gate)
   const void* sb2;        // fused gate/up: the up projection's scales/biases
   int y_f32;              // 1: y is f32 whatever x's dtype (QMM_FLAG_F32_OUT)
+  const float* xsums;     // null, or the group sums of x: [K/group][xsums_ld] (qmm_run_sums)
+  int xsums_ld;
 };
 
 // All launchers return hipSuccess or the launch error.
@@ -119,9 +121,12 @@ bool attention_supported(int D, int rep);
 hipError_t launch_attention(int bits, int D, int rep, const AttnArgs& a, hipStream_t st);
 
 bool residual_rms_norm_supported(long D);
+// sums: null, or the per-(group, row) sums of the stored normalized values
+// at sums[g * sums_ld + row] for groups of group_size (32, 64, 128) values.
 hipError_t launch_residual_rms_norm(bool bf16, const void* x, const void* update,
                                     const void* weight, void* residual, void* normalized,
-                                    int rows, int D, float eps, hipStream_t st);
+                                    int rows, int D, float eps, float* sums, int group_size,
+                                    int sums_ld, hipStream_t st);
 // Fused gate/up through the resident kernel: tile pairs per workgroup (1 or
 // 2) that are built for cq chunks, and the launch.
 bool gate_up_shape(int nC, int pairs, int* nw, int* cpw);

@@ -11,6 +11,14 @@
 // the residual sum is rounded before it is squared, the normalized value
 // before the weight multiplies it, and the weighted product is stored in T.
 //
+// With group sums (GL > 0 lanes per group of 8*GL values) the kernel also
+// writes, per row m and group g, the f32 sum of the group's stored
+// normalized values to sums[g * ld + m]: the per-group sum of x that the
+// projection's factored form needs for the bias term (the same page's
+// affine3-rows.ts header: s * sum(q x) + b * sum(x)), formed here while the
+// values are in registers.  Each thread adds its 8 values in order, then the
+// GL threads of a group add their partial sums by lane swaps (fixed order).
+//
 // gfx950 design: one workgroup of 256 threads per row; each thread owns
 // 8-value vectors (16 bytes of bf16) spread over the row.  The rounded
 // residuals stay in registers between the two passes (no second read); the
@@ -91,10 +99,11 @@ __device__ __forceinline__ float block_sum(float s, float* red) {
   return t;
 }
 
-template <bool BF16, int NV>
+template <bool BF16, int NV, int GL>
 __global__ void __launch_bounds__(kNormThreads) residual_rms_norm_kernel(
     const void* __restrict__ x, const void* __restrict__ update, const void* __restrict__ weight,
-    void* __restrict__ residual, void* __restrict__ normalized, int D, float eps) {
+    void* __restrict__ residual, void* __restrict__ normalized, int D, float eps,
+    float* __restrict__ sums, int ld) {
   __shared__ float red[kNormThreads / 64];
   const int row = blockIdx.x;
   const int nv = D / 8;  // 8-value vectors per row
@@ -121,28 +130,55 @@ __global__ void __launch_bounds__(kNormThreads) residual_rms_norm_kernel(
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int v = threadIdx.x + j * kNormThreads;
+    float gsum = 0.f;
     if (v < nv) {
       Vec8<BF16> wv, o;
       wv.load(weight, v);  // L2-resident after the first rows
 #pragma unroll
       for (int e = 0; e < 8; ++e) o.v[e] = wv.v[e] * round_t<BF16>(r[j].v[e] * inv);
       o.store(normalized, base + v);  // rounded to T by the store
+      if constexpr (GL > 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gsum += round_t<BF16>(o.v[e]);  // the stored values
+      }
+    }
+    if constexpr (GL > 0) {
+      // every lane takes part in the swaps; a group lies wholly below or
+      // above the row's end (D is a multiple of the group size)
+      if (j * kNormThreads < nv) {  // block-uniform
+#pragma unroll
+        for (int off = 1; off < GL; off <<= 1) gsum += __shfl_xor(gsum, off);
+        if (v < nv && (v & (GL - 1)) == 0) sums[(long)(v / GL) * ld + row] = gsum;
+      }
     }
   }
 }
 
-template <bool BF16>
+template <bool BF16, int GL>
 hipError_t norm_dispatch(const void* x, const void* u, const void* w, void* res, void* out,
-                         int rows, int D, float eps, hipStream_t st) {
+                         int rows, int D, float eps, float* sums, int ld, hipStream_t st) {
   const int nv = D / 8;
   const int per = (nv + kNormThreads - 1) / kNormThreads;
 #define QMM_NV(N)                                                                         \
   if (per <= N) {                                                                         \
-    residual_rms_norm_kernel<BF16, N><<<rows, kNormThreads, 0, st>>>(x, u, w, res, out, D, eps); \
+    residual_rms_norm_kernel<BF16, N, GL><<<rows, kNormThreads, 0, st>>>(x, u, w, res, out, D, \
+                                                                        eps, sums, ld);   \
     return hipGetLastError();                                                             \
   }
   QMM_NV(1) QMM_NV(2) QMM_NV(4) QMM_NV(8)
 #undef QMM_NV
+  return hipErrorInvalidValue;
+}
+
+template <bool BF16>
+hipError_t norm_dispatch_gs(const void* x, const void* u, const void* w, void* res, void* out,
+                            int rows, int D, float eps, float* sums, int group_size, int ld,
+                            hipStream_t st) {
+  if (!sums) return norm_dispatch<BF16, 0>(x, u, w, res, out, rows, D, eps, nullptr, 0, st);
+  if (group_size == 32) return norm_dispatch<BF16, 4>(x, u, w, res, out, rows, D, eps, sums, ld, st);
+  if (group_size == 64) return norm_dispatch<BF16, 8>(x, u, w, res, out, rows, D, eps, sums, ld, st);
+  if (group_size == 128)
+    return norm_dispatch<BF16, 16>(x, u, w, res, out, rows, D, eps, sums, ld, st);
   return hipErrorInvalidValue;
 }
 
@@ -154,9 +190,13 @@ bool residual_rms_norm_supported(long D) {
 
 hipError_t launch_residual_rms_norm(bool bf16, const void* x, const void* update,
                                     const void* weight, void* residual, void* normalized,
-                                    int rows, int D, float eps, hipStream_t st) {
-  if (bf16) return norm_dispatch<true>(x, update, weight, residual, normalized, rows, D, eps, st);
-  return norm_dispatch<false>(x, update, weight, residual, normalized, rows, D, eps, st);
+                                    int rows, int D, float eps, float* sums, int group_size,
+                                    int sums_ld, hipStream_t st) {
+  if (bf16)
+    return norm_dispatch_gs<true>(x, update, weight, residual, normalized, rows, D, eps, sums,
+                                  group_size, sums_ld, st);
+  return norm_dispatch_gs<false>(x, update, weight, residual, normalized, rows, D, eps, sums,
+                                 group_size, sums_ld, st);
 }
 
 }  // namespace qmm

@@ -45,22 +45,27 @@ __device__ __forceinline__ float silu_mul(float gate, float up) {
   return silu * u;  // rounded to bf16 by the store
 }
 
-// Timing build: the wait for chunk j's weights (LPT*TM loads per later chunk
+// Timing build: the wait for chunk j's weights (LPC loads per later chunk
 // outstanding); j is a constant once the caller's loop is unrolled.
-template <int CPW, int TM, int LPT, int J = 0>
+template <int CPW, int LPC, int J = 0>
 __device__ __forceinline__ void stamp_chunk(int j) {
   if constexpr (J < CPW) {
     if (j == J)
-      stamp_wait<(CPW - 1 - J) * TM * LPT>();
+      stamp_wait<(CPW - 1 - J) * LPC>();
     else
-      stamp_chunk<CPW, TM, LPT, J + 1>(j);
+      stamp_chunk<CPW, LPC, J + 1>(j);
   }
 }
 
-template <typename F, int NW, int CPW, int TM, bool GU = false>
+// XS = true: the group sums of x come from a.xsums (qmm_run_sums; written by
+// the residual add + RMS norm that produced x) in place of the all-ones
+// products: per chunk and group, lane (r, kb) loads the sums of rows
+// 4kb .. 4kb+3 (one 16-byte load, issued with the chunk's weights).
+template <typename F, int NW, int CPW, int TM, bool GU = false, bool XS = false>
 __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   constexpr int BITS = F::kBits, GC = F::kGroups, SPG = F::kSpg;
   constexpr int LPT = F::kCodeLoads + 1;  // loads per (chunk, tile slot)
+  constexpr int LPC = TM * LPT + (XS ? GC : 0);  // loads per chunk
   using ST = typename F::St;
   constexpr int TMH = GU ? TM / 2 : TM;  // distinct tiles per workgroup
   static_assert(!GU || TM % 2 == 0, "gate/up slots come in pairs");
@@ -109,9 +114,16 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   const ST* __restrict__ sbp2 = reinterpret_cast<const ST*>(a.sb2);
   uint32_t W[CPW][TM][BITS];
   typename F::Sb SBv[CPW][TM];
+  f32x4 exv[XS ? CPW : 1][GC];
 #pragma unroll
   for (int j = 0; j < CPW; ++j) {
     const int c = min(w + j * NW, clast);
+    if constexpr (XS) {
+#pragma unroll
+      for (int g = 0; g < GC; ++g)
+        exv[j][g] = *reinterpret_cast<const f32x4*>(a.xsums + (long)(GC * c + g) * a.xsums_ld +
+                                                    4 * kg);
+    }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const bool second = GU && t >= TMH;  // compile-time once unrolled
@@ -128,7 +140,7 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   //    wait also drains the LDS counter: until it does, the compiler counts
   //    the LDS-direct loads as pending on both counters and may turn later
   //    weight waits into full ones (vmcnt(0)).
-  wait_vm_lds<(CPW * TM * LPT < 63 ? CPW * TM * LPT : 63)>();
+  wait_vm_lds<(CPW * LPC < 63 ? CPW * LPC : 63)>();
   ts.mark(2);
 
   // 3. compute in load order; rows past the last one read the last row
@@ -145,7 +157,7 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   for (int j = 0; j < CPW; ++j) {
     const bool live = j < count;
     const int c = min(w + j * NW, clast);
-    stamp_chunk<CPW, TM, LPT>(j);  // timing build: wait for chunk j's weights,
+    stamp_chunk<CPW, LPC>(j);      // timing build: wait for chunk j's weights,
     ts.mark(3 + j);                // then stamp their arrival
     const u32x4* xrow = reinterpret_cast<const u32x4*>(lds + (size_t)c * M * 256) + xm * 16;
     u32x4 A[4];
@@ -155,12 +167,16 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
     f32x4 ex[GC];
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
-      f32x4 e = zero;
+      if constexpr (XS) {
+        ex[g] = exv[j][g];
+      } else {
+        f32x4 e = zero;
 #pragma unroll
-      for (int u = 0; u < SPG; ++u)
-        e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[g * SPG + u]),
-                                                    __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
-      ex[g] = e;
+        for (int u = 0; u < SPG; ++u)
+          e = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[g * SPG + u]),
+                                                      __builtin_bit_cast(bf16x8, ones), e, 0, 0, 0);
+        ex[g] = e;
+      }
     }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
@@ -261,13 +277,29 @@ size_t resident_lds_bytes(int nw, int tm, int M, int K) {
   return std::max((size_t)resident_rows(M) * K * 2, (size_t)tm * nw * 64 * 16);
 }
 
+// Shapes built with given group sums: eight waves or fewer, and at most 48
+// registers of sums (4 * GC per chunk); other shapes form their own sums.
+template <typename F, bool XS>
+constexpr bool resident_built(int nw, int cpw, int tm) {
+  return F::resident_fits(nw, cpw, tm) && (!XS || (nw <= 8 && cpw * F::kGroups * 4 <= 48));
+}
+
 template <typename F>
-static hipError_t resident_dispatch(int nw, int cpw, int tm, const LaunchArgs& a, int grid,
-                                    size_t lds, hipStream_t st) {
+static bool resident_xs_shape(int nw, int cpw, int tm) {
+#define QMM_HAS(W, C, T) \
+  if (nw == W && cpw == C && tm == T) return resident_built<F, true>(W, C, T);
+  QMM_RESIDENT_SHAPES(QMM_HAS)
+#undef QMM_HAS
+  return false;
+}
+
+template <typename F, bool XS>
+static hipError_t resident_dispatch_xs(int nw, int cpw, int tm, const LaunchArgs& a, int grid,
+                                       size_t lds, hipStream_t st) {
 #define QMM_GO(W, C, T)                                                                       \
-  if constexpr (F::resident_fits(W, C, T)) {                                                  \
+  if constexpr (resident_built<F, XS>(W, C, T)) {                                             \
     if (nw == W && cpw == C && tm == T) {                                                     \
-      auto* kfn = &resident_kernel<F, W, C, T>;                                               \
+      auto* kfn = &resident_kernel<F, W, C, T, false, XS>;                                               \
       hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),                  \
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
       if (e != hipSuccess) return e;                                                          \
@@ -278,6 +310,16 @@ static hipError_t resident_dispatch(int nw, int cpw, int tm, const LaunchArgs& a
   QMM_RESIDENT_SHAPES(QMM_GO)
 #undef QMM_GO
   return hipErrorInvalidValue;
+}
+
+template <typename F>
+static hipError_t resident_dispatch(int nw, int cpw, int tm, const LaunchArgs& a, int grid,
+                                    size_t lds, hipStream_t st) {
+  if (a.xsums && resident_xs_shape<F>(nw, cpw, tm))
+    return resident_dispatch_xs<F, true>(nw, cpw, tm, a, grid, lds, st);
+  LaunchArgs b = a;
+  b.xsums = nullptr;
+  return resident_dispatch_xs<F, false>(nw, cpw, tm, b, grid, lds, st);
 }
 
 hipError_t launch_resident(int bits, int step_gs, bool sb_f32, int nw, int cpw, int tm,

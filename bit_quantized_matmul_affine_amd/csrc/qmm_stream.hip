@@ -31,6 +31,9 @@ namespace qmm {
 // kg = 0 add b' * (the group's sum of x); the four lane quarters of a row are
 // added by cross-lane swaps before the fold, and output row m comes from the
 // lanes kg = 0 of column r.
+// XS = true takes the group sums of x from a.xsums (qmm_run_sums: written by
+// the residual add + RMS norm that produced x) instead of forming them from
+// the slices: loaded with the slices, stored to the same LDS area.
 // LDS per wave: rows x (CPW*256 + 16) bytes of slices (the 16-byte pad puts
 // consecutive rows on different banks) and rows x CPW x F::kGroups group sums.
 // ---------------------------------------------------------------------------
@@ -82,7 +85,7 @@ __device__ __forceinline__ void stamp_chunk(int j) {
   }
 }
 
-template <typename F, int NW, int CPW, int MQ, bool VALU = false>
+template <typename F, int NW, int CPW, int MQ, bool VALU = false, bool XS = false>
 __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
   constexpr int BITS = F::kBits, GC = F::kGroups, SPG = F::kSpg;
   using ST = typename F::St;
@@ -118,6 +121,20 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
     xv[i] = *reinterpret_cast<const u32x4*>(xg + (long)m * a.ldx + kChunkK * c + 8 * e);
     xo[i] = m * ROWB + j * 256 + 16 * e;
   }
+  // XS: the given group sums of this wave's entries (row m, slot j, group g)
+  // in the LDS order of the sums, (m * CPW + j) * GC + g
+  constexpr int XSL = XS ? (MQ * CPW * GC + 63) / 64 : 1;
+  const int ns = a.M * CPW * GC;
+  float xsv[XSL];
+  if constexpr (XS) {
+#pragma unroll
+    for (int i = 0; i < XSL; ++i) {
+      const int e = min(lane + 64 * i, ns - 1);
+      const int m = e / (CPW * GC), j = (e / GC) % CPW, g = e % GC;
+      const int c = min(w + j * NW, clast);
+      xsv[i] = a.xsums[(long)(GC * c + g) * a.xsums_ld + m];
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   ts.mark(1);
 
@@ -143,6 +160,7 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
 #pragma unroll
   for (int i = 0; i < XL; ++i) {
     *reinterpret_cast<u32x4*>(xw + xo[i]) = xv[i];
+    if constexpr (XS) continue;
     // (each element is copied out first: a bit cast of a vector subscript
     // compiles to element 0 here)
     float s = 0.f;
@@ -158,6 +176,11 @@ __global__ void __launch_bounds__(NW * 64) stream_kernel(LaunchArgs a) {
       const int m = v / (CPW * 16), rem = v - m * (CPW * 16);
       xsum[(m * CPW + (rem >> 4)) * GC + (rem & 15) / F::kGroupVecs] = s;
     }
+  }
+  if constexpr (XS) {
+#pragma unroll
+    for (int i = 0; i < XSL; ++i)
+      if (lane + 64 * i < ns) xsum[lane + 64 * i] = xsv[i];
   }
   // other lanes of this wave read what these lanes wrote: keep the compiler
   // from moving the reads above the writes (LDS runs a wave's accesses in order)
@@ -295,14 +318,14 @@ bool stream_fits(int nw, int cpw, int M, int groups, size_t max_lds) {
   return M >= 1 && M <= kStreamMaxRows && stream_lds_bytes(nw, cpw, M, groups) <= max_lds;
 }
 
-template <typename F, int MQ, bool VALU>
+template <typename F, int MQ, bool VALU, bool XS>
 static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_t lds,
                                      hipStream_t st) {
   const unsigned grid = (unsigned)(a.N / kTileN);
 #define QMM_STREAM(NWV, CPWV)                                                                \
   if constexpr (F::stream_fits(NWV, CPWV)) {                                                 \
     if (nw == NWV && cpw == CPWV) {                                                          \
-      auto* kfn = &stream_kernel<F, NWV, CPWV, MQ, VALU>;                                          \
+      auto* kfn = &stream_kernel<F, NWV, CPWV, MQ, VALU, XS>;                                          \
       if (lds > 64 * 1024) {                                                                 \
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),               \
                                            hipFuncAttributeMaxDynamicSharedMemorySize,       \
@@ -319,12 +342,21 @@ static hipError_t stream_dispatch_mq(int nw, int cpw, const LaunchArgs& a, size_
   return hipErrorInvalidValue;
 }
 
+template <typename F, bool VALU, bool XS>
+static hipError_t stream_dispatch_xs(int nw, int cpw, const LaunchArgs& a, size_t lds,
+                                     hipStream_t st) {
+  if (a.M == 1) return stream_dispatch_mq<F, 1, VALU, XS>(nw, cpw, a, lds, st);
+  if (a.M == 2) return stream_dispatch_mq<F, 2, VALU, XS>(nw, cpw, a, lds, st);
+  return stream_dispatch_mq<F, 4, VALU, XS>(nw, cpw, a, lds, st);
+}
+
+// The matrix-core form takes given group sums (a.xsums); the vector-ALU form
+// always forms its own.
 template <typename F, bool VALU = false>
 static hipError_t stream_dispatch(int nw, int cpw, const LaunchArgs& a, size_t lds,
                                   hipStream_t st) {
-  if (a.M == 1) return stream_dispatch_mq<F, 1, VALU>(nw, cpw, a, lds, st);
-  if (a.M == 2) return stream_dispatch_mq<F, 2, VALU>(nw, cpw, a, lds, st);
-  return stream_dispatch_mq<F, 4, VALU>(nw, cpw, a, lds, st);
+  if (!VALU && a.xsums) return stream_dispatch_xs<F, false, true>(nw, cpw, a, lds, st);
+  return stream_dispatch_xs<F, VALU, false>(nw, cpw, a, lds, st);
 }
 
 bool stream_step_fits(int bits, int group_size, int nw, int cpw) {

@@ -203,6 +203,26 @@ qmm_status qmm_run_ex(const qmm_plan* plan, int32_t variant, int32_t ntw, int32_
                       void* y, int32_t rows, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Values per group of the group sums qmm_run_sums takes for this plan: 64
+ * for 3- and 4-bit weights (a group of 128 is stored as two halves of 64 with
+ * the same scale and bias), else the plan's group size.  0 for NULL. */
+int32_t qmm_sum_group(const qmm_plan* plan);
+
+/* qmm_run with the per-group sums of x given (the bias term of the factored
+ * form sum_g s * sum(q x) + b * sum(x), page "@mlx-bun/inference 0.0.0-stage
+ * -> 1.0.0", affine3-rows.ts header), as qmm_residual_rms_norm_ex writes
+ * them while it produces x: x_sums f32 [K / qmm_sum_group(plan)][sums_ld],
+ * element (g, m) the sum of x[m][g*G .. (g+1)*G) for G = qmm_sum_group(plan),
+ * 16-byte aligned, sums_ld a multiple of 16 and >= rows rounded up to 16
+ * (entries of rows >= `rows` are read and never affect y).  The streaming
+ * and resident kernels use them in place of forming them (the resident
+ * kernel where its shape has the registers for them); the other families,
+ * and the vector-ALU forms, form their own.  Otherwise as qmm_run;
+ * QMM_ERR_INVALID_ARG for a NULL x_sums or a sums_ld outside these rules. */
+qmm_status qmm_run_sums(const qmm_plan* plan, const void* x, const float* x_sums,
+                        int32_t sums_ld, const void* codes, const void* sb, void* y,
+                        int32_t rows, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Fused gate/up projections of a gated MLP with a SiLU-times-up epilogue
  * ("mlx-bun 0.4.0 -> 1.0.0" page, trellis-shared-m.ts, its gate/up kernel:
  * both projections of one activation row block, then sigmoid, SiLU and
@@ -238,6 +258,21 @@ qmm_status qmm_run_gate_up(const qmm_plan* plan, const void* x, const void* gate
 qmm_status qmm_residual_rms_norm(const void* x, const void* update, const void* weight,
                                  void* residual, void* normalized, int32_t rows, int64_t D,
                                  float eps, int32_t dtype, void* stream);
+
+/* qmm_residual_rms_norm that also writes, when group_sums is not NULL, the
+ * sum of every group of group_size (32, 64, 128) stored normalized values:
+ * group_sums[g * sums_ld + m] = sum over i in [g*group_size, (g+1)*group_size)
+ * of normalized[m][i] as stored (each thread adds its 8 values in order, the
+ * threads of a group add their partial sums by lane swaps in a fixed order;
+ * f32).  These are the sums qmm_run_sums takes for the projection that reads
+ * `normalized` (group_size = qmm_sum_group of its plan; sums_ld as that call
+ * needs).  Errors as qmm_residual_rms_norm, plus QMM_ERR_INVALID_ARG for a
+ * group size other than 32, 64, 128, D not a multiple of it, sums_ld < rows
+ * or a misaligned group_sums. */
+qmm_status qmm_residual_rms_norm_ex(const void* x, const void* update, const void* weight,
+                                    void* residual, void* normalized, float* group_sums,
+                                    int32_t group_size, int32_t sums_ld, int32_t rows, int64_t D,
+                                    float eps, int32_t dtype, void* stream);
 
 /* Decode attention over an affine-quantized KV cache ("mlx-bun 0.0.4" page,
  * fused-decode-kernel.ts): one query row per head, head h attending to all N

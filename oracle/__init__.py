@@ -29,6 +29,8 @@ from .oracle import (  # noqa: F401
     round_f32,
     residual_rms_norm,
     residual_rms_norm_tolerance,
+    group_sums,
+    group_sum_tolerance,
     unpack_lsb,
     dequant_rows,
     decode_attention,

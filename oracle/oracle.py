@@ -379,6 +379,33 @@ def residual_rms_norm_tolerance(normalized_ref, D: int, dtype: str) -> np.ndarra
     return np.abs(normalized_ref) * (2 * ulp + (D + 2) * 2.0 ** -24) + 1e-30
 
 
+def group_sums(values, group_size: int) -> np.ndarray:
+    """Sum of every group of group_size consecutive values of each row, in
+    float64, group-major: out[g, m] = sum of values[m, g*G .. (g+1)*G) for
+    G = group_size.  The sum of x per quantization group is what the bias
+    term of the factored form takes ("@mlx-bun/inference 0.0.0-stage ->
+    1.0.0" page, affine3-rows.ts header: s * sum(q x) + b * sum(x)); the
+    residual add + RMS norm can hand it to the projection it feeds."""
+    v = np.asarray(values, dtype=np.float64)
+    rows, D = v.shape
+    if D % group_size != 0:
+        raise ValueError("D=%d is not a multiple of group_size=%d" % (D, group_size))
+    out = np.zeros((D // group_size, rows), dtype=np.float64)
+    for g in range(D // group_size):
+        for i in range(g * group_size, (g + 1) * group_size):
+            out[g] += v[:, i]
+    return out
+
+
+def group_sum_tolerance(values, group_size: int) -> np.ndarray:
+    """Bound on |f32 sum - exact sum| of each group (group-major like
+    group_sums) for an f32 evaluation in any order of group_size exact
+    terms: at most group_size - 1 roundings of relative size u = 2^-24 on any
+    term's path, so (G-1) u / (1 - (G-1) u) times the sum of the magnitudes."""
+    p = (group_size - 1) * F32_UNIT
+    return p / (1.0 - p) * group_sums(np.abs(np.asarray(values, dtype=np.float64)), group_size)
+
+
 # ---------------------------------------------------------------------------
 # Decode attention over an affine-quantized KV cache ("mlx-bun 0.0.4" page,
 # fused-decode-kernel.ts): one query row per head attends to all N cached

@@ -166,3 +166,30 @@ def test_noalloc_refuses_oversized_calls_without_gpu():
     assert b"qmm_run_noalloc holds" in L.qmm_last_error()
     q = b.Plan(3, 5120, 10240, 64, "bf16")
     assert 0 < L.qmm_workspace_bytes_ex(q.handle, 0, 0, 0, 0, 64) <= 8 << 20
+
+
+def test_group_sum_entry_points_validate_without_gpu():
+    """qmm_sum_group names the group width of the sums qmm_run_sums takes (64
+    on the native layout, groups of 128 included; the group size otherwise);
+    qmm_run_sums and qmm_residual_rms_norm_ex reject bad sums arguments before
+    any HIP call."""
+    L = b.lib()
+    assert b.Plan(3, 5120, 10240, 16, "bf16").sum_group() == 64
+    assert b.Plan(4, 5120, 10240, 16, "bf16", group_size=128).sum_group() == 64
+    assert b.Plan(2, 5120, 10240, 16, "bf16", group_size=32).sum_group() == 32
+    assert b.Plan(8, 5120, 10240, 16, "bf16", group_size=128).sum_group() == 128
+    assert L.qmm_sum_group(None) == 0
+    p = b.Plan(3, 5120, 10240, 16, "bf16")
+    fake = ctypes.c_void_p(1 << 20)
+    run = lambda sums, ld, rows: L.qmm_run_sums(p.handle, fake, sums, ld, fake, fake, fake, rows,
+                                                None, 0, None)
+    assert run(None, 16, 4) == b.QMM_ERR_INVALID_ARG
+    assert b"x_sums is NULL" in L.qmm_last_error()
+    assert run(fake, 8, 4) == b.QMM_ERR_INVALID_ARG       # not a multiple of 16
+    assert run(fake, 16, 17) == b.QMM_ERR_INVALID_ARG     # below rows rounded up to 16
+    assert run(ctypes.c_void_p((1 << 20) + 4), 16, 4) == b.QMM_ERR_INVALID_ARG  # misaligned
+    norm = lambda sums, gs, ld, D: L.qmm_residual_rms_norm_ex(fake, fake, fake, fake, fake, sums,
+                                                             gs, ld, 4, D, 1e-5, b.QMM_BF16, None)
+    assert norm(fake, 48, 16, 512) == b.QMM_ERR_INVALID_ARG   # not an MLX group size
+    assert norm(fake, 64, 16, 96) == b.QMM_ERR_INVALID_ARG    # D not a multiple of 64
+    assert norm(fake, 64, 2, 512) == b.QMM_ERR_INVALID_ARG    # sums_ld below rows

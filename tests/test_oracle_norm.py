@@ -93,3 +93,36 @@ def test_rounding_points():
     res, norm = oracle.residual_rms_norm(x, u, np.array([1.0078125, 1.0078125]), 0.0, "bf16")
     # 1.0078125 * 229/512 = 0.450759 = 230.79 steps of 2^-9 -> 231/512
     assert norm[0, 0] == 231 / 512
+
+
+def test_group_sums_hand_worked():
+    """Group-major sums of hand-worked rows (groups of 4): row 0 is 1..8, row
+    1 mixes signs; out[g, m] is group g of row m."""
+    v = np.array([[1, 2, 3, 4, 5, 6, 7, 8], [-1, 0, 1, 0, 2, 2, 2, 2]], dtype=np.float64)
+    got = oracle.group_sums(v, 4)
+    assert got.shape == (2, 2)
+    assert got.tolist() == [[10.0, 0.0], [26.0, 8.0]]
+    assert oracle.group_sums(np.ones((3, 128)), 64).tolist() == [[64.0] * 3, [64.0] * 3]
+    with pytest.raises(ValueError):
+        oracle.group_sums(v, 3)
+
+
+def test_group_sum_tolerance_covers_f32_orders():
+    """The bound holds for the sequential f32 sum and a pairwise f32 sum of
+    bf16 values, and is zero-width where the terms are exact in f32 (small
+    integers)."""
+    rng = np.random.default_rng(5)
+    v = oracle.round_bf16(rng.standard_normal((4, 256)) * 3.0)
+    exact = oracle.group_sums(v, 64)
+    tol = oracle.group_sum_tolerance(v, 64)
+    f = v.astype(np.float32).reshape(4, 4, 64)
+    seq = np.zeros((4, 4), dtype=np.float32)
+    for i in range(64):
+        seq = np.float32(seq + f[:, :, i])
+    pair = f
+    while pair.shape[-1] > 1:
+        pair = (pair[..., 0::2] + pair[..., 1::2]).astype(np.float32)
+    for got in (seq.T, pair[..., 0].T):
+        assert np.all(np.abs(got.astype(np.float64) - exact) <= tol)
+    ints = np.arange(128, dtype=np.float64).reshape(1, 128)
+    assert oracle.group_sums(ints, 64).tolist() == [[2016.0], [6112.0]]
