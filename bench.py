@@ -485,7 +485,8 @@ def other_workloads(torch, binding, synth, probe):
             fmt["%d-bit group-%d, %d row%s" % (bits, gs, rows, "s" if rows > 1 else "")] = {
                 "us": round(us, 3), "weight_bytes": pf.weight_bytes, "weight_GBps": round(gb, 1),
                 "variant": v, "frac_of_measured_peak": round(gb / probe, 4) if probe else None}
-    out["format variants 5120->10240, bf16 (generic: the step-layout kernel)"] = fmt
+    out["format variants 5120->10240, bf16 (step layout on the streaming and resident "
+        "kernels; 3/4-bit groups of 128 on the native layout)"] = fmt
     out["residual add + RMS norm, bf16"] = {
         "4x3840 (decode)": time_norm(torch, binding, synth, 4, 3840),
         "16384x5120 (HBM-bound)": time_norm(torch, binding, synth, 16384, 5120)}
