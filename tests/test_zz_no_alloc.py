@@ -46,6 +46,20 @@ def test_noalloc_matches_qmm_run_two_calls_in_a_row():
                              label="noalloc rows %d" % rows)
 
 
+def test_noalloc_step_layout_plan():
+    """A plan of another format (8-bit weights, groups of 32: the step layout
+    on the streaming and resident kernels, no workspace) through
+    qmm_run_noalloc equals qmm_run."""
+    p = synth.small(56, bits=8, K=2048, N=512, M=16, group_size=32)
+    r = Runner(p, max_rows=16)
+    for rows in (16, 1):
+        say("noalloc step layout rows", rows)
+        need, st, y_run, y_na = _both(r, rows)
+        assert need == 0 and st["last_variant"] in ("stream", "resident"), (need, st)
+        assert np.array_equal(y_na, y_run)
+        check_against_oracle(p.rows(rows), y_na, rows=rows, label="noalloc 8-bit g32 rows %d" % rows)
+
+
 def test_noalloc_smaller_plan_after_larger_and_no_workspace_case():
     """A different, smaller projection after the large one (its ticket words
     sit at the same place in the array), then a call that needs no workspace
