@@ -16,7 +16,8 @@
  *     weight is scale*q + bias.  The hot path is the pages' 3- and 4-bit,
  *     group-64 format; width 8 and group sizes 32 and 128 (which the pages
  *     name for their affine KV cache, "mlx-bun 0.0.4" page,
- *     fused-decode-kernel.ts) and MLX's width 2 run on a generic kernel.
+ *     fused-decode-kernel.ts) and MLX's width 2 run on the same matrix-core
+ *     kernels through a second layout (qmm_desc).
  *   - affine-split-mma.ts, affineSplitMma(): x [..., K] times W^T gives
  *     [..., N] in x's dtype; it borrows its inputs and throws when there are
  *     no rows.  affineSplitMmaEligible(): a separate yes/no predicate (affine,
@@ -24,8 +25,10 @@
  * So for rows m < M and outputs n < N, with gs the group size:
  *     y[m][n] = sum_k x[m][k] * (scale[n][k/gs] * q(n,k) + bias[n][k/gs]).
  * Beside it: the fused gate/up projection pair (qmm_run_gate_up), residual
- * add + RMS normalization (qmm_residual_rms_norm) and decode attention over
- * an affine-quantized KV cache (qmm_decode_attention).
+ * add + RMS normalization (qmm_residual_rms_norm, and with the per-group
+ * sums of its output for the projection, qmm_residual_rms_norm_ex and
+ * qmm_run_sums) and decode attention over an affine-quantized KV cache
+ * (qmm_decode_attention).
  * Summation order is the kernels' own (not bit-identical to any other
  * implementation); each kernel is deterministic run to run.
  *
@@ -66,17 +69,23 @@ typedef enum { QMM_F32 = 0, QMM_BF16 = 1 } qmm_dtype;
 /* Kernel families (qmm_run picks one; qmm_run_ex can force one). */
 typedef enum {
   QMM_VARIANT_AUTO = 0,
-  QMM_VARIANT_GEMV = 1,   /* vector-ALU kernel, activations staged in LDS; 1..8 rows per pass */
+  QMM_VARIANT_GEMV = 1,   /* vector-ALU kernels: for bf16 activations the streaming kernel's
+                             structure with v_dot2_f32_bf16 products (1..4 rows per launch);
+                             for f32 activations (the default for them) a kernel staging the
+                             activations of its K split in LDS, 1..8 rows per pass */
   QMM_VARIANT_MFMA = 2,   /* blocked matrix-core kernel (bf16 in, f32 accumulate), 1..64 rows
                              per pass; bf16 activations only */
   QMM_VARIANT_STREAM = 3, /* matrix-core kernel for 1..4 rows per launch (more rows run as
                              blocks of 4): one workgroup per 16 rows of W, each wave stages
                              the activations of its own chunks and issues all its weight
-                             loads up front; K <= 16384; bf16 activations */
+                             loads up front; K <= 16384; bf16 activations; also runs the
+                             other formats (default for 1..2 rows) */
   QMM_VARIANT_RESIDENT = 4, /* matrix-core kernel for 1..16 rows whose activation block fits in
                                one compute unit's LDS (rows*K*2 <= 160 KB, K <= 16384): one
                                workgroup holds up to four 16-row tiles of W, each wave takes
-                               a share of K for all of them; bf16 activations */
+                               a share of K for all of them; bf16 activations; also runs the
+                               other formats (default from 3 rows, as many rows per launch as
+                               fit the LDS, at most 16) */
   QMM_VARIANT_SLAB = 5      /* matrix-core kernel for 17..64 rows per pass: one workgroup per
                                compute unit owning three 16-row tiles of W, activations streamed
                                through an LDS ring in slices of 512 columns by loader waves;
@@ -87,8 +96,9 @@ typedef enum {
                                splitk = 2 the split one at 17..32 rows too);
                                built for K = 5120 and 8192; bf16 activations */,
   QMM_VARIANT_GENERIC = 6   /* vector-ALU kernel for the other formats (bits 2 and 8, and 3 or
-                               4 with groups of 32 or 128) on MLX's own layout; 1..2 rows per
-                               pass; the only family such plans run on */,
+                               4 with groups of 32) with f32 activations or f32 scales, on
+                               MLX's own layout; 1..2 rows per pass; the only family such
+                               plans run on */,
   QMM_VARIANT_WIDE = 7      /* matrix-core kernel for 65..128 rows per pass (the default above
                                64 rows where N/128 workgroups fill at least half the compute
                                units; 96-row blocks up to 96 rows, else 128): eight 16-row
@@ -108,10 +118,16 @@ typedef enum {
 #define QMM_FLAG_F32_OUT 1u
 
 /* Shape and format of one projection.  bits: 2, 3, 4 or 8 (5 and 6 are
- * UNSUPPORTED).  group_size: 32, 64 or 128.  3- and 4-bit group-64 weights
- * run on the matrix-core families in the native layout; every other format
- * runs on QMM_VARIANT_GENERIC in MLX's layout.  K: multiple of 128.  N:
- * multiple of 16.
+ * UNSUPPORTED).  group_size: 32, 64 or 128.  3- and 4-bit weights with groups
+ * of 64 or 128 run on every family in the native layout (a group of 128 as
+ * two halves of 64 with the same scale and bias); the other formats with
+ * bf16 activations and bf16 scales run on QMM_VARIANT_STREAM and
+ * QMM_VARIANT_RESIDENT in the step layout (codes placed as the matrix cores'
+ * operands of 32-column steps, so a group of 32, 64 or 128 is whole steps)
+ * where a built shape covers K (K <= 16384; 8-bit codes with groups of 32 or
+ * 64 up to K = 8192); with f32 activations or scales, or beyond those K, on
+ * QMM_VARIANT_GENERIC in MLX's layout.  K: multiple of 128.  N: multiple of
+ * 16.
  * max_rows: the largest row count qmm_run will be given (>= 1).
  * x_dtype: dtype of x and y.  sb_dtype: dtype of scales and biases.
  * flags: 0 or QMM_FLAG_F32_OUT (other bits: QMM_ERR_INVALID_ARG). */
@@ -148,7 +164,9 @@ void qmm_destroy(qmm_plan* plan);
 
 /* Bytes of the two buffers of the kernel-native weight layout written by
  * qmm_prepack: packed codes (exactly N*K*bits/8, the MLX byte count) and
- * packed scales+biases (exactly 2*N*(K/group_size) elements of sb_dtype). */
+ * packed scales+biases (2*N*(K/group_size) elements of sb_dtype; for 3- and
+ * 4-bit groups of 128, 2*N*(K/64): each group's pair is stored for both of
+ * its halves). */
 qmm_status qmm_packed_bytes(const qmm_plan* plan, size_t* codes_bytes, size_t* sb_bytes);
 
 /* One-time weight loader: MLX layout -> kernel-native layout.
@@ -156,11 +174,13 @@ qmm_status qmm_packed_bytes(const qmm_plan* plan, size_t* codes_bytes, size_t* s
  *   scales  sb_dtype [N, K/group_size]
  *   biases  sb_dtype [N, K/group_size]
  *   codes_out, sb_out: buffers of qmm_packed_bytes().
- * In the native layout (3- and 4-bit group 64) the 16 rows x 128 columns of
- * W that one wavefront multiplies are contiguous, and each lane's codes are
- * ordered so that the unpack to bf16 pairs is a shift and one and-or per
- * pair.  Other formats keep MLX's layout: the codes are copied as they are
- * and sb_out holds the scales, then the biases.  Enqueued on `stream`; the
+ * In the native layout (3- and 4-bit, groups of 64 or 128) and the step
+ * layout (the other formats, bf16 activations and scales) the 16 rows x 128
+ * columns of W that one wavefront multiplies are contiguous, and each lane's
+ * codes are ordered so that the unpack to bf16 pairs is a shift and one
+ * and-or per pair (8-bit codes: byte conversions).  Plans on MLX's layout
+ * (f32 activations or scales of the other formats) copy the codes as they
+ * are and store the scales, then the biases.  Enqueued on `stream`; the
  * inputs may be freed once it completes. */
 qmm_status qmm_prepack(const qmm_plan* plan, const uint32_t* w, const void* scales,
                        const void* biases, void* codes_out, void* sb_out, void* stream);
@@ -327,8 +347,9 @@ qmm_status qmm_run_noalloc(const qmm_plan* plan, const void* x, const void* code
 size_t qmm_workspace_bytes_ex(const qmm_plan* plan, int32_t variant, int32_t ntw,
                               int32_t kwaves, int32_t splitk, int32_t rows);
 
-/* Test hook: decode the native layout with the compute kernels' own unpack
- * and write the codes q(n,k) as uint8 [N, K] (device buffer). */
+/* Test hook: decode the native or step layout with the compute kernels' own
+ * unpack and write the codes q(n,k) as uint8 [N, K] (device buffer);
+ * QMM_ERR_UNSUPPORTED for plans that keep MLX's layout. */
 qmm_status qmm_debug_unpack(const qmm_plan* plan, const void* codes, uint8_t* codes_nk,
                             void* stream);
 
