@@ -492,10 +492,13 @@ qmm_status run_impl(const qmm_plan* p, int variant_req, int ntw_req, int wk_req,
     a.sb = sb;
     a.y = static_cast<char*>(y) + (size_t)r0 * p->d.N * ye;
     a.y_f32 = p->f32_out ? 1 : 0;
-    // given group sums: the matrix-core streaming kernel, and the resident
-    // kernel where its 16-byte reads of four rows stay aligned
+    // given group sums: the matrix-core streaming kernel (rows < rb only),
+    // and the resident kernel where its reads stay inside x_sums: it reads
+    // rows r0 .. r0+15 of every group, 16 bytes at a time, which sums_ld
+    // (a multiple of 16, at least rows rounded up to 16) covers when r0 is a
+    // multiple of 16
     const bool takes_sums = (vb == QMM_VARIANT_STREAM) ||
-                            (vb == QMM_VARIANT_RESIDENT && r0 % 4 == 0);
+                            (vb == QMM_VARIANT_RESIDENT && r0 % 16 == 0);
     a.xsums = xsums && takes_sums ? xsums + r0 : nullptr;
     a.xsums_ld = xsums_ld;
     a.tickets = static_cast<uint32_t*>(ws);

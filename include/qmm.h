@@ -236,8 +236,9 @@ int32_t qmm_sum_group(const qmm_plan* plan);
  * 16-byte aligned, sums_ld a multiple of 16 and >= rows rounded up to 16
  * (entries of rows >= `rows` are read and never affect y).  The streaming
  * and resident kernels use them in place of forming them (the resident
- * kernel where its shape has the registers for them); the other families,
- * and the vector-ALU forms, form their own.  Otherwise as qmm_run;
+ * kernel where its shape has the registers for them and for row blocks
+ * starting at a multiple of 16); the other families, and the vector-ALU
+ * forms, form their own.  Otherwise as qmm_run;
  * QMM_ERR_INVALID_ARG for a NULL x_sums or a sums_ld outside these rules. */
 qmm_status qmm_run_sums(const qmm_plan* plan, const void* x, const float* x_sums,
                         int32_t sums_ld, const void* codes, const void* sb, void* y,

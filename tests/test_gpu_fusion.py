@@ -54,7 +54,11 @@ def test_norm_group_sums(dtype, rows, D, gs):
 # of 32: no registers for given ones)
 CHAIN = [(3, 64, 5120, 1024, 1), (3, 64, 5120, 1024, 2), (3, 64, 5120, 1024, 9),
          (4, 64, 5120, 1024, 16), (4, 128, 3840, 512, 9), (2, 64, 1024, 512, 20),
-         (2, 32, 2048, 512, 1), (8, 32, 5120, 512, 12), (8, 128, 2048, 512, 2)]
+         (2, 32, 2048, 512, 1), (8, 32, 5120, 512, 12), (8, 128, 2048, 512, 2),
+         # 12 rows per resident launch at K = 6656: the second block (row 12)
+         # forms its own sums (the given ones are read 16 rows at a time from
+         # a block start that is a multiple of 16)
+         (2, 128, 6656, 512, 13)]
 
 
 @pytest.mark.parametrize("case", CHAIN, ids=lambda c: "b%d_g%d_K%d_N%d_M%d" % c)
