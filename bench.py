@@ -382,58 +382,81 @@ def time_attention(torch, binding, synth, H, KV, N, D, bits, gs, reps=5):
 
 
 def wave_timeline(torch, binding, synth):
-    """Per-wave phase times of the streaming kernel (1 row) and the resident
-    kernel (9 and 16 rows) on the 3-bit 5120 -> 10240 workload, cold (a ring
-    of weight copies), from the timing build: each wave stamps a 100 MHz
-    device-wide counter at its phase boundaries and writes the stamps at its
-    end.  Times in us from the earliest wave start of the last launch,
-    percentiles 0/10/50/90/100 over waves.  The timing build waits for each
-    chunk's weights explicitly before stamping them (the ordinary build
-    waits at the first use)."""
+    """Per-wave phase times of the streaming kernel (1 row), the resident
+    kernel (9 and 16 rows) and the split slab kernel (64 rows) on the 3-bit
+    5120 -> 10240 workload, cold (a ring of weight copies), from the timing
+    build: each wave stamps a 100 MHz device-wide counter at its phase
+    boundaries and writes the stamps at its end.  Times in us from the
+    earliest wave start of the last launch, percentiles 0/10/50/90/100 over
+    waves (the split slab kernel's: over its compute waves).  The timing
+    build waits for each chunk's weights explicitly before stamping them (the
+    ordinary build waits at the first use); the split slab kernel's stamps
+    add no waits."""
     import numpy as np
     names = {"stream": {0: "start", 1: "activation loads issued", 2: "weight loads issued",
                         3: "activations landed (in LDS with sums)", 12: "compute done",
                         13: "workgroup barrier", 14: "stores issued (storing wave)"},
              "resident": {0: "start", 1: "loads issued", 2: "activations landed",
                           12: "compute done", 13: "workgroup barrier",
-                          14: "stores issued (storing waves)"}}
+                          14: "stores issued (storing waves)"},
+             "slab": {0: "start", 1: "slice 0 landed (first barrier)", 10: "fold barrier",
+                      11: "partial tiles added in LDS", 12: "partials stored (coherent)",
+                      13: "ticket taken", 14: "y stored (second arrivals)"}}
     first_chunk = {"stream": 4, "resident": 3}
     (prob,) = synth.workload(2, M=64)
     out = {}
-    for fam, rows in (("stream", 1), ("resident", 9), ("resident", 16)):
+    for fam, rows in (("stream", 1), ("resident", 9), ("resident", 16), ("slab", 64)):
         lin = binding.QuantizedLinear(prob, max_rows=64)
         ring = max(2, -(-RING_BYTES // weight_bytes()))
         copies = [(lin.codes, lin.sb)] + [(lin.codes.clone(), lin.sb.clone())
                                           for _ in range(ring - 1)]
         x = binding.to_device(prob.x[:rows])
         y = torch.empty(rows, N, dtype=torch.bfloat16, device="cuda")
-        ws = torch.zeros(4 << 20, dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(8 << 20, dtype=torch.uint8, device="cuda")
         for _ in range(2):
             for c, sbv in copies:
                 lin.plan.run(x, c, sbv, out=y, variant=fam, workspace=ws)
         torch.cuda.synchronize()
         st = lin.plan.stats()
-        nw, cpw = 8, 5
-        grid = st["last_grid"] if fam == "resident" else N // 16
-        tick = ((N // 16) * 4 + 255) // 256 * 256
-        raw = ws.cpu().numpy()[tick:].view(np.uint64)[: grid * nw * 16]
+        if fam == "slab":
+            # 12 compute waves and 4 loader waves; 5 slices of 512 k; the
+            # stamps follow the kernel's own tickets and partial tiles
+            assert st["last_splitk"] == 2, "64 rows run on the split slab kernel"
+            nw, nsl, skip = 16, 5, lin.plan.workspace_bytes(rows)
+        else:
+            nw, cpw = 8, 5
+            skip = ((N // 16) * 4 + 255) // 256 * 256
+        grid = st["last_grid"] if fam != "stream" else N // 16
+        raw = ws.cpu().numpy()[skip:].view(np.uint64)[: grid * nw * 16]
         s16 = raw.reshape(grid, nw, 16).astype(np.int64)
         t0 = s16[:, :, 0].min()
         rel = (s16 - t0) * 0.01                      # 100 MHz ticks -> us
         rec = {"family": fam, "rows": rows, "workgroups": grid, "waves": grid * nw}
         stamps = dict(names[fam])
-        for j in range(cpw):
-            stamps[first_chunk[fam] + j] = "chunk %d weights landed" % j
+        if fam == "slab":
+            for j in range(nsl):
+                stamps[2 + j] = "slice %d done (barrier)" % j
+            comp = rel[:, :12, :]
+            cs16 = s16[:, :12, :]
+        else:
+            for j in range(cpw):
+                stamps[first_chunk[fam] + j] = "chunk %d weights landed" % j
+            comp, cs16 = rel, s16
         for k in sorted(stamps):
-            v = rel[:, :, k][s16[:, :, k] > 0]
+            v = comp[:, :, k][cs16[:, :, k] > 0]
             rec[stamps[k]] = [round(float(np.percentile(v, q)), 2) for q in (0, 10, 50, 90, 100)]
         rec["workgroup start"] = [round(float(np.percentile(rel[:, :, 0].min(axis=1), q)), 2)
                                   for q in (0, 10, 50, 90, 100)]
-        land = 3 if fam == "stream" else 2
-        rec["activations landed, median by wave index"] = [
-            round(float(np.median(rel[:, w, land])), 2) for w in range(nw)]
-        rec["compute done, median by wave index"] = [
-            round(float(np.median(rel[:, w, 12])), 2) for w in range(nw)]
+        if fam == "slab":
+            rec["slice time, median over workgroups (us)"] = [
+                round(float(np.median(rel[:, 0, 2 + j] - rel[:, 0, 1 + j])), 3)
+                for j in range(nsl)]
+        else:
+            land = 3 if fam == "stream" else 2
+            rec["activations landed, median by wave index"] = [
+                round(float(np.median(rel[:, w, land])), 2) for w in range(nw)]
+            rec["compute done, median by wave index"] = [
+                round(float(np.median(rel[:, w, 12])), 2) for w in range(nw)]
         out["%s %d row(s)" % (fam, rows)] = rec
         del copies, lin
         torch.cuda.synchronize()

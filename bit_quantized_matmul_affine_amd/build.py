@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libqmm.so")
 # compiled with per-wave timestamps (QMM_WAVE_STAMPS); loaded only by
 # `bench.py --wave-timeline`.
 STAMPS_LIB = os.path.join(PKG, "libqmm_stamps.so")
-STAMPED = ("qmm_stream.hip", "qmm_resident.hip")
+STAMPED = ("qmm_stream.hip", "qmm_resident.hip", "qmm_slab.hip")
 SOURCES = ["qmm_layout.hip", "qmm_mfma.hip", "qmm_stream.hip", "qmm_resident.hip",
            "qmm_slab.hip", "qmm_wide.hip", "qmm_norm.hip", "qmm_attention.hip",
            "qmm_generic.hip", "qmm_fmt.hip", "qmm_noalloc.hip", "qmm_api.cpp"]

@@ -291,14 +291,15 @@ __device__ __forceinline__ ChunkRange wave_chunks(int c0, int c1, int wk, int WK
 // ordinary builds every call below is empty).  mark(k) reads s_memrealtime,
 // a 100 MHz counter common to the whole device, into a register; flush()
 // writes the 16 stamps of the wave once, at its end, from lane 0 to
-// a.part[16 * wave_index ...] (the caller passes a workspace large enough;
-// no store happens while the kernel runs, so the stamps do not delay it).
+// 64-bit word skip + 16 * wave_index of a.part (skip: the words a kernel keeps
+// for its own use there; the caller passes a workspace large enough; no store
+// happens while the kernel runs, so the stamps do not delay it).
 struct WaveStamps {
 #ifdef QMM_WAVE_STAMPS
   uint64_t t[16];
   uint64_t* dst;
-  __device__ __forceinline__ WaveStamps(const LaunchArgs& a, long wave_index) {
-    dst = a.part ? reinterpret_cast<uint64_t*>(a.part) + wave_index * 16 : nullptr;
+  __device__ __forceinline__ WaveStamps(const LaunchArgs& a, long wave_index, long skip = 0) {
+    dst = a.part ? reinterpret_cast<uint64_t*>(a.part) + skip + wave_index * 16 : nullptr;
 #pragma unroll
     for (int k = 0; k < 16; ++k) t[k] = 0;
   }
@@ -314,7 +315,7 @@ struct WaveStamps {
     }
   }
 #else
-  __device__ __forceinline__ WaveStamps(const LaunchArgs&, long) {}
+  __device__ __forceinline__ WaveStamps(const LaunchArgs&, long, long = 0) {}
   __device__ __forceinline__ void mark(int) {}
   __device__ __forceinline__ void flush(int) {}
 #endif

@@ -227,6 +227,9 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
   const int kp = __builtin_amdgcn_readfirstlane(wave - slot_i * KP);
   const int r = lane & 15, kg = lane >> 4;
   f32x4* red = reinterpret_cast<f32x4*>(lds);  // fold area [TG][MT][KP][64], after the loop
+  // timing build only: stamps after the partial tiles' words
+  WaveStamps ts(a, (long)blockIdx.x * (NWC + NWL) + wave, (long)gridDim.x * TG * MT * 128);
+  ts.mark(0);
 
   if (wave >= NWC) {
     // ---- loader waves
@@ -249,6 +252,7 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
     for (int s = 0; s < NB; ++s) issue(s);
     wait_vm<(NB - 1) * RPL>();
     wg_barrier();
+    ts.mark(1);
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       // after barrier j every compute wave is done with slice j-1
@@ -258,6 +262,7 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
         wait_slices<RPL, RB - 2>(last - (j + 1));
       }
       wg_barrier();
+      ts.mark(2 + j);
     }
   } else {
     // ---- compute waves
@@ -290,6 +295,7 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[i][mt] = zero;
     wg_barrier();
+    ts.mark(1);
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       const bool live = (sl0 + j) * KP + kp < nC;
@@ -339,6 +345,7 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
       }
       wait_lds();
       wg_barrier();
+      ts.mark(2 + j);
     }
     // the slots are dead: park the partial tiles for the fold
 #pragma unroll
@@ -348,6 +355,7 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
         red[(((slot_i * TW + i) * MT + mt) * KP + kp) * 64 + lane] = acc[i][mt];
   }
   __syncthreads();
+  ts.mark(10);
   // wave (slot, kp) folds row tile mt = kp of its TW tiles in K order
   const bool folds = wave < NWC && kp < MT;
   const int mt = kp;
@@ -361,6 +369,7 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
       for (int k = 1; k < KP; ++k) v[i] += red[(base + k) * 64 + lane];
     }
   }
+  ts.mark(11);
   auto store_tiles = [&]() {
 #pragma unroll
     for (int i = 0; i < TW; ++i) {
@@ -376,6 +385,7 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
   };
   if (S == 1) {
     if (folds) store_tiles();
+    ts.flush(lane);
     return;
   }
   // S == 2: partial tile (grp, kpart, slot, i, mt) at part[(((grp*S + kpart)*TG + slot*TW + i)*MT
@@ -391,12 +401,17 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
         __hip_atomic_store(part_at(kpart, i, q), v[i][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_vm<0>();  // the partials have reached the point of coherence
   }
+  ts.mark(12);
   __syncthreads();
   if (threadIdx.x == 0)
     s_last = __hip_atomic_fetch_add(&a.tickets[grp], 1u, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(S - 1);
   __syncthreads();
-  if (!s_last) return;
+  ts.mark(13);
+  if (!s_last) {
+    ts.flush(lane);
+    return;
+  }
   if (folds) {
 #pragma unroll
     for (int i = 0; i < TW; ++i)
@@ -406,6 +421,8 @@ __global__ void __launch_bounds__((NSLOT * 4 + 4) * 64) split_slab_kernel(Launch
                                      __HIP_MEMORY_SCOPE_AGENT);
     store_tiles();
   }
+  ts.mark(14);
+  ts.flush(lane);
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.tickets[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
