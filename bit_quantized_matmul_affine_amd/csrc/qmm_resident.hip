@@ -18,12 +18,15 @@ namespace qmm {
 // so each activation fragment it reads, and each group sum it forms, serves
 // TM tiles.  Order of work in a wave:
 //   1. LDS-direct loads (no registers) of the activation slices of its
-//      chunks, then the loads of ALL its weights (CPW chunks x TM tiles), so
-//      a compute unit's whole share of W is in flight at once;
+//      chunks, then the weight loads of its first two chunks (TM tiles each);
 //   2. a wait for its own activation slices only (loads retire in issue
 //      order, so the weights stay in flight); no barrier;
 //   3. per chunk, in arrival order: the A fragments and the group sums
-//      (all-ones MFMA), then per tile: unpack, MFMA, per-group scale;
+//      (all-ones MFMA), then per tile: unpack, MFMA, per-group scale; then
+//      the weight loads of the chunk two ahead go out into the registers
+//      this chunk's words and scales leave (a two-chunk ring: with every
+//      chunk's loads issued up front, a compute unit's queue of weight
+//      requests held back its later waves' activation loads);
 //   4. the NW partial tiles of each tile are added through LDS (reusing the
 //      activation space) in wave order.
 // LDS holds chunk c's slice at c*M*256 bytes, row m's 16-byte vector e at
@@ -45,15 +48,19 @@ __device__ __forceinline__ float silu_mul(float gate, float up) {
   return silu * u;  // rounded to bf16 by the store
 }
 
-// Timing build: the wait for chunk j's weights (LPC loads per later chunk
-// outstanding); j is a constant once the caller's loop is unrolled.
-template <int CPW, int LPC, int J = 0>
+// Weight loads in flight per wave: chunks of the register ring.
+constexpr int kResidentRing = 2;
+
+// Timing build: the wait for chunk j's weights (LPC loads outstanding per
+// chunk issued after it: the ring holds chunks j .. j+RD-1); j is a
+// constant once the caller's loop is unrolled.
+template <int CPW, int LPC, int RD, int J = 0>
 __device__ __forceinline__ void stamp_chunk(int j) {
   if constexpr (J < CPW) {
     if (j == J)
-      stamp_wait<(CPW - 1 - J) * LPC>();
+      stamp_wait<((J + RD < CPW ? J + RD : CPW) - 1 - J) * LPC>();
     else
-      stamp_chunk<CPW, LPC, J + 1>(j);
+      stamp_chunk<CPW, LPC, RD, J + 1>(j);
   }
 }
 
@@ -104,7 +111,7 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 1b. every weight load, chunk-major
+  // 1b. the weight loads of the ring's first chunks, chunk-major
   int tl[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) {
@@ -112,35 +119,41 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
     tl[t] = tile < nT ? tile : g;
   }
   const ST* __restrict__ sbp2 = reinterpret_cast<const ST*>(a.sb2);
-  uint32_t W[CPW][TM][BITS];
-  typename F::Sb SBv[CPW][TM];
-  f32x4 exv[XS ? CPW : 1][GC];
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
+  constexpr int RD = CPW < kResidentRing ? CPW : kResidentRing;
+  // chunk j's words, scales and given sums in ring slot j % RD
+  uint32_t W[RD][TM][BITS];
+  typename F::Sb SBv[RD][TM];
+  f32x4 exv[XS ? RD : 1][GC];
+  auto issue = [&](int j) {  // j is a constant once the callers are unrolled
+    const int d = j % RD;
     const int c = min(w + j * NW, clast);
     if constexpr (XS) {
 #pragma unroll
       for (int g = 0; g < GC; ++g)
-        exv[j][g] = *reinterpret_cast<const f32x4*>(a.xsums + (long)(GC * c + g) * a.xsums_ld +
+        exv[d][g] = *reinterpret_cast<const f32x4*>(a.xsums + (long)(GC * c + g) * a.xsums_ld +
                                                     4 * kg);
     }
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       const bool second = GU && t >= TMH;  // compile-time once unrolled
       const long blk = (long)tl[t] * nC + c;
-      F::load(second ? a.codes2 : a.codes, blk, lane, W[j][t]);
-      SBv[j][t].load((second ? sbp2 : sbp) + (blk * kTileN + r) * F::kSbElems);
+      F::load(second ? a.codes2 : a.codes, blk, lane, W[d][t]);
+      SBv[d][t].load((second ? sbp2 : sbp) + (blk * kTileN + r) * F::kSbElems);
     }
+  };
+#pragma unroll
+  for (int j = 0; j < RD; ++j) {
+    issue(j);
     __builtin_amdgcn_sched_barrier(0);  // chunk j's loads issue before chunk j+1's
   }
   ts.mark(1);
 
   // 2. this wave's activation slices have landed once at most its weight
-  //    loads (LPT per chunk and tile, counted low) are outstanding.  The
+  //    loads (LPC per chunk in the ring, counted low) are outstanding.  The
   //    wait also drains the LDS counter: until it does, the compiler counts
   //    the LDS-direct loads as pending on both counters and may turn later
   //    weight waits into full ones (vmcnt(0)).
-  wait_vm_lds<(CPW * LPC < 63 ? CPW * LPC : 63)>();
+  wait_vm_lds<(RD * LPC < 63 ? RD * LPC : 63)>();
   ts.mark(2);
 
   // 3. compute in load order; rows past the last one read the last row
@@ -157,7 +170,8 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
   for (int j = 0; j < CPW; ++j) {
     const bool live = j < count;
     const int c = min(w + j * NW, clast);
-    stamp_chunk<CPW, LPC>(j);      // timing build: wait for chunk j's weights,
+    const int d = j % RD;
+    stamp_chunk<CPW, LPC, RD>(j);  // timing build: wait for chunk j's weights,
     ts.mark(3 + j);                // then stamp their arrival
     const u32x4* xrow = reinterpret_cast<const u32x4*>(lds + (size_t)c * M * 256) + xm * 16;
     u32x4 A[4];
@@ -168,7 +182,7 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
 #pragma unroll
     for (int g = 0; g < GC; ++g) {
       if constexpr (XS) {
-        ex[g] = exv[j][g];
+        ex[g] = exv[d][g];
       } else {
         f32x4 e = zero;
 #pragma unroll
@@ -181,7 +195,7 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
 #pragma unroll
     for (int t = 0; t < TM; ++t) {
       uint32_t P[16];
-      F::unpack(W[j][t], P, mask_v);
+      F::unpack(W[d][t], P, mask_v);
 #pragma unroll
       for (int g = 0; g < GC; ++g) {
         f32x4 dd = zero;
@@ -192,12 +206,13 @@ __global__ void __launch_bounds__(NW * 64) resident_kernel(LaunchArgs a) {
           dd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[st]),
                                                        __builtin_bit_cast(bf16x8, B), dd, 0, 0, 0);
         }
-        const Affine af = F::affine(g, SBv[j][t]);
+        const Affine af = F::affine(g, SBv[d][t]);
         const float sc = live ? af.sc : 0.f, bp = live ? af.bp : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[t][q] = fmaf(sc, dd[q], fmaf(bp, ex[g][q], acc[t][q]));
       }
     }
+    if (j + RD < CPW) issue(j + RD);  // into the slot chunk j leaves
     __builtin_amdgcn_sched_barrier(0);
   }
 
