@@ -76,6 +76,10 @@ struct NativeFmt {
   static constexpr bool resident_fits(int, int, int) { return true; }
 };
 
+// Chunks of weight loads a wave of the resident kernel keeps in flight (its
+// ring of weight registers).
+constexpr int kResidentRing = 2;
+
 typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -208,12 +212,15 @@ struct StepFmt {
     return Affine{s, sb.b(g) - kOffset * s};
   }
   // Shapes whose weight registers (codes and scale/bias words of every
-  // chunk and tile slot a wave holds) leave room for the rest without
-  // spilling: 128 words with up to 8 waves (two per SIMD); with 16 waves
-  // (128 registers each) 72, and 56 for the streaming kernel, whose waves
-  // also hold their activation slices in registers.
+  // chunk and tile slot a wave holds at once: the resident kernel's ring
+  // holds kResidentRing chunks, the streaming kernel all of its chunks)
+  // leave room for the rest without spilling: 128 words with up to 8 waves
+  // (two per SIMD); with 16 waves (128 registers each) 72, and 56 for the
+  // streaming kernel, whose waves also hold their activation slices in
+  // registers.
   static constexpr bool resident_fits(int nw, int cpw, int tm) {
-    return cpw * tm * (BITS + kGroups) <= (nw >= 16 ? 72 : 128);
+    return (cpw < kResidentRing ? cpw : kResidentRing) * tm * (BITS + kGroups) <=
+           (nw >= 16 ? 72 : 128);
   }
   static constexpr bool stream_fits(int nw, int cpw) {
     return cpw * (BITS + kGroups) <= (nw >= 16 ? 56 : 128);

@@ -48,9 +48,6 @@ __device__ __forceinline__ float silu_mul(float gate, float up) {
   return silu * u;  // rounded to bf16 by the store
 }
 
-// Weight loads in flight per wave: chunks of the register ring.
-constexpr int kResidentRing = 2;
-
 // Timing build: the wait for chunk j's weights (LPC loads outstanding per
 // chunk issued after it: the ring holds chunks j .. j+RD-1); j is a
 // constant once the caller's loop is unrolled.
@@ -293,10 +290,12 @@ size_t resident_lds_bytes(int nw, int tm, int M, int K) {
 }
 
 // Shapes built with given group sums: eight waves or fewer, and at most 48
-// registers of sums (4 * GC per chunk); other shapes form their own sums.
+// registers of sums (4 * GC per chunk of the ring); other shapes form their
+// own sums.
 template <typename F, bool XS>
 constexpr bool resident_built(int nw, int cpw, int tm) {
-  return F::resident_fits(nw, cpw, tm) && (!XS || (nw <= 8 && cpw * F::kGroups * 4 <= 48));
+  return F::resident_fits(nw, cpw, tm) &&
+         (!XS || (nw <= 8 && (cpw < kResidentRing ? cpw : kResidentRing) * F::kGroups * 4 <= 48));
 }
 
 template <typename F>
