@@ -383,6 +383,29 @@ def test_workload4_sampled(variant):
     assert np.all(np.isfinite(yf))
 
 
+def test_workload4_families_agree_everywhere():
+    """All 128 x 28672 outputs of the 4-bit 8192 -> 28672 block, from three
+    kernel families: the wide kernel (bf16-rounded weights, no per-group
+    epilogue) and the split slab and MFMA kernels (the factored form).  Each
+    is within the acceptance bound of the exact result where the oracle
+    samples it, so at every output any two must agree within twice that
+    bound; a missing, stale or misplaced tile in one of them shows as a gap
+    of the outputs' own size.  Most outputs agree to a small fraction of it."""
+    (p,) = synth.workload(4)
+    say("workload 4, every output, three families")
+    r = Runner(p)
+    ys = {v: y_to_f64(r.run(variant=v), p.x_dtype) for v in ("wide", "slab", "mfma")}
+    sx, mw = oracle.bound_terms(p.bits, p.K, p.x, p.w, p.scales, p.biases)
+    tol = oracle.tolerance_coefficient(p.x_dtype) * np.outer(sx, mw) + 1e-6
+    for v, y in ys.items():
+        assert y.shape == (p.M, p.N) and np.all(np.isfinite(y)), v
+    for a, c in (("wide", "mfma"), ("slab", "mfma")):
+        ratio = np.abs(ys[a] - ys[c]) / tol
+        worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+        assert ratio.max() <= 2.0, "%s vs %s: ratio %.3f at %s" % (a, c, ratio.max(), worst)
+        assert np.median(ratio) < 0.01, "%s vs %s: median ratio %.4f" % (a, c, np.median(ratio))
+
+
 @pytest.mark.parametrize("bits", [3, 4])
 def test_degenerate_weights_every_family(bits):
     """Zero scales and biases give exact zeros; a zero activation block gives
