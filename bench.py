@@ -463,6 +463,31 @@ def wave_timeline(torch, binding, synth):
     return out
 
 
+def timeline_summary(path: str) -> str:
+    """Markdown tables of a --wave-timeline JSON (no GPU needed): per family
+    and row count, p0 / p10 / p50 / p90 / p100 of every phase, then the
+    per-wave-index medians."""
+    with open(path) as f:
+        d = json.load(f)
+    out = []
+    for name, r in d.items():
+        out.append("## %s: %d workgroups, %d waves\n" % (name, r["workgroups"], r["waves"]))
+        out.append("| phase | p0 | p10 | p50 | p90 | p100 |")
+        out.append("|---|---|---|---|---|---|")
+        extra = []
+        for k, v in r.items():
+            if not isinstance(v, list):
+                continue
+            if "median" in k:
+                extra.append("%s: %s" % (k[0].upper() + k[1:], ", ".join("%.2f" % x for x in v)))
+                continue
+            out.append("| %s | %s |" % (k, " | ".join("%.2f" % x for x in v)))
+        out.append("")
+        for e in extra:
+            out.append(e + "\n")
+    return "\n".join(out)
+
+
 def other_workloads(torch, binding, synth, probe):
     """The remaining configurations, each cold-read as above."""
     out = {}
@@ -545,8 +570,11 @@ def main() -> int:
                     help="row counts of a step (default 1,9,16,32,64, the measured workload; a "
                          "single row count serves per-row-count kernel traces)")
     ap.add_argument("--wave-timeline", action="store_true",
-                    help="print per-wave phase times of the streaming and resident kernels from "
-                         "the timing build (libqmm_stamps.so) and exit")
+                    help="print per-wave phase times of the streaming, resident and split slab "
+                         "kernels from the timing build (libqmm_stamps.so) and exit")
+    ap.add_argument("--timeline-summary", metavar="JSON",
+                    help="print the phase tables of a --wave-timeline JSON and exit (no GPU "
+                         "needed)")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-dispatch duration statistics (median, p10, p90) of a "
                          "rocprofv3 --kernel-trace CSV and exit (no GPU needed)")
@@ -557,6 +585,9 @@ def main() -> int:
                     help="only run the HBM read probe on a 1 GiB buffer five times (a kernel of "
                          "known traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
+    if args.timeline_summary:
+        print(timeline_summary(args.timeline_summary))
+        return 0
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
         return 0
