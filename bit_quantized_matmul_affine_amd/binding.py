@@ -249,6 +249,9 @@ class Plan:
                               dtype=torch.float32 if self.f32_out else x.dtype, device=x.device)
         if x_sums.dtype != torch.float32 or x_sums.dim() != 2 or not x_sums.is_contiguous():
             raise ValueError("x_sums must be a contiguous f32 [groups, ld] tensor")
+        if x_sums.shape[0] < self.K // self.sum_group():
+            raise ValueError("x_sums holds %d groups; K / sum_group() = %d"
+                             % (x_sums.shape[0], self.K // self.sum_group()))
         if workspace is None:
             workspace = self.workspace(self.workspace_bytes(rows), x.device, stream)
         wsb = workspace.numel() if workspace is not None else 0
@@ -323,6 +326,9 @@ def residual_rms_norm(x, update, weight, eps: float, residual=None, normalized=N
         if (group_sums.dtype != torch.float32 or group_sums.dim() != 2 or
                 not group_sums.is_contiguous()):
             raise ValueError("group_sums must be a contiguous f32 [groups, ld] tensor")
+        if group_size > 0 and group_sums.shape[0] < D // group_size:
+            raise ValueError("group_sums holds %d groups; D / group_size = %d"
+                             % (group_sums.shape[0], D // group_size))
         _check(lib().qmm_residual_rms_norm_ex(_ptr(x), _ptr(update), _ptr(weight), _ptr(residual),
                                               _ptr(normalized), _ptr(group_sums), group_size,
                                               group_sums.shape[1], rows, D, float(eps), dt,

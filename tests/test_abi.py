@@ -193,3 +193,17 @@ def test_group_sum_entry_points_validate_without_gpu():
     assert norm(fake, 48, 16, 512) == b.QMM_ERR_INVALID_ARG   # not an MLX group size
     assert norm(fake, 64, 16, 96) == b.QMM_ERR_INVALID_ARG    # D not a multiple of 64
     assert norm(fake, 64, 2, 512) == b.QMM_ERR_INVALID_ARG    # sums_ld below rows
+
+
+def test_group_sum_shapes_checked_by_the_binding():
+    """The binding rejects sums buffers with fewer groups than the
+    projection's K (or the norm's D) needs, before any library call."""
+    import torch
+    p = b.Plan(3, 1024, 64, 4, "bf16")
+    x = torch.zeros(4, 1024, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="groups"):
+        p.run_sums(x, torch.zeros(1024 // 64 - 1, 16), None, None)
+    w = torch.zeros(1024, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="groups"):
+        b.residual_rms_norm(x, x, w, 1e-5, group_sums=torch.zeros(1024 // 32 - 1, 16),
+                            group_size=32)
