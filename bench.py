@@ -463,6 +463,40 @@ def wave_timeline(torch, binding, synth):
     return out
 
 
+def counter_summary(paths) -> str:
+    """Markdown table of rocprofv3 --pmc CSVs (no GPU needed): per kernel, the
+    mean over its dispatches of each counter (the rows of one dispatch, one
+    per hardware block instance, added) and of the dispatch duration."""
+    import csv
+    from collections import defaultdict
+    per = defaultdict(lambda: defaultdict(float))  # (kernel, dispatch) -> counter -> value
+    dur = {}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("qmm::", "")
+                key = (name, path, r["Dispatch_Id"])
+                per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+                dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    kernels = defaultdict(list)
+    for key in per:
+        kernels[key[0]].append(key)
+    counters = sorted({c for v in per.values() for c in v})
+    lines = ["| kernel | dispatches | mean us | " + " | ".join(counters) + " |",
+             "|---|---|---|" + "---|" * len(counters)]
+    for name, keys in sorted(kernels.items()):
+        if name.startswith("at::") or name.startswith("__amd"):
+            continue
+        cells = []
+        for c in counters:
+            vals = [per[k][c] for k in keys if c in per[k]]
+            cells.append("%.4g" % (sum(vals) / len(vals)) if vals else "")
+        lines.append("| `%s` | %d | %.2f | %s |" % (name, len(keys),
+                                                   sum(dur[k] for k in keys) / len(keys),
+                                                   " | ".join(cells)))
+    return "\n".join(lines)
+
+
 def timeline_summary(path: str) -> str:
     """Markdown tables of a --wave-timeline JSON (no GPU needed): per family
     and row count, p0 / p10 / p50 / p90 / p100 of every phase, then the
@@ -486,6 +520,16 @@ def timeline_summary(path: str) -> str:
         for e in extra:
             out.append(e + "\n")
     return "\n".join(out)
+
+
+def crossover(torch, binding, synth, reps=3):
+    """The 4-bit 8192 -> 28672 block of 128 rows (the compute/bandwidth
+    crossover), cold as in time_workload."""
+    (p4,) = synth.workload(4)
+    us, v = time_workload(torch, binding, p4, p4.M, reps=reps)
+    tf = 2.0 * p4.M * p4.N * p4.K / (us * 1e-6) / 1e12
+    return {"us": round(us, 3), "weight_GBps": round(p4.weight_bytes / (us * 1e-6) / 1e9, 1),
+            "tflops": round(tf, 2), "frac_of_bf16_mfma_peak": round(tf / 2500.0, 4), "variant": v}
 
 
 def other_workloads(torch, binding, synth, probe):
@@ -518,12 +562,7 @@ def other_workloads(torch, binding, synth, probe):
                           "what": "silu(x.Wg^T)*(x.Wu^T) in one kernel (qmm_run_gate_up)"},
         "trio_fused_us": round(fused_us, 3), "weight_GBps_fused": round(fgb, 1),
         "frac_of_measured_peak_fused": round(fgb / probe, 4) if probe else None}
-    (p4,) = synth.workload(4)
-    us, v = time_workload(torch, binding, p4, p4.M, reps=3)
-    tf = 2.0 * p4.M * p4.N * p4.K / (us * 1e-6) / 1e12
-    out["4-bit 8192->28672, 128 rows, bf16"] = {
-        "us": round(us, 3), "weight_GBps": round(p4.weight_bytes / (us * 1e-6) / 1e9, 1),
-        "tflops": round(tf, 2), "frac_of_bf16_mfma_peak": round(tf / 2500.0, 4), "variant": v}
+    out["4-bit 8192->28672, 128 rows, bf16"] = crossover(torch, binding, synth)
     fmt = {}
     for bits, gs in ((2, 64), (2, 32), (8, 64), (8, 128), (3, 32), (4, 32), (4, 128), (3, 128)):
         pf = synth.small(900 + bits + gs, bits=bits, K=5120, N=10240, M=16, group_size=gs)
@@ -572,6 +611,9 @@ def main() -> int:
     ap.add_argument("--wave-timeline", action="store_true",
                     help="print per-wave phase times of the streaming, resident and split slab "
                          "kernels from the timing build (libqmm_stamps.so) and exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="print per-kernel means of rocprofv3 --pmc counter CSVs and exit (no "
+                         "GPU needed)")
     ap.add_argument("--timeline-summary", metavar="JSON",
                     help="print the phase tables of a --wave-timeline JSON and exit (no GPU "
                          "needed)")
@@ -581,10 +623,16 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs="+", metavar="CSV",
                     help="PROBE_FETCH_CSV ROWS:FETCH_CSV:WRITE_CSV ...: HBM bytes per dispatch "
                          "from rocprofv3 --pmc runs; writes profiles/hbm_traffic.json (no GPU)")
+    ap.add_argument("--crossover-only", action="store_true",
+                    help="only time the 4-bit 8192 -> 28672 block of 128 rows (cold weights) and "
+                         "print its figures")
     ap.add_argument("--probe-only", action="store_true",
                     help="only run the HBM read probe on a 1 GiB buffer five times (a kernel of "
                          "known traffic, used to scale hardware byte counters)")
     args = ap.parse_args()
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
+        return 0
     if args.timeline_summary:
         print(timeline_summary(args.timeline_summary))
         return 0
@@ -617,6 +665,9 @@ def main() -> int:
     if args.wave_timeline:
         binding.LIB_PATH = qbuild.STAMPS_LIB
         print(json.dumps(wave_timeline(torch, binding, synth)), flush=True)
+        return 0
+    if args.crossover_only:
+        print(json.dumps(crossover(torch, binding, synth, reps=1)), flush=True)
         return 0
     if args.probe_only:
         gbps = measure_hbm(torch, binding, gib=1)
