@@ -207,3 +207,34 @@ def test_variant_rules():
         r.lin.plan.run_gate_up(x, r.lin.codes, r.lin.sb, r.lin.codes, r.lin.sb)
     assert ei.value.status == b.QMM_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+def _random_step_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        bits, gs = STEP_FORMATS[int(rng.integers(0, len(STEP_FORMATS)))]
+        out.append((bits, gs, 128 * int(rng.integers(1, 41)), 16 * int(rng.integers(1, 31)),
+                    int(rng.integers(1, 21))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_step_cases(20261204, 16),
+                         ids=lambda c: "b%d_g%d_K%d_N%d_M%d" % c)
+def test_random_step_layout_shapes(case):
+    """Seeded random shapes of the step-layout formats (K a multiple of 128 up
+    to 5120, N a multiple of 16 up to 480, 1..20 rows): the library's choice,
+    and the streaming and resident kernels forced where they take the shape."""
+    bits, gs, K, N, M = case
+    p = synth.small(7000 + K + N + M + bits, bits=bits, K=K, N=N, M=M, group_size=gs)
+    r = Runner(p)
+    say("random step shape", case)
+    check_against_oracle(p, r.run(), label="random %s auto" % (case,))
+    for v in ("stream", "resident"):
+        try:
+            y = r.run(rows=min(M, 4), variant=v)
+        except b.QmmError as e:
+            assert e.status == b.QMM_ERR_UNSUPPORTED, (case, v, e.status)
+            continue
+        check_against_oracle(p, y, rows=min(M, 4), label="random %s %s" % (case, v))
+

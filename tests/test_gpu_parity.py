@@ -109,6 +109,32 @@ def test_small_parity(case):
             check_against_oracle(p, y, label=label)
 
 
+def _random_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.choice([3, 4])), 128 * int(rng.integers(1, 49)), 16 * int(rng.integers(1, 41)),
+             int(rng.integers(1, 21))) for _ in range(n)]
+
+
+RANDOM = _random_cases(20261203, 24)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=lambda c: "b%d_K%d_N%d_M%d" % c)
+def test_random_shapes_every_family(case):
+    """Seeded random shapes (K a multiple of 128 up to 6144, N a multiple of
+    16 up to 640, 1..20 rows) on every family that takes them, default
+    launch shapes: indexing that depends on the shape (chunks per wave, tile
+    slots, ragged waves and tile groups) is checked away from the fixed
+    cases."""
+    bits, K, N, M = case
+    p = synth.small(5000 + K + N + M, bits=bits, K=K, N=N, M=M)
+    r = Runner(p)
+    fams = ["auto", "mfma", "gemv"] + (["stream"] if stream_ok(K, M, N) else []) + (
+        ["resident"] if resident_ok(K, M) else [])
+    for v in fams:
+        say("random shape", case, v)
+        check_against_oracle(p, r.run(variant=v), label="random %s %s" % (case, v))
+
+
 # ------------------------------------------------------------------ properties
 
 def test_determinism_and_row_independence():
