@@ -21,11 +21,13 @@
 //     reading one row's words as one contiguous run); lane j owns values
 //     j*D/16 .. (j+1)*D/16 - 1 of a row for the score and of the output;
 //   * scores in the page's factored form s * sum_d c_d q_d + b * sum_d q_d
-//     with exact products: each code becomes its exact bf16 value (one
-//     v_cvt_f32_ubyteN on the word's byte or nibble planes, then two codes
-//     per v_cvt_pk_bf16_f32; every code below 256 is exact in bf16), pairs of
-//     codes meet pairs of query values in v_dot2_f32_bf16 (8-bit by 8-bit
-//     significands: exact products), each lane applies its group's scale and
+//     with exact products: each code becomes its exact bf16 value (4-bit:
+//     the word's two nibble planes read as e4m3 bytes and converted two at a
+//     time with a scale of 2^9; 8-bit: one v_cvt_f32_ubyteN per byte, then
+//     two codes per v_cvt_pk_bf16_f32; every code below 256 is exact in
+//     bf16), pairs of codes meet the matching pairs of query values in
+//     v_dot2_f32_bf16 (8-bit by 8-bit significands: exact products), each
+//     lane applies its group's scale and
 //     bias, the 16 lanes add their parts with DPP row operations, and the
 //     score is rounded to bf16;
 //   * two passes over the block's rows held in registers: the scores first
@@ -65,6 +67,7 @@ __device__ __forceinline__ float round_bf16(float v) {
 }
 
 typedef short bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -109,31 +112,62 @@ __device__ __forceinline__ uint32_t sgpr_const(uint32_t v) {
   return r;
 }
 
-// The lane's codes as floats, in value order: bytes of a word (8-bit), or of
-// its low and high nibble planes (4-bit), each converted by one
-// v_cvt_f32_ubyteN (the planes pass through an opaque move, so the compiler
-// keeps the byte form instead of refolding every code into a bit-field
-// extract and a conversion).
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
+// The lane's 8-bit codes as floats, in value order: one v_cvt_f32_ubyteN
+// per byte of a word.
+template <int WPL>
+__device__ __forceinline__ void code_floats8(const uint32_t* w, float* c) {
+#pragma unroll
+  for (int j = 0; j < WPL; ++j)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) c[4 * j + t] = (float)((w[j] >> (8 * t)) & 0xFFu);
 }
-template <int BITS, int WPL>
-__device__ __forceinline__ void code_floats(const uint32_t* w, float* c, uint32_t nib) {
+
+// 4-bit codes: each nibble plane of a word (w & 0x0F0F0F0F, (w >> 4) &
+// 0x0F0F0F0F) holds one code per byte, and a byte c below 16 read as an OCP
+// e4m3 value is exactly c * 2^-9 (a subnormal below 8, exponent field 1
+// from 8), so one scaled conversion by 2^9 turns two of them into two exact
+// bf16 or f32 values.  Plane byte t of word j is value 8j + 2t (low plane)
+// or 8j + 2t + 1 (high plane); half h of a plane holds bytes 2h and 2h+1.
+//   pair 4j + 2*plane + h = values (8j + 4h + plane, 8j + 4h + plane + 2)
+template <int WPL>
+__device__ __forceinline__ void code_pairs4(const uint32_t* w, uint32_t* P, uint32_t nib) {
 #pragma unroll
   for (int j = 0; j < WPL; ++j) {
-    if constexpr (BITS == 8) {
+    const uint32_t pl[2] = {w[j] & nib, (w[j] >> 4) & nib};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) c[4 * j + t] = (float)((w[j] >> (8 * t)) & 0xFFu);
-    } else {
-      const uint32_t lo = opaque(w[j] & nib), hi = opaque((w[j] >> 4) & nib);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        c[8 * j + 2 * t] = (float)((lo >> (8 * t)) & 0xFFu);
-        c[8 * j + 2 * t + 1] = (float)((hi >> (8 * t)) & 0xFFu);
-      }
+    for (int k = 0; k < 2; ++k) {
+      P[4 * j + 2 * k] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pl[k], 512.0f, false));
+      P[4 * j + 2 * k + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pl[k], 512.0f, true));
     }
   }
+}
+template <int WPL>
+__device__ __forceinline__ void code_floats4(const uint32_t* w, float* c, uint32_t nib) {
+#pragma unroll
+  for (int j = 0; j < WPL; ++j) {
+    const uint32_t pl[2] = {w[j] & nib, (w[j] >> 4) & nib};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pl[k], 512.0f, false);
+      const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pl[k], 512.0f, true);
+      c[8 * j + k] = v0[0];
+      c[8 * j + k + 2] = v0[1];
+      c[8 * j + k + 4] = v1[0];
+      c[8 * j + k + 6] = v1[1];
+    }
+  }
+}
+// The value index of the first member of bf16 pair p (the second is 1 or 2
+// later): 4-bit pairs follow code_pairs4, 8-bit pairs are consecutive.
+template <int BITS>
+__device__ __forceinline__ constexpr int pair_first(int p) {
+  return BITS == 4 ? 8 * (p / 4) + 4 * (p % 2) + (p / 2) % 2 : 2 * p;
+}
+template <int BITS>
+__device__ __forceinline__ constexpr int pair_step() {
+  return BITS == 4 ? 2 : 1;
 }
 
 // Two exact bf16 values in one word (low half first): integers below 256
@@ -178,7 +212,8 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qb[e] = qg[(long)h * D + d0 + e];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) Q[r][p] = qb[2 * p] | (qb[2 * p + 1] << 16);
+    for (int p = 0; p < NP; ++p)
+      Q[r][p] = qb[pair_first<BITS>(p)] | (qb[pair_first<BITS>(p) + pair_step<BITS>()] << 16);
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) s += bf16_bits_to_f32(qb[e]);
@@ -226,11 +261,15 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
   for (int r = 0; r < REP; ++r) mx[r] = -INFINITY;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
-    float c[EPL];
-    code_floats<BITS, WPL>(KW[i], c, nib_mask);
     uint32_t P[NP];
+    if constexpr (BITS == 4) {
+      code_pairs4<WPL>(KW[i], P, nib_mask);
+    } else {
+      float c[EPL];
+      code_floats8<WPL>(KW[i], c);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) P[p] = pack_bf16(c[2 * p], c[2 * p + 1]);
+      for (int p = 0; p < NP; ++p) P[p] = pack_bf16(c[2 * p], c[2 * p + 1]);
+    }
 #pragma unroll
     for (int r = 0; r < REP; ++r) {
       float dsum = 0.f;
@@ -271,7 +310,10 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     float c[EPL];
-    code_floats<BITS, WPL>(VW[i], c, nib_mask);
+    if constexpr (BITS == 4)
+      code_floats4<WPL>(VW[i], c, nib_mask);
+    else
+      code_floats8<WPL>(VW[i], c);
 #pragma unroll
     for (int r = 0; r < REP; ++r) {
       const float p = __expf(sc[r][i] - M[r]);  // 0 for rows past the cache

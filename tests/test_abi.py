@@ -207,3 +207,14 @@ def test_group_sum_shapes_checked_by_the_binding():
     with pytest.raises(ValueError, match="groups"):
         b.residual_rms_norm(x, x, w, 1e-5, group_sums=torch.zeros(1024 // 32 - 1, 16),
                             group_size=32)
+
+
+def test_attention_workspace_sizes():
+    # none for one block; else the partial outputs [H, G, D] and the
+    # (max, sum) pairs [H, G, 2] of G = ceil(N / 256) blocks
+    L = b.lib()
+    assert L.qmm_attention_workspace_bytes(16, 256, 256) == 0
+    assert L.qmm_attention_workspace_bytes(16, 1, 128) == 0
+    assert L.qmm_attention_workspace_bytes(16, 8192, 256) == 16 * 32 * 258 * 4
+    assert L.qmm_attention_workspace_bytes(65, 257, 128) == 65 * 2 * 130 * 4
+    assert L.qmm_attention_workspace_bytes(0, 8192, 256) == 0

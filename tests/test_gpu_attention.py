@@ -81,6 +81,24 @@ def test_full_size_and_repeatable():
     assert np.array_equal(again, got)
 
 
+def test_reused_workspace():
+    # one workspace serves call after call (the partial outputs and block
+    # statistics are rewritten by each call before the merge reads them)
+    import torch
+    H, KV, N, D = 16, 8, 4099, 256
+    q, k, v = synth.attention_inputs(21, H=H, KV=KV, N=N, D=D, bits=4, group_size=64)
+    qd, kd, vd = b.to_device(q), _dev(k), _dev(v)
+    need = b.lib().qmm_attention_workspace_bytes(H, N, D)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # no zero-fill needed
+    outs = []
+    for _ in range(3):
+        outs.append(b.to_numpy_bits(b.decode_attention(qd, kd, vd, 4, 64, workspace=ws)))
+        torch.cuda.synchronize()
+    assert all(np.array_equal(o, outs[0]) for o in outs)
+    ref, tol = _ref(q, k, v, 4, 64)
+    _check(oracle.decode_bf16(outs[0]), ref, tol, "attention, reused workspace")
+
+
 def test_exact_scores_agree_within_one_step():
     # integer queries, small codes, key scale 1/8: every score's f32 sum is
     # exact, so both sides round the same value and only the f32 sums of the
