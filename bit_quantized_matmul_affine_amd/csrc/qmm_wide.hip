@@ -14,8 +14,9 @@ namespace qmm {
 // At 128 rows the per-group epilogue of the factored dequant (two FMAs per
 // output and group) would cost more vector instructions than the weights
 // themselves, so here every weight is dequantized once, in registers, to
-// bf16 (w = s*q + b from the same unpacked pairs and group factors, rounded
-// to nearest even) and the MFMAs accumulate y directly over all of K: no
+// bf16 (w = s*q + b, rounded to nearest even; 4-bit codes converted exactly
+// to f32 two at a time by dequant4_exact, 3-bit ones from the unpacked pairs
+// and group factors) and the MFMAs accumulate y directly over all of K: no
 // all-ones MFMA, no epilogue.  The rounding of w to bf16 (relative 2^-9) is
 // inside the accuracy bound of bf16 activations.
 //   * one workgroup owns TG = 8 W tiles (4 slots of 2) over all of K and all
@@ -33,6 +34,27 @@ namespace qmm {
 //     are unpacked; the 2 chunk positions' partial tiles are added through
 //     LDS in K order at the end.
 // ---------------------------------------------------------------------------
+// One B fragment of bf16 weights w = s*q + b from 4-bit word j of the
+// native layout (pair t = field t: codes at bits 4t and 16+4t).  The word's
+// nibble planes hold one code per byte; a byte below 16 read as an OCP e4m3
+// value is exactly q * 2^-9, so one conversion scaled by 2^9 gives two exact
+// codes as f32: plane lo = fields 0 and 2, plane hi = fields 1 and 3, byte
+// halves 0 / 1 = the low / high code of the pair.
+typedef float f32x2_w __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4 dequant4_exact(uint32_t w, float s, float b, uint32_t nib) {
+  const uint32_t lo = w & nib, hi = (w >> 4) & nib;
+  const f32x2_w l0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, false);
+  const f32x2_w l1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 512.0f, true);
+  const f32x2_w h0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, false);
+  const f32x2_w h1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 512.0f, true);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  auto pk = [&](float qa, float qb) {
+    const bf16x2_t v = {(__bf16)fmaf(s, qa, b), (__bf16)fmaf(s, qb, b)};
+    return __builtin_bit_cast(uint32_t, v);
+  };
+  return u32x4{pk(l0[0], l1[0]), pk(h0[0], h1[0]), pk(l0[1], l1[1]), pk(h0[1], h1[1])};
+}
+
 template <int BITS, int MT, typename ST>
 __global__ void __launch_bounds__(12 * 64) wide_kernel(LaunchArgs a) {
   constexpr int TW = 2, NSLOT = 4, KP = 2, NWC = NSLOT * KP, NWL = 4;
@@ -107,6 +129,7 @@ __global__ void __launch_bounds__(12 * 64) wide_kernel(LaunchArgs a) {
     };
     load(0);
     const PairMasks mask_v = pair_mask_vgpr<BITS>();
+    const uint32_t nib = opaque_sgpr(0x0F0F0F0Fu);  // 4-bit: one code per byte
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 acc[TW][MT];
 #pragma unroll
@@ -124,10 +147,17 @@ __global__ void __launch_bounds__(12 * 64) wide_kernel(LaunchArgs a) {
       for (int gp = 0; gp < 2; ++gp) {
         uint32_t P[TW][16];
         Affine f[TW];
+        uint32_t Wg[TW][2];  // 4-bit: the words of group gp
 #pragma unroll
         for (int i = 0; i < TW; ++i) {
-          unpack_pairs<BITS>(W[i], P[i], mask_v);
-          f[i] = group_affine<BITS>(gp, SBv[i].s(gp), SBv[i].b(gp));
+          if constexpr (BITS == 4) {
+            Wg[i][0] = W[i][2 * gp];
+            Wg[i][1] = W[i][2 * gp + 1];
+            f[i] = Affine{SBv[i].s(gp), SBv[i].b(gp)};
+          } else {
+            unpack_pairs<BITS>(W[i], P[i], mask_v);
+            f[i] = group_affine<BITS>(gp, SBv[i].s(gp), SBv[i].b(gp));
+          }
         }
         if (gp == 1 && j + 1 < NS) load(j + 1);  // the raw words are unpacked
 #pragma unroll
@@ -136,6 +166,10 @@ __global__ void __launch_bounds__(12 * 64) wide_kernel(LaunchArgs a) {
           u32x4 B[TW];
 #pragma unroll
           for (int i = 0; i < TW; ++i) {
+            if constexpr (BITS == 4) {
+              B[i] = dequant4_exact(Wg[i][h], f[i].sc, f[i].bp, nib);
+              continue;
+            }
             uint32_t bd[4];
 #pragma unroll
             for (int pp = 0; pp < 4; ++pp) {
