@@ -68,6 +68,35 @@ def test_matches_oracle(case):
     _check(got, ref, tol, "attention %s" % (case,))
 
 
+def _random_attention_cases(seed, n):
+    # supported shapes only: D in {128, 256, 512}, H/KV in {1, 2, 4, 8} with
+    # D * H/KV <= 1024; N from one row to a dozen blocks (ragged last block)
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        D = int(rng.choice([128, 256, 512]))
+        rep = int(rng.choice([1, 2, 4, 8]))
+        if D * rep > 1024:
+            continue
+        KV = int(rng.integers(1, 5))
+        out.append((KV * rep, KV, int(rng.integers(1, 3073)), D, int(rng.choice([4, 8])),
+                    int(rng.choice([32, 64, 128]))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_attention_cases(20261205, 12),
+                         ids=lambda c: "H%d_KV%d_N%d_D%d_b%d_g%d" % c)
+def test_random_shapes(case):
+    # seeded random shapes: block counts, ragged last blocks, head groups and
+    # code widths away from the fixed cases
+    H, KV, N, D, bits, gs = case
+    say("random attention", case)
+    q, k, v = synth.attention_inputs(3000 + N + D, H=H, KV=KV, N=N, D=D, bits=bits, group_size=gs)
+    ref, tol = _ref(q, k, v, bits, gs)
+    got = _run(q, k, v, bits, gs)
+    _check(got, ref, tol, "random attention %s" % (case,))
+
+
 def test_full_size_and_repeatable():
     # 16 query heads over 8 KV heads of 256 values, 8192 cached rows, 4-bit
     # group-64 keys and values
