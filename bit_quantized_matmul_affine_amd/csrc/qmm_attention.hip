@@ -30,13 +30,16 @@
 //     lane applies its group's scale and
 //     bias, the 16 lanes add their parts with DPP row operations, and the
 //     score is rounded to bf16;
-//   * two passes over the block's rows held in registers: the scores first
-//     (block maximum through LDS), then the weights e^(s - M) and the values,
-//     accumulated per lane as sum p s_v c (one FMA per value) plus one
-//     sum p b_v per row slice -- no rescaling of running sums;
+//   * two passes over the wave's rows held in registers: the scores first
+//     (the wave's maximum M_w by cross-lane swaps, no barrier, so a wave
+//     whose rows have landed goes on at once), then the weights e^(s - M_w)
+//     and the values, accumulated per lane as sum p s_v c (one FMA per
+//     value) plus one sum p b_v per row slice -- no rescaling of running
+//     sums;
 //   * the 16 lane groups' partial outputs are added through LDS in a fixed
-//     order; the block writes its unnormalized output and (M, sum e^(s - M))
-//     to the workspace, or, when one block covers the cache, the result;
+//     order, each scaled by its wave's e^(M_w - M) (M the block maximum);
+//     the block writes its unnormalized output and (M, sum e^(s - M)) to the
+//     workspace, or, when one block covers the cache, the result;
 //   * kernel 2 merges the blocks of each head (64 values per workgroup) in a
 //     fixed order (deterministic).
 #include <hip/hip_runtime.h>
@@ -254,7 +257,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
 
   const uint32_t nib_mask = sgpr_const(0x0F0F0F0Fu);
 
-  // pass 1: scores (bf16-rounded) and the block maximum
+  // pass 1: scores (bf16-rounded) and the wave's maximum
   float sc[REP][R];
   float mx[REP];
 #pragma unroll
@@ -281,21 +284,18 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
       mx[r] = fmaxf(mx[r], sc[r][i]);
     }
   }
+  // over the 4 lane groups of the wave: each wave goes on to its values
+  // without waiting for the others (their partials are rescaled to the
+  // block maximum when they are added); a wave whose rows all lie past the
+  // cache has weight 0 everywhere
+  float Mw[REP];
 #pragma unroll
   for (int r = 0; r < REP; ++r) {
-    // over the 4 lane groups of the wave, then the 4 waves
     float m = mx[r];
     m = fmaxf(m, __shfl_xor(m, 16));
     m = fmaxf(m, __shfl_xor(m, 32));
     if (lane == 0) red_max[wave][r] = m;
-  }
-  __syncthreads();
-  float M[REP];
-#pragma unroll
-  for (int r = 0; r < REP; ++r) {
-    M[r] = red_max[0][r];
-#pragma unroll
-    for (int w = 1; w < kAttnThreads / 64; ++w) M[r] = fmaxf(M[r], red_max[w][r]);
+    Mw[r] = m == -INFINITY ? 0.f : m;
   }
 
   // pass 2: weights and values
@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
       code_floats8<WPL>(VW[i], c);
 #pragma unroll
     for (int r = 0; r < REP; ++r) {
-      const float p = __expf(sc[r][i] - M[r]);  // 0 for rows past the cache
+      const float p = __expf(sc[r][i] - Mw[r]);  // 0 for rows past the cache
       lsum[r] += p;
       pb[r] = fmaf(p, vb[i], pb[r]);
       const float ps = p * vs[i];
@@ -334,13 +334,33 @@ __global__ void __launch_bounds__(kAttnThreads) attn_block_kernel(AttnArgs a) {
   if (sub == 0)
 #pragma unroll
     for (int r = 0; r < REP; ++r) red_sum[lg][r] = lsum[r];
+  // the block maximum, and each wave's factor e^(M_w - M) (0 for a wave
+  // without rows in the cache)
+  __shared__ float cw[REP][kAttnThreads / 64];
+  __syncthreads();
+  float M[REP];
+#pragma unroll
+  for (int r = 0; r < REP; ++r) {
+    M[r] = red_max[0][r];
+#pragma unroll
+    for (int w = 1; w < kAttnThreads / 64; ++w) M[r] = fmaxf(M[r], red_max[w][r]);
+  }
+  if (threadIdx.x < REP * (kAttnThreads / 64)) {
+    const int r = threadIdx.x / (kAttnThreads / 64), w = threadIdx.x % (kAttnThreads / 64);
+    const float m = red_max[w][r];
+    float mb = red_max[0][r];
+    for (int u = 1; u < kAttnThreads / 64; ++u) mb = fmaxf(mb, red_max[u][r]);
+    cw[r][w] = m == -INFINITY ? 0.f : __expf(m - mb);
+  }
   __syncthreads();
   for (int idx = threadIdx.x; idx < REP * D; idx += kAttnThreads) {
     const int r = idx / D, d = idx - r * D;
     float v = 0.f, l = 0.f;
+#pragma unroll
     for (int j = 0; j < kAttnGroups; ++j) {
-      v += lds[(j * REP + r) * D + d];
-      l += red_sum[j][r];
+      const float c = cw[r][j / 4];  // lane group j belongs to wave j / 4
+      v = fmaf(lds[(j * REP + r) * D + d], c, v);
+      l = fmaf(red_sum[j][r], c, l);
     }
     const int h = kv * REP + r;
     if (a.G == 1) {
